@@ -1,0 +1,275 @@
+"""The MoE-layer forward pass, written out plainly in fp64 (numpy).
+
+What is computed (MoK paper "Mixture-of-Kittens: MoE Megakernel for NVL72s",
+§2.1, MoE equation; MoK blog repost, section "Overlapping computation and
+communication in MoE"):
+
+    MoE(x, s) = f_shared(x) + sum_{i in E} g_i f_i(x),   g_i = s_i / sum_{j in E} s_j
+    f_i(x)    = W_down^(i) ( SiLU(W_gate^(i) x) * W_up^(i) x ),  SiLU(a) = a * sigmoid(a)
+
+with E the k experts selected by the router projection (§2.1), and the
+dispatch schedule of Algorithm 1 (§3.1) placing the routed rows in
+expert-contiguous buffer positions.
+
+Readings where the pages are silent (listed in the design doc):
+* router scores s are the softmax of fp32 router logits over all experts; the
+  selection is the k largest fp32 logits, ties to the lower expert id, with
+  -0.0 equal to +0.0; slot s of token t is its s-th selection in that order and
+  route j = t*k + s;
+* the intermediate h is stored in bf16 (MX along I in MXFP8 mode) and each
+  routed expert's output row is stored in bf16; the shared expert's output and
+  the gate-weighted sum stay at full precision;
+* in MXFP8 mode the routed experts see MX-quantised activations and weights
+  (§3.4 "MXFP8 Support"); the shared expert and the router stay bf16.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+from . import bf16 as _bf16
+from . import mx as _mx
+
+
+# ----------------------------------------------------------------------------
+# Router projection, top-k selection and normalised gates (§2.1)
+# ----------------------------------------------------------------------------
+
+def router_logits(x_bits: np.ndarray, w_router_bits: np.ndarray) -> np.ndarray:
+    """logits[t, e] = sum_d x[t, d] * W_r[e, d], in fp64 from the bf16 inputs."""
+    return _bf16.to_f64(x_bits) @ _bf16.to_f64(w_router_bits).T
+
+
+def topk(logits_f32: np.ndarray, k: int) -> np.ndarray:
+    """The k selected experts of each token, in slot order.
+
+    The decision is taken on the fp32 logits themselves.  Experts are ordered by
+    (larger logit first, then lower id); -0.0 and +0.0 are the same logit.
+    Returns int32 [T, k]: entry (t, s) is the expert in slot s of token t.
+    """
+    l = np.asarray(logits_f32, dtype=np.float32)
+    if not np.all(np.isfinite(l)):
+        raise ValueError("non-finite router logit")
+    T, E = l.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    lv = l.astype(np.float64) + 0.0  # -0.0 + 0.0 == +0.0
+    ids = np.broadcast_to(np.arange(E), (T, E))
+    # lexsort sorts by the last key first: primary key -logit, secondary key id
+    order = np.lexsort((ids, -lv), axis=-1)
+    return order[:, :k].astype(np.int32)
+
+
+def router_scores(logits_f32: np.ndarray) -> np.ndarray:
+    """s = softmax of the logits over all experts (reading of "router weights")."""
+    l = np.asarray(logits_f32, dtype=np.float64)
+    z = np.exp(l - l.max(axis=-1, keepdims=True))
+    return z / z.sum(axis=-1, keepdims=True)
+
+
+def gates(logits_f32: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """g_i = s_i / sum_{j in E} s_j over the selected experts E (fp64, [T, k])."""
+    s = router_scores(logits_f32)
+    sel = np.take_along_axis(s, np.asarray(idx, dtype=np.int64), axis=-1)
+    return sel / sel.sum(axis=-1, keepdims=True)
+
+
+# ----------------------------------------------------------------------------
+# Dispatch schedule (Algorithm 1, §3.1 "Scheduling")
+# ----------------------------------------------------------------------------
+
+def schedule(A: np.ndarray, c: int, L: int) -> Dict[str, np.ndarray]:
+    """Algorithm 1 of the MoK paper, step by step.
+
+    A [R, N*K]: A[r, j] is the global expert of route j on source rank r.
+    c: current rank; local expert l is global expert c*L + l.
+
+    Returns
+      M        [R, L]  routes per (source rank, local expert)
+      counts   [L]     rows received per local expert (sum over r of M)
+      offsets  [L+1]   S_l, the start of expert l's region; offsets[L] = P
+      sched    [P]     Phi: position p receives route (r, j), stored as r*N*K + j
+      route_dst [R*N*K] position of each route on this rank, -1 if not local
+    """
+    A = np.asarray(A, dtype=np.int64)
+    R, NK = A.shape
+    local = (A >= c * L) & (A < c * L + L)
+    M = np.zeros((R, L), dtype=np.int64)
+    for r in range(R):
+        M[r] = np.bincount(A[r][local[r]] - c * L, minlength=L)
+    counts = M.sum(axis=0)
+    S = np.concatenate([[0], np.cumsum(counts)])
+    P = int(S[L])
+    sched = np.full(P, -1, dtype=np.int64)
+    route_dst = np.full(R * NK, -1, dtype=np.int64)
+    for r in range(R):
+        seen = np.zeros(L, dtype=np.int64)  # earlier routes of rank r per local expert
+        for j in range(NK):
+            if not local[r, j]:
+                continue
+            l = int(A[r, j] - c * L)
+            o = int(seen[l])  # |{j' < j : A[r, j'] = A[r, j]}|
+            seen[l] += 1
+            Ml = M[:, l]
+            p = int(np.minimum(Ml, o).sum()) + int(np.count_nonzero(Ml[:r] > o))
+            pos = int(S[l]) + p
+            assert sched[pos] == -1
+            sched[pos] = r * NK + j
+            route_dst[r * NK + j] = pos
+    assert np.all(sched >= 0)
+    return {"M": M, "counts": counts, "offsets": S.astype(np.int64), "sched": sched,
+            "route_dst": route_dst}
+
+
+def schedule_by_sort(A: np.ndarray, c: int, L: int) -> np.ndarray:
+    """The same table as a sort of the local routes by the key (l, o, r) (§3.1).
+
+    Returns the sched column (r*N*K + j for each position).
+    """
+    A = np.asarray(A, dtype=np.int64)
+    R, NK = A.shape
+    keys = []
+    for r in range(R):
+        count = {}
+        for j in range(NK):
+            e = int(A[r, j])
+            if c * L <= e < c * L + L:
+                o = count.get(e, 0)
+                count[e] = o + 1
+                keys.append((e - c * L, o, r, r * NK + j))
+    keys.sort()
+    return np.array([key[3] for key in keys], dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------
+# Expert feed-forward networks (§2.1; SiLU gate from the blog's notation)
+# ----------------------------------------------------------------------------
+
+def silu(a: np.ndarray) -> np.ndarray:
+    return a / (1.0 + np.exp(-a))
+
+
+def ffn(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray,
+        h_store: str = "bf16", y_store: Optional[str] = "bf16") -> np.ndarray:
+    """f(x) = W_down (SiLU(W_gate x) * W_up x) for rows x [n, D], fp64.
+
+    w_gate, w_up: [I, D]; w_down: [D, I] (all fp64 values).  h is rounded the
+    way it is stored ("bf16", "mx" along I, or None), and so is the output row
+    ("bf16" or None).
+    """
+    a_g = x @ w_gate.T
+    a_u = x @ w_up.T
+    h = silu(a_g) * a_u
+    if h_store == "bf16":
+        h = _bf16.round_f64(h)
+    elif h_store == "mx":
+        h = _mx.round_f64(h)
+    elif h_store is not None:
+        raise ValueError(h_store)
+    y = h @ w_down.T
+    if y_store == "bf16":
+        y = _bf16.round_f64(y)
+    elif y_store is not None:
+        raise ValueError(y_store)
+    return y
+
+
+def _expert_weights(weights: Dict[str, np.ndarray], e: int, precision: str):
+    """fp64 values of expert e's weights as the routed FFN sees them."""
+    if precision == "bf16":
+        return (_bf16.to_f64(weights["w_gate"][e]), _bf16.to_f64(weights["w_up"][e]),
+                _bf16.to_f64(weights["w_down"][e]))
+    if precision == "mxfp8":
+        return (_mx.dequantize(weights["q_gate"][e], weights["s_gate"][e]),
+                _mx.dequantize(weights["q_up"][e], weights["s_up"][e]),
+                _mx.dequantize(weights["q_down"][e], weights["s_down"][e]))
+    raise ValueError(precision)
+
+
+def routed_outputs(x_bits: np.ndarray, weights: Dict[str, np.ndarray], idx: np.ndarray,
+                   precision: str = "bf16", tokens: Optional[np.ndarray] = None,
+                   exact: bool = False) -> np.ndarray:
+    """Y[t, s] = f_{idx[t,s]}(x_t) for every route, fp64 [len(tokens), k, D].
+
+    The routes of one expert are evaluated together (a matmul per expert); each
+    route's row is independent of the others.  In MXFP8 mode x is MX-quantised
+    along D before the projections (§3.4: activation quantisation in dispatch).
+    ``exact`` skips the storage rounding of h and of the output rows.
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    tokens = np.arange(idx.shape[0]) if tokens is None else np.asarray(tokens)
+    x = _bf16.to_f64(x_bits[tokens])
+    if precision == "mxfp8":
+        x = _mx.round_f64(x)
+    sel = idx[tokens]
+    n, k = sel.shape
+    Y = np.zeros((n, k, x.shape[1]), dtype=np.float64)
+    h_store = None if exact else ("bf16" if precision == "bf16" else "mx")
+    y_store = None if exact else "bf16"
+    for e in np.unique(sel):
+        ti, si = np.nonzero(sel == e)
+        wg, wu, wd = _expert_weights(weights, int(e), precision)
+        Y[ti, si] = ffn(x[ti], wg, wu, wd, h_store=h_store, y_store=y_store)
+    return Y
+
+
+def shared_output(x_bits: np.ndarray, weights: Dict[str, np.ndarray],
+                  tokens: Optional[np.ndarray] = None, exact: bool = False) -> np.ndarray:
+    """f_shared(x) in fp64 (bf16 weights, h stored in bf16, output unrounded)."""
+    x = _bf16.to_f64(x_bits if tokens is None else x_bits[tokens])
+    return ffn(x, _bf16.to_f64(weights["ws_gate"]), _bf16.to_f64(weights["ws_up"]),
+               _bf16.to_f64(weights["ws_down"]), h_store=None if exact else "bf16", y_store=None)
+
+
+def combine(shared: np.ndarray, g: np.ndarray, Y: np.ndarray) -> np.ndarray:
+    """MoE(x) = f_shared(x) + sum_s g_s * Y_s (the router-weighted sum)."""
+    return shared + np.einsum("tk,tkd->td", g, Y)
+
+
+def forward(x_bits: np.ndarray, weights: Dict[str, np.ndarray], logits_f32: np.ndarray, k: int,
+            precision: str = "bf16", tokens: Optional[np.ndarray] = None,
+            exact: bool = False) -> Dict[str, np.ndarray]:
+    """The whole layer for the given (or all) tokens from fp32 router logits.
+
+    The selection and the gates are taken on the given fp32 logits (the same
+    values the GPU path routes on).  Returns idx, gates, Y and out (fp64).
+    ``exact`` evaluates the formula with no storage rounding of intermediates.
+    """
+    idx = topk(logits_f32, k)
+    g = gates(logits_f32, idx)
+    tok = np.arange(idx.shape[0]) if tokens is None else np.asarray(tokens)
+    Y = routed_outputs(x_bits, weights, idx, precision, tok, exact=exact)
+    sh = shared_output(x_bits, weights, tok, exact=exact)
+    return {"idx": idx, "gates": g, "Y": Y, "shared": sh, "out": combine(sh, g[tok], Y)}
+
+
+def layer_flops(T: int, D: int, I: int, k: int) -> float:
+    """Expert-FFN FLOP of one forward, 6*T*(k+1)*D*I (§4.1)."""
+    return 6.0 * T * (k + 1) * D * I
+
+
+def quantize_weights_mx(weights: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    """MX-quantise the routed expert weights along their K axis (D for gate and
+    up, I for down) from their bf16 values."""
+    out = dict(weights)
+    for name, q, s in (("w_gate", "q_gate", "s_gate"), ("w_up", "q_up", "s_up"),
+                       ("w_down", "q_down", "s_down")):
+        out[q], out[s] = _mx.quantize(_bf16.to_f64(weights[name]))
+    return out
+
+
+def logit_bound(x_bits: np.ndarray, w_router_bits: np.ndarray) -> np.ndarray:
+    """Bound on |fl32(logit) - logit| for any fp32 summation order.
+
+    bf16 x bf16 products are exact in fp32, so only the D-1 additions round:
+    |err| <= gamma_D * sum_d |x_d w_{e,d}| with gamma_D = D u / (1 - D u)
+    (Higham, "Accuracy and Stability of Numerical Algorithms", §3.1), taken
+    here with u = 2^-23 so that it also holds if the hardware adder truncates.
+    """
+    x = np.abs(_bf16.to_f64(x_bits))
+    w = np.abs(_bf16.to_f64(w_router_bits))
+    D = x.shape[1]
+    u = 2.0 ** -23  # twice the round-to-nearest unit: also covers truncating adders
+    return (D * u / (1 - D * u)) * (x @ w.T)

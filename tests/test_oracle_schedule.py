@@ -1,0 +1,104 @@
+"""Pins of the oracle's dispatch schedule (Algorithm 1 of the MoK paper).
+
+The paper gives two descriptions of the same table: Algorithm 1's closed form
+for the position p, and "sort the routes by the key (local expert, ordinal,
+source rank)" (§3.1 "Scheduling").  Each one checks the other.  On top of
+that: library routines (bincount, stable argsort) and the properties the
+table must have (a bijection onto expert-contiguous regions, source ranks
+interleaved round-robin inside a region).
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import moe
+
+
+def random_routes(R, N, K, E_total, seed, skew=None):
+    rng = np.random.default_rng(seed)
+    A = np.empty((R, N * K), dtype=np.int64)
+    p = None
+    if skew is not None:
+        p = np.arange(1, E_total + 1, dtype=np.float64) ** (-skew)
+        p /= p.sum()
+    for r in range(R):
+        for t in range(N):
+            A[r, t * K:(t + 1) * K] = rng.choice(E_total, size=K, replace=False, p=p)
+    return A
+
+
+CASES = [  # R, N, K, L, c, E_total, skew
+    (1, 50, 2, 8, 0, 8, None),
+    (1, 200, 8, 16, 0, 16, 1.2),
+    (4, 30, 3, 5, 2, 20, None),
+    (8, 40, 4, 4, 0, 32, 1.2),
+    (3, 25, 2, 6, 1, 18, 2.0),
+]
+
+
+@pytest.mark.parametrize("R,N,K,L,c,E_total,skew", CASES)
+def test_closed_form_equals_sort_by_key(R, N, K, L, c, E_total, skew):
+    A = random_routes(R, N, K, E_total, seed=R * 100 + N, skew=skew)
+    s = moe.schedule(A, c, L)
+    assert np.array_equal(s["sched"], moe.schedule_by_sort(A, c, L))
+
+
+@pytest.mark.parametrize("R,N,K,L,c,E_total,skew", CASES)
+def test_table_properties(R, N, K, L, c, E_total, skew):
+    A = random_routes(R, N, K, E_total, seed=R * 7 + N, skew=skew)
+    s = moe.schedule(A, c, L)
+    M, counts, S, sched, dst = s["M"], s["counts"], s["offsets"], s["sched"], s["route_dst"]
+    local = (A >= c * L) & (A < (c + 1) * L)
+    # counts are per-(rank, expert) histograms
+    for r in range(R):
+        assert np.array_equal(M[r], np.bincount(A[r][local[r]] - c * L, minlength=L))
+    assert np.array_equal(S, np.concatenate([[0], np.cumsum(counts)]))
+    # bijection between local routes and positions; route_dst is the inverse
+    flat_local = np.nonzero(local.reshape(-1))[0]
+    assert np.array_equal(np.sort(sched), flat_local)
+    assert np.array_equal(dst[sched], np.arange(S[-1]))
+    assert np.all(dst[~local.reshape(-1)] == -1)
+    # expert-contiguous regions of the right length
+    expert_of = A.reshape(-1)[sched] - c * L
+    for l in range(L):
+        assert np.all(expert_of[S[l]:S[l + 1]] == l)
+    # within a region: per source rank, routes keep their original order, and
+    # the first min_r M[r, l] rounds cycle through the ranks round-robin
+    for l in range(L):
+        reg = sched[S[l]:S[l + 1]]
+        ranks, js = reg // (N * K), reg % (N * K)
+        for r in range(R):
+            assert np.all(np.diff(js[ranks == r]) > 0)
+        present = [r for r in range(R) if M[r, l] > 0]
+        rounds = min(M[r, l] for r in present) if present else 0
+        head = ranks[: rounds * len(present)]
+        assert np.array_equal(head, np.tile(present, rounds))
+
+
+def test_single_rank_is_stable_counting_sort():
+    A = random_routes(1, 300, 8, 32, seed=11, skew=1.2)
+    s = moe.schedule(A, 0, 32)
+    assert np.array_equal(s["sched"], np.argsort(A[0], kind="stable"))
+
+
+def test_empty_experts_and_all_to_one():
+    A = np.zeros((1, 40), dtype=np.int64)  # every route to expert 0
+    s = moe.schedule(A, 0, 4)
+    assert list(s["counts"]) == [40, 0, 0, 0]
+    assert list(s["offsets"]) == [0, 40, 40, 40, 40]
+    assert np.array_equal(s["sched"], np.arange(40))
+    # no local route at all
+    s2 = moe.schedule(A + 8, 0, 4)
+    assert s2["offsets"][-1] == 0 and s2["sched"].size == 0 and np.all(s2["route_dst"] == -1)
+
+
+def test_ep_share_generator_counts():
+    counts = synth.zipf_counts(600, 4, 1.2)
+    assert sum(counts) == 600 and counts == sorted(counts, reverse=True)
+    A = synth.ep_share_routes(R=8, N=100, k=4, E_total=32, rank=0, L=4, counts=counts, seed=1)
+    s = moe.schedule(A, 0, 4)
+    assert list(s["counts"]) == counts
+    # each token holds distinct experts
+    tok = A.reshape(8, 100, 4)
+    assert all(len(set(tok[r, t])) == 4 for r in range(8) for t in range(100))
