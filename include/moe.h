@@ -1,0 +1,228 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) MoE-layer forward library, libmoe.so.
+ *
+ * The library computes the forward pass of one DeepSeek-V3-style MoE layer on
+ * one GPU's share of the work (MoK paper "Mixture-of-Kittens: MoE Megakernel
+ * for NVL72s", §2.1, MoE equation):
+ *
+ *   MoE(x) = f_shared(x) + sum_{i in E} g_i f_i(x),   g_i = s_i / sum_{j in E} s_j
+ *   f_i(x) = W_down^(i) ( SiLU(W_gate^(i) x) * W_up^(i) x )
+ *
+ * in three calls, in stream order:
+ *   moe_route     router projection, top-k selection and normalised gates;
+ *   moe_schedule  the dispatch schedule of Algorithm 1 (per-expert counts,
+ *                 prefix sums, the position -> source-route table and its
+ *                 inverse);
+ *   moe_forward   shared expert, then per minibatch of b routed rows: gather
+ *                 into the ring buffer, grouped up/gate GEMM with SwiGLU,
+ *                 grouped down GEMM; then the fixed-order gate-weighted combine.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, allocated and owned by the caller;
+ *     all tensors are dense row-major.  bf16 data are raw IEEE bfloat16 bit
+ *     patterns (uint16_t), e4m3 data raw OCP E4M3FN bytes, scales raw E8M0
+ *     bytes.
+ *   - The library never allocates, frees or synchronises device memory, and
+ *     never reads device memory on the host.  All work is enqueued on `stream`
+ *     (a hipStream_t; NULL is the default stream).  Calls on distinct
+ *     workspaces are independent; calls sharing a workspace must be ordered by
+ *     the caller (stream order does that).
+ *   - Shapes are validated on the host from `moe_shape` alone, before any
+ *     launch; violations return MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED.
+ *   - Data errors found on the device (an expert id out of range, more routed
+ *     rows than `max_rows`, a non-finite router logit) set bits of a sticky
+ *     word in the workspace and never cause an out-of-bounds access; read it
+ *     with moe_get_device_error().  Tokens are never dropped silently.
+ *   - Results are bitwise identical from run to run, and for every minibatch
+ *     size b and ring size C: no floating-point atomics, no split-K, and the
+ *     combine sums the k routed rows in slot order (MoK paper §3.4,
+ *     "Determinism").
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, inconsistent sizes, bad tunable */
+  MOE_ERR_UNSUPPORTED = -2, /* valid request this build does not implement */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+/* Arithmetic of the routed experts (MoK paper §3.4, "MXFP8 Support": the shared
+ * expert always stays bf16). */
+typedef enum { MOE_BF16 = 0, MOE_MXFP8 = 1 } moe_precision;
+
+/* Device error bits, OR-ed into the workspace's sticky error word. */
+#define MOE_DEVERR_EXPERT_RANGE 0x1 /* a route names an expert outside [0, E_total) */
+#define MOE_DEVERR_ROW_OVERFLOW 0x2 /* routed rows exceed max_rows; extra rows skipped */
+#define MOE_DEVERR_NONFINITE 0x4    /* a router logit is NaN or infinite */
+
+/*
+ * Sizes and tunables.  On one GPU: num_src_ranks = 1, rank = 0,
+ * experts_per_rank = E_total, tokens_per_src_rank = T, max_rows = T*k.
+ * The (R, c, L, N) fields are those of Algorithm 1 (MoK paper §3.1): R source
+ * ranks with N tokens each, this is rank c, which holds local experts
+ * c*L .. c*L+L-1; they let one GPU build and run its share of an
+ * expert-parallel layer from an all-gathered route matrix.
+ */
+typedef struct {
+  int64_t T;                   /* tokens of this rank (rows of x_local, gates) */
+  int64_t D;                   /* hidden width; multiple of 64 */
+  int64_t I;                   /* routed expert intermediate width; multiple of 64 */
+  int64_t I_shared;            /* shared expert intermediate width; multiple of 64 */
+  int64_t E_total;             /* router width (all routed experts); <= 1024 */
+  int64_t k;                   /* experts per token; 1 <= k <= min(E_total, 16) */
+  int64_t num_src_ranks;       /* R */
+  int64_t rank;                /* c */
+  int64_t experts_per_rank;    /* L; R*L == E_total; L <= 1024 */
+  int64_t tokens_per_src_rank; /* N; == T when R == 1 */
+  int64_t max_rows;            /* bound on routed rows P received; T*k when R == 1 */
+  int64_t minibatch_rows;      /* b: rows per gather/GEMM step (granularity), >= 1 */
+  int64_t ring_rows;           /* C: ring buffer capacity, a positive multiple of b */
+  int32_t precision;           /* moe_precision */
+  int32_t reserved;            /* must be 0 */
+} moe_shape;
+
+/* Expert weights, all K-contiguous (each output row is a contiguous K vector):
+ *   routed  w_gate, w_up [L, I, D]; w_down [L, D, I]   (bf16, or e4m3 for MXFP8)
+ *           s_gate, s_up [L, I, D/32]; s_down [L, D, I/32]   (E8M0, MXFP8 only)
+ *   shared  ws_gate, ws_up [I_shared, D]; ws_down [D, I_shared]   (bf16) */
+typedef struct {
+  const void *w_gate, *w_up, *w_down;
+  const uint8_t *s_gate, *s_up, *s_down;
+  const void *ws_gate, *ws_up, *ws_down;
+} moe_weights;
+
+/* Bytes of device workspace the three calls below need for `shape` (one
+ * workspace serves all of them; it also holds the sticky error word).
+ * Returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED for a bad shape. */
+moe_status moe_workspace_bytes(const moe_shape* shape, size_t* bytes);
+
+/* Clear the workspace's sticky error word (one small kernel on `stream`). */
+moe_status moe_workspace_init(const moe_shape* shape, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Router projection, top-k selection and gates (MoK paper §2.1: the router
+ * projection picks each token's k routed experts and gives each one a weight;
+ * the weights are normalised over the chosen experts, g_i = s_i / sum_{j in E}
+ * s_j in the MoK blog's notation, with s the softmax of the logits).
+ *
+ *   x         [T, D] bf16, or NULL: then `logits` is an INPUT (given logits,
+ *             as in the MoK paper's §4.1 benchmark protocol)
+ *   w_router  [E_total, D] bf16 (ignored when x is NULL)
+ *   logits    [T, E_total] fp32: output of x @ w_router^T (fp32 accumulation),
+ *             or input when x is NULL
+ *   topk_idx  [T, k] int32 out: slot s of token t holds the expert with the
+ *             s-th largest logit; ties go to the lower expert id; -0.0 == +0.0
+ *   topk_gate [T, k] fp32 out: exp(l_s - l_0) / sum_{s'} exp(l_s' - l_0)
+ * A non-finite logit sets MOE_DEVERR_NONFINITE (NaN then ranks last).
+ */
+moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router, float* logits,
+                     int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dispatch schedule of Algorithm 1 (MoK paper §3.1): for routes A [R, N*k]
+ * (global expert ids; topk_idx is A when R == 1), with local expert l = global
+ * expert c*L + l:
+ *   M[r][l]  routes from source rank r to local expert l;
+ *   S_l      = sum_{l' < l} sum_r M[r][l']   (expert_offsets[l]; [L] = P);
+ *   o        = earlier routes j' < j of the same rank to the same expert;
+ *   p        = sum_{r'} min(M[r'][l], o) + #{r' < r : M[r'][l] > o};
+ *   sched_src[S_l + p] = r*N*k + j  (the table row is the buffer position);
+ *   route_dst[r*N*k + j] = S_l + p, or -1 for a route to a non-local expert.
+ * Outputs: expert_counts [L], expert_offsets [L+1], sched_src [max_rows]
+ * (entries >= P untouched), route_dst [R*N*k].  Integer only; deterministic
+ * (no order-dependent atomics).  Bit-exact with the definition above.
+ */
+moe_status moe_schedule(const moe_shape* shape, const int32_t* routes, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* sched_src, int32_t* route_dst, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*
+ * The layer forward from a schedule (MoK paper §2.1 MoE equation; §3.3 ring
+ * buffer; §3.4 "Shared Expert", "Determinism").
+ *
+ *   x_src      [R*N, D] bf16: source token rows; route r*N*k + j reads row
+ *              r*N + j/k (x_src == x_local when R == 1)
+ *   x_local    [T, D] bf16: this rank's tokens, input of the shared expert
+ *   topk_gate  [T, k] fp32 gates of this rank's routes (from moe_route)
+ *   expert_offsets, sched_src, route_dst: from moe_schedule
+ *   out        [T, D] bf16 out: RNE of out32
+ *   out32      [T, D] fp32 out, or NULL: the pre-cast result
+ *
+ * Per minibatch m (rows m*b .. m*b+b-1 of the schedule, in ascending order):
+ * rows are gathered into ring slots (p mod C) with no other local copy; the
+ * up/gate GEMM + SwiGLU writes h (bf16); the down GEMM writes each routed
+ * output row (bf16) to the route it came from (R == 1: slot sched_src[p],
+ * reusing the table for the combine as in §3.1) or to outbox row p (R > 1).
+ * The combine then forms, for each local token t, in this fixed order and fp32:
+ *   acc = 0; for s in 0..k-1: acc = fma(g[t,s], y[t,s], acc); out32[t] = acc + shared[t]
+ * where y[t,s] is the row of route t*k+s, or 0 for a route to a remote expert
+ * (R > 1: its row comes back from another rank, outside this library).
+ */
+moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const void* x_src,
+                       const void* x_local, const float* topk_gate, const int32_t* expert_offsets,
+                       const int32_t* sched_src, const int32_t* route_dst, void* out, float* out32,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * MX quantisation along rows (MoK paper §3.4, "MXFP8 Support": weights are
+ * pre-quantised by a dedicated kernel).  src [rows, K] bf16, K a multiple of
+ * 32 -> q [rows, K] E4M3FN and scale [rows, K/32] E8M0: per block of 32,
+ * X = floor(log2(amax)) - 8 clamped to [-127, 127] (all-zero block: X = -127),
+ * scale byte X + 127, elements RNE(v / 2^X) saturated to +-448.
+ */
+moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale,
+                              void* stream);
+
+/* Read the sticky device error word (MOE_DEVERR_* bits).  SYNCHRONISES the
+ * stream: diagnostics only, never on the hot path. */
+moe_status moe_get_device_error(const moe_shape* shape, const void* ws, size_t ws_bytes,
+                                void* stream, int32_t* host_code);
+
+/*
+ * Benchmark instrumentation, not part of the layer.  While a probe is active,
+ * every launch of kernel `kernel_id` (one of moe_kernel_id) made by the calls
+ * above is bracketed by a pair of HIP events recorded on the launch stream,
+ * for up to `max_launches` launches.  moe_probe_end() SYNCHRONISES the device,
+ * returns the summed event time in ms and the number of timed launches, and
+ * releases the events.  One probe per process; not thread-safe.
+ */
+typedef enum {
+  MOE_K_ROUTER_GEMM = 0, /* moe_route: logits = x W_r^T */
+  MOE_K_TOPK = 1,        /* moe_route: top-k + gates */
+  MOE_K_SCHEDULE = 2,    /* moe_schedule: all three schedule kernels, as one interval */
+  MOE_K_TILES = 3,       /* moe_forward: per-minibatch tile lists */
+  MOE_K_SHARED_UP = 4,   /* shared expert up/gate + SwiGLU */
+  MOE_K_SHARED_DOWN = 5, /* shared expert down projection */
+  MOE_K_GATHER = 6,      /* routed rows into the ring */
+  MOE_K_UP_GATE = 7,     /* routed grouped up/gate + SwiGLU */
+  MOE_K_DOWN = 8,        /* routed grouped down projection */
+  MOE_K_COMBINE = 9,     /* gate-weighted combine */
+  MOE_K_COUNT = 10
+} moe_kernel_id;
+
+moe_status moe_probe_begin(int32_t kernel_id, int32_t max_launches);
+moe_status moe_probe_end(double* total_ms, int32_t* launches);
+
+/* Static string for a status code. */
+const char* moe_status_str(moe_status status);
+
+/* MOE_ABI_VERSION of the built library. */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

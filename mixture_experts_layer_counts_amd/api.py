@@ -1,0 +1,181 @@
+"""Thin torch binding of libmoe.so: argument checks and marshalling only.
+
+Torch supplies device memory and the current HIP stream; the C calls do all
+of the work.  Names follow include/moe.h: ``route``, ``schedule``,
+``forward`` and ``quantize_mxfp8``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import _lib
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device: torch.device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def shape_for(T: int, D: int, I: int, E: int, k: int, I_shared: Optional[int] = None,
+              minibatch_rows: Optional[int] = None, ring_rows: Optional[int] = None,
+              precision: str = "bf16", R: int = 1, rank: int = 0, max_rows: Optional[int] = None) -> _lib.MoeShape:
+    """A moe_shape for one GPU (R = 1) or for rank ``rank`` of R source ranks."""
+    L = E // R
+    max_rows = T * k if max_rows is None else max_rows
+    b = minibatch_rows or max(max_rows, 1)
+    C = ring_rows or b
+    s = _lib.MoeShape()
+    s.T, s.D, s.I, s.I_shared, s.E_total, s.k = T, D, I, I if I_shared is None else I_shared, E, k
+    s.num_src_ranks, s.rank, s.experts_per_rank, s.tokens_per_src_rank = R, rank, L, T
+    s.max_rows, s.minibatch_rows, s.ring_rows = max_rows, b, C
+    s.precision = {"bf16": _lib.MOE_BF16, "mxfp8": _lib.MOE_MXFP8}[precision]
+    s.reserved = 0
+    return s
+
+
+class MoELayer:
+    """One layer's shape plus its device workspace, on ``device``."""
+
+    def __init__(self, shape: _lib.MoeShape, device="cuda"):
+        self.lib = _lib.load()
+        self.shape = shape
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        nbytes = ctypes.c_size_t(0)
+        _lib.check("moe_workspace_bytes", self.lib.moe_workspace_bytes(ctypes.byref(shape), ctypes.byref(nbytes)))
+        self.ws_bytes = nbytes.value
+        # the caching allocator hands out 512-byte aligned blocks
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=self.device)
+        _lib.check("moe_workspace_init",
+                   self.lib.moe_workspace_init(ctypes.byref(shape), _ptr(self.ws), self.ws_bytes, _stream()))
+
+    # -- sizes -------------------------------------------------------------
+    @property
+    def T(self):
+        return self.shape.T
+
+    @property
+    def k(self):
+        return self.shape.k
+
+    # -- moe_route ---------------------------------------------------------
+    def route(self, x: Optional[torch.Tensor], w_router: Optional[torch.Tensor],
+              logits: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        s, dev = self.shape, self.device
+        if x is None:
+            if logits is None:
+                raise ValueError("given-logits mode needs logits")
+            _need(logits, "logits", torch.float32, (s.T, s.E_total), dev)
+        else:
+            _need(x, "x", torch.bfloat16, (s.T, s.D), dev)
+            _need(w_router, "w_router", torch.bfloat16, (s.E_total, s.D), dev)
+            logits = torch.empty((s.T, s.E_total), dtype=torch.float32, device=dev)
+        idx = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
+        gate = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+        _lib.check("moe_route", self.lib.moe_route(ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(logits),
+                                                   _ptr(idx), _ptr(gate), _ptr(self.ws), self.ws_bytes, _stream()))
+        return logits, idx, gate
+
+    # -- moe_schedule ------------------------------------------------------
+    def schedule(self, routes: torch.Tensor) -> Dict[str, torch.Tensor]:
+        s, dev = self.shape, self.device
+        NK = s.T * s.k
+        routes = routes.reshape(s.num_src_ranks, NK)
+        _need(routes, "routes", torch.int32, (s.num_src_ranks, NK), dev)
+        L = s.experts_per_rank
+        out = {
+            "counts": torch.empty(L, dtype=torch.int32, device=dev),
+            "offsets": torch.empty(L + 1, dtype=torch.int32, device=dev),
+            "sched": torch.empty((max(s.max_rows, 1),), dtype=torch.int32, device=dev),
+            "route_dst": torch.empty(s.num_src_ranks * NK, dtype=torch.int32, device=dev),
+        }
+        _lib.check("moe_schedule", self.lib.moe_schedule(
+            ctypes.byref(s), _ptr(routes), _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["sched"]),
+            _ptr(out["route_dst"]), _ptr(self.ws), self.ws_bytes, _stream()))
+        return out
+
+    # -- moe_forward -------------------------------------------------------
+    def forward(self, weights: Dict[str, torch.Tensor], x_src: torch.Tensor, x_local: torch.Tensor,
+                gate: torch.Tensor, sched: Dict[str, torch.Tensor], out32: bool = True,
+                out: Optional[torch.Tensor] = None, out_f32: Optional[torch.Tensor] = None):
+        s, dev = self.shape, self.device
+        L, D, I, Is = s.experts_per_rank, s.D, s.I, s.I_shared
+        _need(x_local, "x_local", torch.bfloat16, (s.T, D), dev)
+        _need(x_src, "x_src", torch.bfloat16, (s.num_src_ranks * s.T, D), dev)
+        _need(gate, "gate", torch.float32, (s.T, s.k), dev)
+        w = _lib.MoeWeights()
+        if s.precision == _lib.MOE_BF16:
+            for n, shp in (("w_gate", (L, I, D)), ("w_up", (L, I, D)), ("w_down", (L, D, I))):
+                _need(weights[n], n, torch.bfloat16, shp, dev)
+                setattr(w, n, _ptr(weights[n]))
+        else:
+            for n, qn, sn, shp in (("w_gate", "q_gate", "s_gate", (L, I, D)), ("w_up", "q_up", "s_up", (L, I, D)),
+                                   ("w_down", "q_down", "s_down", (L, D, I))):
+                _need(weights[qn], qn, torch.uint8, shp, dev)
+                _need(weights[sn], sn, torch.uint8, shp[:-1] + (shp[-1] // 32,), dev)
+                setattr(w, n, _ptr(weights[qn]))
+                setattr(w, sn, _ptr(weights[sn]))
+        for n, shp in (("ws_gate", (Is, D)), ("ws_up", (Is, D)), ("ws_down", (D, Is))):
+            _need(weights[n], n, torch.bfloat16, shp, dev)
+            setattr(w, n, _ptr(weights[n]))
+        if out is None:
+            out = torch.empty((s.T, D), dtype=torch.bfloat16, device=dev)
+        _need(out, "out", torch.bfloat16, (s.T, D), dev)
+        if out32 and out_f32 is None:
+            out_f32 = torch.empty((s.T, D), dtype=torch.float32, device=dev)
+        if out_f32 is not None:
+            _need(out_f32, "out32", torch.float32, (s.T, D), dev)
+        _lib.check("moe_forward", self.lib.moe_forward(
+            ctypes.byref(s), ctypes.byref(w), _ptr(x_src), _ptr(x_local), _ptr(gate), _ptr(sched["offsets"]),
+            _ptr(sched["sched"]), _ptr(sched["route_dst"]), _ptr(out), _ptr(out_f32), _ptr(self.ws), self.ws_bytes,
+            _stream()))
+        return out, out_f32
+
+    # -- whole layer -------------------------------------------------------
+    def __call__(self, x: torch.Tensor, w_router: Optional[torch.Tensor], weights: Dict[str, torch.Tensor],
+                 logits: Optional[torch.Tensor] = None):
+        """route + schedule + forward for R = 1 (from x, or from given logits)."""
+        lg, idx, gate = self.route(None if logits is not None else x, w_router, logits)
+        sched = self.schedule(idx)
+        out, out32 = self.forward(weights, x, x, gate, sched)
+        return {"logits": lg, "idx": idx, "gate": gate, "out": out, "out32": out32, **sched}
+
+    def device_error(self) -> int:
+        code = ctypes.c_int32(0)
+        _lib.check("moe_get_device_error", self.lib.moe_get_device_error(
+            ctypes.byref(self.shape), _ptr(self.ws), self.ws_bytes, _stream(), ctypes.byref(code)))
+        return code.value
+
+
+def quantize_mxfp8(src: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MX-quantise a bf16 tensor along its last axis (moe_quantize_mxfp8)."""
+    lib = _lib.load()
+    if src.dtype != torch.bfloat16 or not src.is_contiguous() or src.device.type != "cuda":
+        raise ValueError("src must be a contiguous bf16 device tensor")
+    K = src.shape[-1]
+    rows = src.numel() // max(K, 1)
+    q = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
+    sc = torch.empty(src.shape[:-1] + (K // 32,), dtype=torch.uint8, device=src.device)
+    _lib.check("moe_quantize_mxfp8", lib.moe_quantize_mxfp8(_ptr(src), rows, K, _ptr(q), _ptr(sc), _stream()))
+    return q, sc

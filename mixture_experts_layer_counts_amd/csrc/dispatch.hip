@@ -1,0 +1,123 @@
+// Token movement on gfx950: gather into the ring buffer, and the combine.
+//
+// Gather (MoK paper "Mixture-of-Kittens: MoE Megakernel for NVL72s", §3.1
+// "Scheduling": dispatch walks the schedule table row by row, and rows land
+// directly in expert-contiguous buffer positions, with no other local copy;
+// §3.3: the destination is a fixed-size ring buffer).  Position p of the
+// schedule reads source row sched_src[p] / k and fills ring slot p mod C.
+// One wave copies one 2*D-byte row with 16-byte loads and stores.
+//
+// Combine (§2.1 MoE equation, router-weighted sum; §3.4 "Determinism": no
+// atomics, a fixed order): out32[t] = (sum over s in slot order of
+// fma(g[t,s], y[t,s], .)) + shared[t], in fp32; out = bf16(out32).
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ x_src, int64_t src_rows, int D,
+                                                     int k, const int32_t* __restrict__ sched_src,
+                                                     const int32_t* __restrict__ offsets, int L, int64_t p_begin,
+                                                     int64_t rows, int64_t ring_rows, uint16_t* __restrict__ ring,
+                                                     int* err) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (i >= rows) return;
+  const int64_t p = p_begin + i;
+  if (p >= offsets[L]) return;
+  const int32_t route = sched_src[p];
+  const int64_t src_row = route / k;
+  if (route < 0 || src_row >= src_rows) {  // a table not built by the schedule kernels
+    if (lane_id() == 0) raise_error(err, kErrExpertRange);
+    return;
+  }
+  const uint4* __restrict__ s = reinterpret_cast<const uint4*>(x_src + src_row * D);
+  uint4* __restrict__ d = reinterpret_cast<uint4*>(ring + (p % ring_rows) * D);
+  const int n = D / 8;
+  for (int c = lane_id(); c < n; c += kWave) d[c] = s[c];
+}
+
+hipError_t launch_gather(const uint16_t* x_src, int64_t src_rows, int D, int k, const int32_t* sched_src,
+                         const int32_t* offsets, int L, int64_t p_begin, int64_t rows, int64_t ring_rows,
+                         uint16_t* ring, int* err, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  gather_kernel<<<static_cast<unsigned>((rows + 3) / 4), 256, 0, stream>>>(x_src, src_rows, D, k, sched_src, offsets,
+                                                                           L, p_begin, rows, ring_rows, ring, err);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ Y, const float* __restrict__ sh,
+                                                      const float* __restrict__ gate,
+                                                      const int32_t* __restrict__ route_dst, int64_t route_base,
+                                                      int D, int k, int by_route_dst, uint16_t* __restrict__ out,
+                                                      float* __restrict__ out32) {
+  __shared__ int64_t row_s[16];
+  __shared__ float g_s[16];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < k) {
+    const int64_t j = static_cast<int64_t>(t) * k + tid;
+    g_s[tid] = gate[j];
+    row_s[tid] = by_route_dst ? static_cast<int64_t>(route_dst[route_base + j]) : j;
+  }
+  __syncthreads();
+  for (int c = tid * 8; c < D; c += 256 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int s = 0; s < k; ++s) {
+      const int64_t row = row_s[s];
+      if (row < 0) continue;  // a route to a remote expert: its row is summed where it returns
+      const uint4 y = *reinterpret_cast<const uint4*>(Y + row * D + c);
+      const float g = g_s[s];
+      const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(g, __uint_as_float(w[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(g, __uint_as_float(w[i] & 0xffff0000u), acc[2 * i + 1]);
+      }
+    }
+    const float4* shp = reinterpret_cast<const float4*>(sh + static_cast<int64_t>(t) * D + c);
+    const float4 s0 = shp[0], s1 = shp[1];
+    acc[0] += s0.x;
+    acc[1] += s0.y;
+    acc[2] += s0.z;
+    acc[3] += s0.w;
+    acc[4] += s1.x;
+    acc[5] += s1.y;
+    acc[6] += s1.z;
+    acc[7] += s1.w;
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(out + static_cast<int64_t>(t) * D + c) = o;
+    if (out32) {
+      float4* o32 = reinterpret_cast<float4*>(out32 + static_cast<int64_t>(t) * D + c);
+      o32[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      o32[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+hipError_t launch_combine(const uint16_t* Y, const float* shared_out, const float* gate, const int32_t* route_dst,
+                          int64_t route_base, int T, int D, int k, bool by_route_dst, uint16_t* out, float* out32,
+                          hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  combine_kernel<<<T, 256, 0, stream>>>(Y, shared_out, gate, route_dst, route_base, D, k, by_route_dst ? 1 : 0,
+                                        out, out32);
+  return hipGetLastError();
+}
+
+__global__ void clear_int_kernel(int* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_clear_int(int* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  clear_int_kernel<<<(n + 255) / 256, 256, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,75 @@
+// Host-side launchers of the gfx950 MoE kernels (internal to libmoe.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Workspace pieces used by the schedule kernels.
+struct SchedScratch {
+  int32_t* ord_local;  // [R*N*k] chunk-local ordinal of each route
+  int32_t* chunk_cnt;  // [R][n_chunks][L] histogram, then exclusive chunk base
+  int32_t* M;          // [R][L] routes per (source rank, local expert)
+};
+
+int sched_chunks(int NK);
+
+hipError_t launch_topk_gate(const float* logits, int T, int E, int k, int32_t* idx, float* gate, int* err,
+                            hipStream_t stream);
+
+hipError_t launch_schedule(const int32_t* routes, int R, int NK, int c, int L, int E_total, int64_t max_rows,
+                           int32_t* counts, int32_t* offsets, int32_t* sched_src, int32_t* route_dst,
+                           const SchedScratch& s, int* err, hipStream_t stream);
+
+hipError_t launch_build_tiles(const int32_t* offsets, int L, int64_t b, int64_t max_rows, int BM, int n_minibatches,
+                              int max_tiles, int4* tiles, int32_t* tile_count, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM  C[rows, N] = A[rows, K] * B[e][N, K]^T  (bf16 in, fp32 accumulate)
+// ---------------------------------------------------------------------------
+enum GemmEpilogue : int {
+  kEpiSwiGLU = 0,  // B0 = gate, B1 = up: C = bf16(SiLU(A B0^T) * (A B1^T))
+  kEpiBF16 = 1,    // C = bf16(A B0^T)
+  kEpiF32 = 2,     // C = A B0^T in fp32
+};
+
+struct GemmArgs {
+  const uint16_t* A;  // bf16; tile position p reads row (p - a_sub) mod a_mod
+  int64_t lda;
+  int64_t a_sub;
+  int64_t a_mod;
+  const uint16_t* B0;  // bf16 [experts][N][K]
+  const uint16_t* B1;  // second operand of the SwiGLU epilogue (same layout)
+  int64_t b_expert_stride;
+  int N;
+  int K;
+  void* C;  // output row = c_idx ? c_idx[p] : p - c_sub
+  int64_t ldc;
+  const int32_t* c_idx;
+  int64_t c_sub;
+  const int4* tiles;         // routed: {expert, p0, rows, 0}; NULL: dense rows 0..dense_rows-1
+  const int32_t* tile_count;  // routed: number of valid tiles
+  int dense_rows;
+  int max_tiles;
+};
+
+// Tile rows of the routed GEMM kernels (tile lists are built with it).
+int gemm_routed_bm();
+hipError_t launch_gemm(const GemmArgs& args, int epilogue, hipStream_t stream);
+int gemm_tiles_bound(int64_t rows, int groups, int bm);
+
+// ---------------------------------------------------------------------------
+// Data movement
+// ---------------------------------------------------------------------------
+hipError_t launch_gather(const uint16_t* x_src, int64_t src_rows, int D, int k, const int32_t* sched_src,
+                         const int32_t* offsets, int L, int64_t p_begin, int64_t rows, int64_t ring_rows,
+                         uint16_t* ring, int* err, hipStream_t stream);
+
+hipError_t launch_combine(const uint16_t* Y, const float* shared_out, const float* gate, const int32_t* route_dst,
+                          int64_t route_base, int T, int D, int k, bool by_route_dst, uint16_t* out, float* out32,
+                          hipStream_t stream);
+
+hipError_t launch_clear_int(int* p, int n, hipStream_t stream);
+
+}  // namespace moe

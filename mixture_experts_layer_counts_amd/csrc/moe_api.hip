@@ -1,0 +1,406 @@
+// C ABI of libmoe.so: shape validation, workspace carving and the stream-ordered
+// launch sequence of the MoE-layer forward.  See include/moe.h for the contract.
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t err, ord_local, chunk_cnt, M, tiles, tile_count, ring, h, Y, h_shared, shared_out, total;
+  int64_t n_minibatches;
+  int max_tiles;
+  int64_t y_rows;
+};
+
+bool valid_shape(const moe_shape* s, moe_status* why) {
+  *why = MOE_ERR_INVALID_ARG;
+  if (!s) return false;
+  if (s->reserved != 0) return false;
+  if (s->T < 0 || s->D <= 0 || s->I <= 0 || s->I_shared <= 0 || s->E_total <= 0 || s->k <= 0) return false;
+  if (s->k > s->E_total) return false;
+  if (s->num_src_ranks < 1 || s->rank < 0 || s->rank >= s->num_src_ranks) return false;
+  if (s->experts_per_rank < 1 || s->num_src_ranks * s->experts_per_rank != s->E_total) return false;
+  if (s->tokens_per_src_rank != s->T) return false;
+  if (s->minibatch_rows < 1 || s->ring_rows < s->minibatch_rows || s->ring_rows % s->minibatch_rows != 0)
+    return false;
+  if (s->max_rows < 0) return false;
+  if (s->num_src_ranks == 1 && s->max_rows != s->T * s->k) return false;
+  if (s->max_rows > s->num_src_ranks * s->T * s->k) return false;
+  if (s->precision != MOE_BF16 && s->precision != MOE_MXFP8) return false;
+  *why = MOE_ERR_UNSUPPORTED;
+  if (s->D % 64 || s->I % 64 || s->I_shared % 64) return false;
+  if (s->k > 16 || s->E_total > 1024 || s->experts_per_rank > 1024) return false;
+  if (s->num_src_ranks * s->T * s->k >= (int64_t(1) << 31)) return false;
+  if (s->max_rows >= (int64_t(1) << 31) || s->T >= (int64_t(1) << 31)) return false;
+  if (s->D > 65536 || s->I > 65536 || s->I_shared > 65536) return false;
+  *why = MOE_OK;
+  return true;
+}
+
+Layout layout_of(const moe_shape* s) {
+  Layout L{};
+  const int64_t R = s->num_src_ranks, NK = s->T * s->k, Lx = s->experts_per_rank;
+  const int bm = moe::gemm_routed_bm();
+  L.n_minibatches = s->max_rows > 0 ? (s->max_rows + s->minibatch_rows - 1) / s->minibatch_rows : 0;
+  L.max_tiles = moe::gemm_tiles_bound(std::min<int64_t>(s->minibatch_rows, std::max<int64_t>(s->max_rows, 1)),
+                                      static_cast<int>(Lx), bm);
+  L.y_rows = (R == 1) ? NK : s->max_rows;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.err = take(sizeof(int32_t));
+  L.ord_local = take(sizeof(int32_t) * R * NK);
+  L.chunk_cnt = take(sizeof(int32_t) * R * moe::sched_chunks(static_cast<int>(NK)) * Lx);
+  L.M = take(sizeof(int32_t) * R * Lx);
+  L.tiles = take(sizeof(int4) * L.n_minibatches * L.max_tiles);
+  L.tile_count = take(sizeof(int32_t) * std::max<int64_t>(L.n_minibatches, 1));
+  L.ring = take(sizeof(uint16_t) * s->ring_rows * s->D);
+  L.h = take(sizeof(uint16_t) * s->minibatch_rows * s->I);
+  L.Y = take(sizeof(uint16_t) * L.y_rows * s->D);
+  L.h_shared = take(sizeof(uint16_t) * s->T * s->I_shared);
+  L.shared_out = take(sizeof(float) * s->T * s->D);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY_HIP(expr)                       \
+  do {                                          \
+    const hipError_t e_ = (expr);               \
+    if (e_ != hipSuccess) return MOE_ERR_HIP;   \
+  } while (0)
+
+// Benchmark probe: event pairs around the launches of one kernel.
+struct Probe {
+  int kernel = -1;
+  int max_launches = 0;
+  int used = 0;
+  std::vector<hipEvent_t> start, stop;
+};
+Probe g_probe;
+
+struct ProbeScope {  // records around one launch of `kernel` when the probe asks for it
+  int slot = -1;
+  hipStream_t stream;
+  ProbeScope(int kernel, hipStream_t s) : stream(s) {
+    if (g_probe.kernel == kernel && g_probe.used < g_probe.max_launches) {
+      slot = g_probe.used++;
+      (void)hipEventRecord(g_probe.start[slot], stream);
+    }
+  }
+  ~ProbeScope() {
+    if (slot >= 0) (void)hipEventRecord(g_probe.stop[slot], stream);
+  }
+};
+
+moe_status check_ws(const moe_shape* s, const void* ws, size_t ws_bytes, Layout* L) {
+  moe_status why;
+  if (!valid_shape(s, &why)) return why;
+  *L = layout_of(s);
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < L->total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status st) {
+  switch (st) {
+    case MOE_OK:
+      return "ok";
+    case MOE_ERR_INVALID_ARG:
+      return "invalid argument";
+    case MOE_ERR_UNSUPPORTED:
+      return "unsupported shape or precision";
+    case MOE_ERR_WORKSPACE:
+      return "workspace too small";
+    case MOE_ERR_HIP:
+      return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+moe_status moe_workspace_bytes(const moe_shape* shape, size_t* bytes) {
+  moe_status why;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  if (!valid_shape(shape, &why)) return why;
+  *bytes = layout_of(shape).total;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_init(const moe_shape* shape, void* ws, size_t ws_bytes, void* stream) {
+  Layout L;
+  const moe_status st = check_ws(shape, ws, ws_bytes, &L);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_clear_int(at<int>(ws, L.err), 1, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router, float* logits, int32_t* topk_idx,
+                     float* topk_gate, void* ws, size_t ws_bytes, void* stream) {
+  Layout L;
+  const moe_status st = check_ws(shape, ws, ws_bytes, &L);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_idx || !topk_gate || (x && !w_router)) return MOE_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = static_cast<int>(shape->T), E = static_cast<int>(shape->E_total), k = static_cast<int>(shape->k);
+  if (T == 0) return MOE_OK;
+  if (x) {
+    moe::GemmArgs g{};
+    g.A = static_cast<const uint16_t*>(x);
+    g.lda = shape->D;
+    g.a_sub = 0;
+    g.a_mod = INT64_MAX;
+    g.B0 = static_cast<const uint16_t*>(w_router);
+    g.B1 = nullptr;
+    g.b_expert_stride = 0;
+    g.N = E;
+    g.K = static_cast<int>(shape->D);
+    g.C = logits;
+    g.ldc = E;
+    g.c_idx = nullptr;
+    g.c_sub = 0;
+    g.tiles = nullptr;
+    g.tile_count = nullptr;
+    g.dense_rows = T;
+    ProbeScope probe(MOE_K_ROUTER_GEMM, s);
+    MOE_TRY_HIP(moe::launch_gemm(g, moe::kEpiF32, s));
+  }
+  ProbeScope probe(MOE_K_TOPK, s);
+  return hip_status(moe::launch_topk_gate(logits, T, E, k, topk_idx, topk_gate, at<int>(ws, L.err), s));
+}
+
+moe_status moe_schedule(const moe_shape* shape, const int32_t* routes, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* sched_src, int32_t* route_dst, void* ws, size_t ws_bytes,
+                        void* stream) {
+  Layout L;
+  const moe_status st = check_ws(shape, ws, ws_bytes, &L);
+  if (st != MOE_OK) return st;
+  const int64_t NK = shape->T * shape->k;
+  if (!expert_counts || !expert_offsets || !route_dst || (NK > 0 && !routes) || (shape->max_rows > 0 && !sched_src))
+    return MOE_ERR_INVALID_ARG;
+  moe::SchedScratch sc{at<int32_t>(ws, L.ord_local), at<int32_t>(ws, L.chunk_cnt), at<int32_t>(ws, L.M)};
+  ProbeScope probe(MOE_K_SCHEDULE, static_cast<hipStream_t>(stream));
+  return hip_status(moe::launch_schedule(
+      routes, static_cast<int>(shape->num_src_ranks), static_cast<int>(NK), static_cast<int>(shape->rank),
+      static_cast<int>(shape->experts_per_rank), static_cast<int>(shape->E_total), shape->max_rows, expert_counts,
+      expert_offsets, sched_src, route_dst, sc, at<int>(ws, L.err), static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void* x_src, const void* x_local,
+                       const float* topk_gate, const int32_t* expert_offsets, const int32_t* sched_src,
+                       const int32_t* route_dst, void* out, float* out32, void* ws, size_t ws_bytes,
+                       void* stream) {
+  Layout L;
+  const moe_status st = check_ws(shape, ws, ws_bytes, &L);
+  if (st != MOE_OK) return st;
+  if (shape->precision != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!w || !w->w_gate || !w->w_up || !w->w_down || !w->ws_gate || !w->ws_up || !w->ws_down) return MOE_ERR_INVALID_ARG;
+  if (!expert_offsets || !route_dst || !topk_gate || !out) return MOE_ERR_INVALID_ARG;
+  if (shape->T > 0 && !x_local) return MOE_ERR_INVALID_ARG;
+  if (shape->max_rows > 0 && (!x_src || !sched_src)) return MOE_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = static_cast<int>(shape->T), D = static_cast<int>(shape->D), I = static_cast<int>(shape->I);
+  const int Is = static_cast<int>(shape->I_shared), k = static_cast<int>(shape->k);
+  const int Lx = static_cast<int>(shape->experts_per_rank);
+  const int64_t b = shape->minibatch_rows, C = shape->ring_rows, R = shape->num_src_ranks;
+  if (T == 0 && shape->max_rows == 0) return MOE_OK;
+
+  uint16_t* ring = at<uint16_t>(ws, L.ring);
+  uint16_t* h = at<uint16_t>(ws, L.h);
+  uint16_t* Y = at<uint16_t>(ws, L.Y);
+  uint16_t* h_sh = at<uint16_t>(ws, L.h_shared);
+  float* sh_out = at<float>(ws, L.shared_out);
+  int4* tiles = at<int4>(ws, L.tiles);
+  int32_t* tile_count = at<int32_t>(ws, L.tile_count);
+  const int bm = moe::gemm_routed_bm();
+
+  // 1. tile lists of every minibatch, from the device-side expert offsets
+  {
+    ProbeScope probe(MOE_K_TILES, s);
+    MOE_TRY_HIP(moe::launch_build_tiles(expert_offsets, Lx, b, shape->max_rows, bm,
+                                        static_cast<int>(L.n_minibatches), L.max_tiles,
+                                        tiles, tile_count, s));
+  }
+
+  // 2. shared expert on this rank's tokens (MoK paper §3.4, "Shared Expert":
+  //    it needs no dispatch, so it goes first)
+  if (T > 0) {
+    moe::GemmArgs g{};
+    g.A = static_cast<const uint16_t*>(x_local);
+    g.lda = D;
+    g.a_sub = 0;
+    g.a_mod = INT64_MAX;
+    g.B0 = static_cast<const uint16_t*>(w->ws_gate);
+    g.B1 = static_cast<const uint16_t*>(w->ws_up);
+    g.b_expert_stride = 0;
+    g.N = Is;
+    g.K = D;
+    g.C = h_sh;
+    g.ldc = Is;
+    g.dense_rows = T;
+    {
+      ProbeScope probe(MOE_K_SHARED_UP, s);
+      MOE_TRY_HIP(moe::launch_gemm(g, moe::kEpiSwiGLU, s));
+    }
+    moe::GemmArgs d{};
+    d.A = h_sh;
+    d.lda = Is;
+    d.a_sub = 0;
+    d.a_mod = INT64_MAX;
+    d.B0 = static_cast<const uint16_t*>(w->ws_down);
+    d.b_expert_stride = 0;
+    d.N = D;
+    d.K = Is;
+    d.C = sh_out;
+    d.ldc = D;
+    d.dense_rows = T;
+    ProbeScope probe(MOE_K_SHARED_DOWN, s);
+    MOE_TRY_HIP(moe::launch_gemm(d, moe::kEpiF32, s));
+  }
+
+  // 3. routed experts, one minibatch of b schedule rows at a time
+  for (int64_t m = 0; m < L.n_minibatches; ++m) {
+    const int64_t p_begin = m * b;
+    const int64_t rows = std::min<int64_t>(b, shape->max_rows - p_begin);
+    {
+      ProbeScope probe(MOE_K_GATHER, s);
+      MOE_TRY_HIP(moe::launch_gather(static_cast<const uint16_t*>(x_src), R * shape->T, D, k, sched_src,
+                                     expert_offsets, Lx, p_begin, rows, C, ring, at<int>(ws, L.err), s));
+    }
+    moe::GemmArgs u{};
+    u.A = ring;
+    u.lda = D;
+    u.a_sub = 0;
+    u.a_mod = C;
+    u.B0 = static_cast<const uint16_t*>(w->w_gate);
+    u.B1 = static_cast<const uint16_t*>(w->w_up);
+    u.b_expert_stride = static_cast<int64_t>(I) * D;
+    u.N = I;
+    u.K = D;
+    u.C = h;
+    u.ldc = I;
+    u.c_idx = nullptr;
+    u.c_sub = p_begin;
+    u.tiles = tiles + m * L.max_tiles;
+    u.tile_count = tile_count + m;
+    u.max_tiles = L.max_tiles;
+    {
+      ProbeScope probe(MOE_K_UP_GATE, s);
+      MOE_TRY_HIP(moe::launch_gemm(u, moe::kEpiSwiGLU, s));
+    }
+    moe::GemmArgs d{};
+    d.A = h;
+    d.lda = I;
+    d.a_sub = p_begin;
+    d.a_mod = INT64_MAX;
+    d.B0 = static_cast<const uint16_t*>(w->w_down);
+    d.b_expert_stride = static_cast<int64_t>(D) * I;
+    d.N = D;
+    d.K = I;
+    d.C = Y;
+    d.ldc = D;
+    d.c_idx = (R == 1) ? sched_src : nullptr;  // push each row back to its route (§3.1 table reuse)
+    d.c_sub = 0;
+    d.tiles = tiles + m * L.max_tiles;
+    d.tile_count = tile_count + m;
+    d.max_tiles = L.max_tiles;
+    ProbeScope probe(MOE_K_DOWN, s);
+    MOE_TRY_HIP(moe::launch_gemm(d, moe::kEpiBF16, s));
+  }
+
+  // 4. fixed-order gate-weighted combine
+  ProbeScope probe(MOE_K_COMBINE, s);
+  return hip_status(moe::launch_combine(Y, sh_out, topk_gate, route_dst, shape->rank * T * static_cast<int64_t>(k), T,
+                                        D, k, R > 1, static_cast<uint16_t*>(out), out32, s));
+}
+
+moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale, void* stream) {
+  (void)src;
+  (void)rows;
+  (void)K;
+  (void)q;
+  (void)scale;
+  (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+moe_status moe_probe_begin(int32_t kernel_id, int32_t max_launches) {
+  if (kernel_id < 0 || kernel_id >= MOE_K_COUNT || max_launches < 1 || max_launches > (1 << 20))
+    return MOE_ERR_INVALID_ARG;
+  double ms;
+  int32_t n;
+  if (g_probe.kernel >= 0) moe_probe_end(&ms, &n);
+  g_probe.start.assign(max_launches, nullptr);
+  g_probe.stop.assign(max_launches, nullptr);
+  for (int i = 0; i < max_launches; ++i) {
+    if (hipEventCreate(&g_probe.start[i]) != hipSuccess || hipEventCreate(&g_probe.stop[i]) != hipSuccess) {
+      g_probe.max_launches = i;
+      g_probe.kernel = kernel_id;
+      moe_probe_end(&ms, &n);
+      return MOE_ERR_HIP;
+    }
+  }
+  g_probe.kernel = kernel_id;
+  g_probe.max_launches = max_launches;
+  g_probe.used = 0;
+  return MOE_OK;
+}
+
+moe_status moe_probe_end(double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return MOE_ERR_INVALID_ARG;
+  *total_ms = 0.0;
+  *launches = 0;
+  moe_status st = MOE_OK;
+  if (g_probe.kernel >= 0 && g_probe.used > 0) {
+    if (hipDeviceSynchronize() != hipSuccess) st = MOE_ERR_HIP;
+    for (int i = 0; i < g_probe.used && st == MOE_OK; ++i) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, g_probe.start[i], g_probe.stop[i]) != hipSuccess) st = MOE_ERR_HIP;
+      *total_ms += ms;
+    }
+    *launches = g_probe.used;
+  }
+  for (size_t i = 0; i < g_probe.start.size(); ++i) {
+    if (g_probe.start[i]) (void)hipEventDestroy(g_probe.start[i]);
+    if (g_probe.stop[i]) (void)hipEventDestroy(g_probe.stop[i]);
+  }
+  g_probe = Probe{};
+  return st;
+}
+
+moe_status moe_get_device_error(const moe_shape* shape, const void* ws, size_t ws_bytes, void* stream,
+                                int32_t* host_code) {
+  Layout L;
+  const moe_status st = check_ws(shape, ws, ws_bytes, &L);
+  if (st != MOE_OK) return st;
+  if (!host_code) return MOE_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY_HIP(hipMemcpyAsync(host_code, static_cast<const char*>(ws) + L.err, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  return hip_status(hipStreamSynchronize(s));
+}
+
+}  // extern "C"

@@ -1,0 +1,225 @@
+// Dispatch schedule (MoK paper "Mixture-of-Kittens: MoE Megakernel for
+// NVL72s", §3.1 "Scheduling", Algorithm 1) and the per-minibatch GEMM tile
+// lists derived from it, on gfx950.
+//
+// Algorithm 1 orders the local routes by expert l first, then by ordinal o
+// (how many routes from rank r to expert l precede this one), then by source
+// rank r; its closed form places route (r, j) at
+//   S_l + sum_{r'} min(M[r'][l], o) + #{r' < r : M[r'][l] > o}.
+// Three kernels build it without order-dependent atomics:
+//   count : per chunk of a source rank's routes, the chunk-local ordinal of
+//           every local route (wave ballots + per-wave counts in LDS, taken in
+//           wave order) and the chunk's per-expert histogram;
+//   scan  : per (r, l) exclusive prefix over chunks -> chunk bases and M[r][l];
+//           counts and expert offsets S_l (block-wide scan);
+//   place : o = chunk base + local ordinal, then the closed form above; writes
+//           the table row and its inverse.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kSchedChunk = 1024;  // routes per count block
+constexpr int kMaxExperts = 1024;
+
+// Exclusive scan of one int per thread over a block of 1024 threads.
+__device__ int block_exclusive_scan_1024(int v, int* total) {
+  __shared__ int wave_sum[16];
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) wave_sum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < 16 ? wave_sum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int y = __shfl_up(s, off);
+      if (lane >= off) s += y;
+    }
+    if (lane < 16) wave_sum[lane] = s;  // inclusive prefix of wave totals
+  }
+  __syncthreads();
+  const int before = (w > 0 ? wave_sum[w - 1] : 0) + x - v;
+  if (total) *total = wave_sum[15];
+  __syncthreads();
+  return before;
+}
+
+__global__ __launch_bounds__(256) void sched_count_kernel(const int32_t* __restrict__ A, int NK, int c, int L,
+                                                          int E_total, int nch, int32_t* __restrict__ ord_local,
+                                                          int32_t* __restrict__ chunk_cnt, int* err) {
+  __shared__ int run[kMaxExperts];
+  __shared__ int wcnt[4][kMaxExperts];
+  const int r = blockIdx.y, ch = blockIdx.x;
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  for (int i = tid; i < L; i += 256) {
+    run[i] = 0;
+    wcnt[0][i] = wcnt[1][i] = wcnt[2][i] = wcnt[3][i] = 0;
+  }
+  __syncthreads();
+  const int nbits = 32 - __clz(L);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int sub = 0; sub < kSchedChunk / 256; ++sub) {
+    const int j = ch * kSchedChunk + sub * 256 + tid;
+    int l = -1;
+    if (j < NK) {
+      const int a = A[static_cast<int64_t>(r) * NK + j];
+      if (a < 0 || a >= E_total)
+        raise_error(err, kErrExpertRange);
+      else if (a >= c * L && a < c * L + L)
+        l = a - c * L;
+    }
+    // lanes of this wave routed to the same local expert
+    uint64_t same = __ballot(l >= 0);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = (l >> bit) & 1;
+      const uint64_t bal = __ballot(set);
+      same &= set ? bal : ~bal;
+    }
+    const int rank = __popcll(same & lt_mask);
+    if (l >= 0 && rank == 0) wcnt[w][l] = __popcll(same);
+    __syncthreads();
+    if (l >= 0) {
+      int o = run[l] + rank;
+      for (int w2 = 0; w2 < w; ++w2) o += wcnt[w2][l];
+      ord_local[static_cast<int64_t>(r) * NK + j] = o;
+    }
+    __syncthreads();
+    for (int i = tid; i < L; i += 256) {
+      run[i] += wcnt[0][i] + wcnt[1][i] + wcnt[2][i] + wcnt[3][i];
+      wcnt[0][i] = wcnt[1][i] = wcnt[2][i] = wcnt[3][i] = 0;
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < L; i += 256) chunk_cnt[(static_cast<int64_t>(r) * nch + ch) * L + i] = run[i];
+}
+
+__global__ __launch_bounds__(1024) void sched_scan_kernel(int R, int L, int nch, int NK, int32_t* __restrict__ chunk_cnt,
+                                                          int32_t* __restrict__ Mmat, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets, int64_t max_rows, int* err) {
+  const int tid = threadIdx.x;
+  for (int pair = tid; pair < R * L; pair += 1024) {
+    const int r = pair / L, l = pair % L;
+    int base = 0;
+    for (int ch = 0; ch < (NK > 0 ? nch : 0); ++ch) {  // no count pass ran when there are no routes
+      const int64_t ix = (static_cast<int64_t>(r) * nch + ch) * L + l;
+      const int cnt = chunk_cnt[ix];
+      chunk_cnt[ix] = base;
+      base += cnt;
+    }
+    Mmat[pair] = base;
+  }
+  __syncthreads();
+  int cnt = 0;
+  if (tid < L) {
+    for (int r = 0; r < R; ++r) cnt += Mmat[r * L + tid];
+    counts[tid] = cnt;
+  }
+  int total = 0;
+  const int start = block_exclusive_scan_1024(cnt, &total);
+  if (tid < L) offsets[tid] = start;
+  if (tid == 0) {
+    offsets[L] = total;
+    if (total > max_rows) raise_error(err, kErrRowOverflow);
+  }
+}
+
+__global__ __launch_bounds__(256) void sched_place_kernel(const int32_t* __restrict__ A, int R, int NK, int c, int L,
+                                                          int nch, const int32_t* __restrict__ ord_local,
+                                                          const int32_t* __restrict__ chunk_base,
+                                                          const int32_t* __restrict__ Mmat,
+                                                          const int32_t* __restrict__ offsets, int64_t max_rows,
+                                                          int32_t* __restrict__ sched_src,
+                                                          int32_t* __restrict__ route_dst, int* err) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= static_cast<int64_t>(R) * NK) return;
+  const int r = static_cast<int>(gid / NK), j = static_cast<int>(gid % NK);
+  const int a = A[gid];
+  if (a < c * L || a >= c * L + L) {
+    route_dst[gid] = -1;
+    return;
+  }
+  const int l = a - c * L;
+  const int o = chunk_base[(static_cast<int64_t>(r) * nch + j / kSchedChunk) * L + l] + ord_local[gid];
+  int p = 0;
+  for (int r2 = 0; r2 < R; ++r2) {
+    const int m = Mmat[r2 * L + l];
+    p += m < o ? m : o;
+    if (r2 < r && m > o) ++p;
+  }
+  const int64_t pos = static_cast<int64_t>(offsets[l]) + p;
+  if (pos < max_rows) {
+    sched_src[pos] = static_cast<int32_t>(gid);
+    route_dst[gid] = static_cast<int32_t>(pos);
+  } else {
+    route_dst[gid] = -1;
+    raise_error(err, kErrRowOverflow);
+  }
+}
+
+hipError_t launch_schedule(const int32_t* routes, int R, int NK, int c, int L, int E_total, int64_t max_rows,
+                           int32_t* counts, int32_t* offsets, int32_t* sched_src, int32_t* route_dst,
+                           const SchedScratch& s, int* err, hipStream_t stream) {
+  const int nch = sched_chunks(NK);
+  if (NK > 0) {
+    sched_count_kernel<<<dim3(nch, R), 256, 0, stream>>>(routes, NK, c, L, E_total, nch, s.ord_local, s.chunk_cnt,
+                                                         err);
+  }
+  sched_scan_kernel<<<1, 1024, 0, stream>>>(R, L, nch, NK, s.chunk_cnt, s.M, counts, offsets, max_rows, err);
+  const int64_t n = static_cast<int64_t>(R) * NK;
+  if (n > 0) {
+    sched_place_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(
+        routes, R, NK, c, L, nch, s.ord_local, s.chunk_cnt, s.M, offsets, max_rows, sched_src, route_dst, err);
+  }
+  return hipGetLastError();
+}
+
+int sched_chunks(int NK) { return NK > 0 ? (NK + kSchedChunk - 1) / kSchedChunk : 1; }
+
+// ----------------------------------------------------------------------------
+// Tile lists: for minibatch m (positions m*b .. min(m*b+b, P)-1), every expert
+// segment that overlaps it is cut into row tiles of at most BM rows, in expert
+// order.  Entry = {expert, first position, rows, 0}.
+// ----------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int L, int64_t b,
+                                                           int64_t max_rows, int BM, int max_tiles,
+                                                           int4* __restrict__ tiles, int32_t* __restrict__ tile_count) {
+  const int m = blockIdx.x, l = threadIdx.x;
+  // rows past max_rows were never placed (the schedule flagged the overflow)
+  const int64_t P = offsets[L] < max_rows ? offsets[L] : max_rows;
+  const int64_t lo = static_cast<int64_t>(m) * b;
+  const int64_t hi = lo + b < P ? lo + b : P;
+  int64_t s_lo = 0, s_hi = 0;
+  int n = 0;
+  if (l < L) {
+    s_lo = offsets[l] > lo ? offsets[l] : lo;
+    s_hi = offsets[l + 1] < hi ? offsets[l + 1] : hi;
+    if (s_hi > s_lo) n = static_cast<int>((s_hi - s_lo + BM - 1) / BM);
+  }
+  int total = 0;
+  const int start = block_exclusive_scan_1024(n, &total);
+  int4* out = tiles + static_cast<int64_t>(m) * max_tiles;
+  for (int i = 0; i < n; ++i) {
+    if (start + i >= max_tiles) break;
+    const int64_t p0 = s_lo + static_cast<int64_t>(i) * BM;
+    const int64_t rows = s_hi - p0 < BM ? s_hi - p0 : BM;
+    out[start + i] = make_int4(l, static_cast<int>(p0), static_cast<int>(rows), 0);
+  }
+  if (l == 0) tile_count[m] = total < max_tiles ? total : max_tiles;
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int L, int64_t b, int64_t max_rows, int BM, int n_minibatches,
+                              int max_tiles, int4* tiles, int32_t* tile_count, hipStream_t stream) {
+  if (n_minibatches <= 0) return hipSuccess;
+  build_tiles_kernel<<<n_minibatches, 1024, 0, stream>>>(offsets, L, b, max_rows, BM, max_tiles, tiles, tile_count);
+  return hipGetLastError();
+}
+
+}  // namespace moe

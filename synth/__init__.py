@@ -200,3 +200,18 @@ def zipf_counts(total: int, L: int, s: float) -> list:
     order = np.argsort(-(q - base), kind="stable")
     base[order[:rem]] += 1
     return base.tolist()
+
+
+def random_routes(R: int, N: int, K: int, E_total: int, seed: int, skew: Optional[float] = None) -> np.ndarray:
+    """Route matrix A [R, N*K]: each token draws K distinct experts, uniformly
+    or with Zipf(skew) weights (expert e has weight (e+1)^-skew)."""
+    rng = np.random.default_rng(_seed(seed, "routes", R, N, K, E_total, skew))
+    p = None
+    if skew is not None:
+        p = np.arange(1, E_total + 1, dtype=np.float64) ** (-skew)
+        p /= p.sum()
+    A = np.empty((R, N * K), dtype=np.int32)
+    for r in range(R):
+        for t in range(N):
+            A[r, t * K:(t + 1) * K] = rng.choice(E_total, size=K, replace=False, p=p)
+    return A

@@ -1,0 +1,58 @@
+"""Helpers shared by the GPU parity tests (not collected by pytest)."""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe as ref
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from mixture_experts_layer_counts_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):  # the HIP path has no fallback: a missing build is a failure
+        pytest.fail(f"{_lib.LIB_PATH} not built")
+    return torch.device("cuda", 0)
+
+
+def say(*msg):
+    print("[gpu-case]", *msg, file=sys.stderr, flush=True)
+
+
+def host_weights(inp):
+    return {n: synth.bits(t) for n, t in inp.items() if t.dtype == torch.bfloat16}
+
+
+def to_dev(inp, dev):
+    return {n: t.to(dev) for n, t in inp.items()}
+
+
+def layer(w: synth.Workload, dev, b=None, C=None, R=1):
+    from mixture_experts_layer_counts_amd import MoELayer, shape_for
+    return MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C),
+                    device=dev)
+
+
+def rel_err(got, want):
+    """max|got - want| / RMS(want)."""
+    want = np.asarray(want, dtype=np.float64)
+    return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - want)) / np.sqrt(np.mean(want ** 2)))
+
+
+def gate_tolerance(logits_sel: np.ndarray, k: int) -> np.ndarray:
+    """Relative bound on a gate computed in fp32 from fp32 logits:
+    u * (2 * max_s |l_s - l_0| + k + 8), u = 2^-24 (the subtraction, the
+    exponential's few-ulp error, the k-term sum and the division)."""
+    d = np.abs(logits_sel - logits_sel[:, :1]).max(axis=1, keepdims=True)
+    return 2.0 ** -24 * (2.0 * d + k + 8)
+
+
+def oracle_layer(w: synth.Workload, inp, logits_np, tokens=None):
+    return ref.forward(synth.bits(inp["x"]), host_weights(inp), logits_np, w.k, tokens=tokens)

@@ -1,0 +1,94 @@
+"""The C ABI on the CPU: libmoe.so loads, exports every function include/moe.h
+declares, and its host-side validation answers without touching a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_counts_amd import _lib, shape_for
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from mixture_experts_layer_counts_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = _lib.header_functions()
+    assert {"moe_route", "moe_schedule", "moe_forward", "moe_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    # and the binding declares a signature for each
+    assert set(names) == set(_lib._SIGS)
+
+
+def test_abi_version_matches_header(lib):
+    v = int(re.search(r"#define MOE_ABI_VERSION (\d+)", open(_lib.HEADER).read()).group(1))
+    assert lib.moe_abi_version() == v
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.moe_status_str(code)
+    assert lib.moe_status_str(-99) == b"unknown status"
+
+
+def ws_bytes(lib, s):
+    n = ctypes.c_size_t(0)
+    st = lib.moe_workspace_bytes(ctypes.byref(s), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes(lib):
+    s = shape_for(T=8192, D=7168, I=2048, E=256, k=8, minibatch_rows=8192, ring_rows=8192)
+    st, n = ws_bytes(lib, s)
+    assert st == 0
+    # at least ring + h + routed outputs + shared h + shared fp32 output
+    need = 8192 * 7168 * 2 + 8192 * 2048 * 2 + 65536 * 7168 * 2 + 8192 * 2048 * 2 + 8192 * 7168 * 4
+    assert need <= n < need * 1.05
+    # a larger ring needs more
+    s2 = shape_for(T=8192, D=7168, I=2048, E=256, k=8, minibatch_rows=8192, ring_rows=16384)
+    assert ws_bytes(lib, s2)[1] > n
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("D", 100, -2),             # not a multiple of 64
+    ("I", 96, -2),
+    ("k", 0, -1),
+    ({"k": 17, "max_rows": 64 * 17}, None, -2),  # more than 16 routes per token
+    ("E_total", 2000, -1),      # R * L != E_total
+    ("minibatch_rows", 0, -1),
+    ("ring_rows", 1000, -1),    # not a multiple of b
+    ("max_rows", 5, -1),        # R == 1 needs T*k
+    ("precision", 7, -1),
+    ("reserved", 1, -1),
+    ("tokens_per_src_rank", 3, -1),
+])
+def test_invalid_shapes_are_rejected(lib, field, value, code):
+    s = shape_for(T=64, D=128, I=64, E=32, k=2, minibatch_rows=32, ring_rows=64)
+    assert ws_bytes(lib, s)[0] == 0
+    for f, v in (field.items() if isinstance(field, dict) else [(field, value)]):
+        setattr(s, f, v)
+    assert ws_bytes(lib, s)[0] == code
+
+
+def test_calls_validate_before_launching(lib):
+    s = shape_for(T=64, D=128, I=64, E=8, k=2)
+    st, n = ws_bytes(lib, s)
+    fake = ctypes.c_void_p(4096)  # never dereferenced: every call below returns first
+    # workspace too small
+    assert lib.moe_route(ctypes.byref(s), fake, fake, fake, fake, fake, fake, n - 1, None) == -3
+    # misaligned workspace
+    assert lib.moe_schedule(ctypes.byref(s), fake, fake, fake, fake, fake, ctypes.c_void_p(4097), n, None) == -1
+    # null outputs
+    assert lib.moe_route(ctypes.byref(s), fake, fake, None, fake, fake, fake, n, None) == -1
+    w = _lib.MoeWeights()
+    assert lib.moe_forward(ctypes.byref(s), ctypes.byref(w), fake, fake, fake, fake, fake, fake, fake, None, fake,
+                           n, None) == -1
+    # null shape
+    assert lib.moe_workspace_bytes(None, ctypes.byref(ctypes.c_size_t())) == -1

@@ -1,8 +1,8 @@
 """Pins of the oracle's dispatch schedule (Algorithm 1 of the MoK paper).
 
 The paper gives two descriptions of the same table: Algorithm 1's closed form
-for the position p, and "sort the routes by the key (local expert, ordinal,
-source rank)" (§3.1 "Scheduling").  Each one checks the other.  On top of
+for the position p, and (§3.1 "Scheduling") an ordering of the routes by
+local expert, then per-rank ordinal, then source rank.  Each one checks the other.  On top of
 that: library routines (bincount, stable argsort) and the properties the
 table must have (a bijection onto expert-contiguous regions, source ranks
 interleaved round-robin inside a region).
@@ -16,16 +16,7 @@ from oracle import moe
 
 
 def random_routes(R, N, K, E_total, seed, skew=None):
-    rng = np.random.default_rng(seed)
-    A = np.empty((R, N * K), dtype=np.int64)
-    p = None
-    if skew is not None:
-        p = np.arange(1, E_total + 1, dtype=np.float64) ** (-skew)
-        p /= p.sum()
-    for r in range(R):
-        for t in range(N):
-            A[r, t * K:(t + 1) * K] = rng.choice(E_total, size=K, replace=False, p=p)
-    return A
+    return synth.random_routes(R, N, K, E_total, seed, skew).astype(np.int64)
 
 
 CASES = [  # R, N, K, L, c, E_total, skew
