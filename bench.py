@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--ring", type=int, default=0, help="ring rows C (0: b)")
     ap.add_argument("--routing", default="x", choices=["x", "gaussian", "zipf"],
                     help="x: router projection from x; gaussian/zipf: given fp32 logits")
-    ap.add_argument("--cpu-sample", type=int, default=8, help="tokens of the oracle's timed CPU sample (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=48, help="tokens of the oracle's timed CPU sample (0: skip)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
     return ap.parse_args()
 

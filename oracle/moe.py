@@ -260,6 +260,19 @@ def quantize_weights_mx(weights: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]
     return out
 
 
+def logit_bound_probabilistic(x_bits: np.ndarray, w_router_bits: np.ndarray, lam: float = 8.0) -> np.ndarray:
+    """High-probability bound on |fl32(logit) - logit|: lam * sqrt(D) * u *
+    sum_d |x_d w_{e,d}| (Higham and Mary, "A New Approach to Probabilistic
+    Rounding Error Analysis", SIAM J. Sci. Comput. 41(5), 2019: rounding
+    errors modelled as independent, mean-zero; lam = 8 makes a violation a
+    far-tail event).  Used only to decide which tokens have an unambiguous
+    top-k, never as a tolerance on a value."""
+    x = np.abs(_bf16.to_f64(x_bits))
+    w = np.abs(_bf16.to_f64(w_router_bits))
+    D = x.shape[1]
+    return lam * np.sqrt(D) * 2.0 ** -23 * (x @ w.T)
+
+
 def logit_bound(x_bits: np.ndarray, w_router_bits: np.ndarray) -> np.ndarray:
     """Bound on |fl32(logit) - logit| for any fp32 summation order.
 

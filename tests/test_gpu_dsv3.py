@@ -19,7 +19,7 @@ from tests._gpu import layer, need_gpu, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = [0, 1, 2047, 4096, 6000, 8191]
+SAMPLE = [0, 1, 511, 1024, 2047, 3000, 4096, 5000, 6000, 7000, 8000, 8191]
 
 
 @pytest.fixture(scope="module")
@@ -60,7 +60,7 @@ def test_dsv3_given_logits_route_and_schedule_bit_exact(dsv3):
     l = logits.numpy()
     oi = ref.topk(l, w.k)
     assert np.array_equal(idx.cpu().numpy(), oi)
-    want = ref.schedule(oi[None], 0, w.E)
+    want = ref.schedule(oi.reshape(1, -1), 0, w.E)
     assert np.array_equal(sched["counts"].cpu().numpy(), want["counts"])
     assert np.array_equal(sched["offsets"].cpu().numpy(), want["offsets"])
     assert np.array_equal(sched["sched"].cpu().numpy(), want["sched"])
@@ -83,13 +83,22 @@ def test_dsv3_full_path_sampled_tokens(dsv3):
     bound = ref.logit_bound(xb, wrb)
     lg = r["logits"][torch.as_tensor(tok, device=dev)].cpu().numpy().astype(np.float64)
     assert np.all(np.abs(lg - L64) <= bound)
-    srt = np.sort(L64, axis=1)[:, ::-1]
-    clear = srt[:, w.k - 1] - srt[:, w.k] > 2 * bound.max(axis=1)
-    oi = ref.topk(L64.astype(np.float32), w.k)
+    # the selection must be valid under the worst-case bound for every token,
+    # and equal the oracle's where the gap beats the probabilistic bound
     gi = r["idx"].cpu().numpy()[tok]
+    for i in range(len(tok)):
+        sel = set(gi[i].tolist())
+        lo = min(L64[i, e] + bound[i, e] for e in sel)
+        hi = max(L64[i, f] - bound[i, f] for f in range(w.E) if f not in sel)
+        assert lo >= hi
+    pb = ref.logit_bound_probabilistic(xb, wrb)
+    srt = np.sort(L64, axis=1)[:, ::-1]
+    clear = srt[:, w.k - 1] - srt[:, w.k] > 2 * pb.max(axis=1)
+    oi = ref.topk(L64.astype(np.float32), w.k)
     assert np.array_equal(np.sort(gi[clear], 1), np.sort(oi[clear], 1))
     keep = np.nonzero(clear)[0]
-    assert len(keep) >= len(tok) - 1
+    say("dsv3 unambiguous sampled tokens:", len(keep), "of", len(tok))
+    assert len(keep) >= len(tok) // 2
     # host copies of the experts the kept tokens use, and the oracle per token
     experts = np.unique(oi[keep])
     say("dsv3 oracle on", len(keep), "tokens,", len(experts), "experts")

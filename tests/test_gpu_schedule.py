@@ -56,7 +56,7 @@ def test_schedule_from_topk_of_given_logits():
     dev = need_gpu()
     w = synth.workload("mid", routing="gaussian")
     l = synth.make_logits(w).numpy()
-    A = ref.topk(l, w.k)[None]
+    A = ref.topk(l, w.k).reshape(1, -1)
     want = ref.schedule(A, 0, w.E)
     say("schedule_from_topk", w)
     _, got = run_schedule(dev, A, w.T, w.k, w.E, 1, 0)
