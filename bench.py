@@ -47,6 +47,9 @@ def parse():
                     help="x: router projection from x; gaussian/zipf: given fp32 logits")
     ap.add_argument("--cpu-sample", type=int, default=48, help="tokens of the oracle's timed CPU sample (0: skip)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the run, copy a MIB-MiB buffer 3 times with a plain device copy (a known-size "
+                         "reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -193,6 +196,16 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
+        del src, dst
 
     if args.cpu_sample > 0:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample)

@@ -3,24 +3,35 @@
 // MoK paper "Mixture-of-Kittens: MoE Megakernel for NVL72s", §2.1: an
 // expert's FFN is two input projections (up, gate) combined through a gated
 // activation, then an output (down) projection; the MoK blog's notation makes
-// the gate SiLU (SwiGLU).  The
-// routed experts run as expert-grouped GEMMs over expert-contiguous row tiles
-// of the ring buffer (§3.1, condition 3: rows of one expert sit contiguously,
-// so no local reordering precedes the GEMMs).
+// the gate SiLU (SwiGLU).  The routed experts run as expert-grouped GEMMs over
+// expert-contiguous row tiles of the ring buffer (§3.1, condition 3: rows of
+// one expert sit contiguously, so no local reordering precedes the GEMMs).
 //
-// One workgroup (4 waves) computes a BM x BN output tile with
-// v_mfma_f32_32x32x16_bf16: both operands are K-contiguous (rows of the
-// activations and rows of the weights), so every lane feeds the matrix core
-// with one 16-byte LDS read per operand.  Tiles of K = 64 are staged through
-// LDS, double-buffered, with the next tile's global loads in flight while the
-// current one is multiplied.  The K loop always runs in the same order from
-// k = 0 and there is no split-K, so a row's result does not depend on which
-// tile or minibatch it falls in.
+// Tiling.  A workgroup of 4 waves computes a BM x BN output tile with
+// v_mfma_f32_32x32x16_bf16; each wave owns a (BM/2) x (BN/2) quadrant.  Both
+// operands are K-contiguous (activation rows and weight rows), so each lane
+// feeds the matrix core with one 16-byte LDS read per operand.  K tiles of 64
+// are staged through LDS, double-buffered, with the next tile's global loads
+// in flight while the current one is multiplied.  The K loop always runs from
+// k = 0 in the same order and there is no split-K, so a row's result does not
+// depend on the tile or minibatch it falls in.
 //
-// Epilogues: SwiGLU (gate and up tiles share the output coordinates; h =
+// Work order (routed).  The 256 MI355X CUs sit in 8 XCDs, each with its own
+// L2, and workgroups are dealt to XCDs round-robin.  Work items are ordered
+// expert-major, then by N block, then by row tile, and workgroup b runs item
+// (b mod 8) * ceil(W/8) + b / 8: each XCD walks a contiguous run of items, so
+// the N-block tiles of one expert (which share the same activation rows) and
+// the row tiles of one (expert, N block) (which share the same weight rows)
+// run side by side on one XCD and meet in its L2, while every weight byte is
+// fetched from HBM about once.  With BM = 256 an expert's rows at the
+// DeepSeek-V3 shape (about 256 per expert) mostly fit in one tile; 32-row
+// blocks past the end of a tile are not multiplied.
+//
+// Epilogues: SwiGLU (gate and up tiles share output coordinates; h =
 // SiLU(g) * u rounded to bf16), plain bf16 store (routed down projection,
-// optionally scattered to the row of the route it came from) and fp32 store
-// (shared expert output, router logits).
+// optionally scattered to the row of the route it came from, reusing the
+// schedule table as in §3.1) and fp32 store (shared expert output, router
+// logits).
 
 #include "common.h"
 #include "kernels.h"
@@ -29,84 +40,235 @@ namespace moe {
 
 namespace {
 
-constexpr int kBK = 64;
-constexpr int kLdsLd = kBK + 8;  // padded LDS row (bf16 elements): conflict-free 16-byte reads
+constexpr int kXcds = 8;
+constexpr int kStageK = 64;  // K elements per pipeline stage (one 128-byte line per row)
+constexpr int kStages = 2;   // LDS ring depth
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// Operand sources of a tile: buffer resources over the activation rows and the
+// weight rows (gate and up halves for SwiGLU).  Per-lane 32-bit byte offsets
+// select the rows; the K position goes in the scalar offset; reads past a
+// resource's end return zero.
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t a, b0, b1;
+};
+
+// Byte position of (row, 16-byte chunk c) inside a stage whose rows are RB
+// bytes (CH = RB / 16 chunks).  Chunks are XOR-swizzled by the row's position
+// within a 256-byte LDS bank sweep, so that the 32 rows an MFMA fragment read
+// touches fall on distinct banks in every 16-lane phase.
+template <int RB>
+__device__ __forceinline__ int swz(int row, int c) {
+  constexpr int CH = RB / 16;
+  constexpr int ROWS_PER_SWEEP = 256 / RB;  // rows that share one sweep of the 64 banks
+  return row * RB + ((c ^ ((row / ROWS_PER_SWEEP) & (CH - 1))) << 4);
+}
+
+// One direct 16-byte-per-lane load into LDS: lane l's bytes land at lds + 16 l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0,
+                                           0);
+}
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= lgkm, expcnt untouched.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8); }
+
+// The K loop of one workgroup: an NST-stage LDS ring of BK-wide K tiles fed
+// by direct buffer->LDS loads (lane l's 16 bytes land at base + 16 l, so one
+// wave instruction fills 1 KB of a stage; each lane fetches the global chunk
+// the swizzle maps to its slot).  Stage kt+NST-1 is requested at the top of
+// step kt.  The 16-wide K steps of a stage run back to back with the next
+// step's fragments read under the current MFMAs; before the last step's MFMAs
+// the wave waits for stage kt+1 and passes the one barrier of the step, so
+// that stage kt+1's first fragments are read under them.  FML = 32-row MFMA
+// blocks of this wave that hold tile rows (the rest of the quadrant lies past
+// the tile and is skipped).
+template <int BM, int BN, int WM, int WN, int NB, int FML, int FM, int FN, int NST, int BK, int AI, int BI>
+__device__ __forceinline__ void k_loop_dma(char* smem, const TileSrc& src, const uint32_t (&a_off)[AI],
+                                           const uint32_t (&b_off)[BI], int nk, int a_rows, int tid, int wm, int wn,
+                                           f32x16_t (&acc)[NB][FM][FN]) {
+  constexpr int RB = BK * 2;  // bytes of one row of a stage
+  constexpr int BROWS = NB * BN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int STAGE = (BM + BROWS) * RB;
+  constexpr int KS = BK / 16;  // 16-wide K steps per stage
+  constexpr int ROWS_PER_LD = 1024 / RB;
+  static_assert(AI * ROWS_PER_LD * 4 == BM && BI * ROWS_PER_LD * 4 == BROWS, "DMA instructions per wave per stage");
+  constexpr int NLD = AI + BI;
+  constexpr int VM_AHEAD = (NST - 2) * NLD;  // loads allowed in flight when a stage must be complete
+  static_assert(VM_AHEAD < 64, "vmcnt range");
+  const int wave = tid >> 6, lane = tid & 63;
+  const int frag_row = lane & 31, frag_c = lane >> 5;
+
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    const int buf = kt % NST;
+    const int ko = (kt < nk ? kt : nk - 1) * RB;  // past the end: the last stage again, into a free slot
+    char* sa = smem + buf * STAGE;
+    char* sb = sa + BM * RB;
+    // A row groups past the tile are not fetched (their rows only feed dropped
+    // outputs); a dummy reload of the group's first row keeps the per-wave load
+    // count, which the vmcnt waits rely on, the same for every wave
+#pragma unroll
+    for (int j = 0; j < AI; ++j)
+      dma16(src.a, sa + (wave * AI + j) * 1024, (wave * AI + j) * ROWS_PER_LD < a_rows ? a_off[j] : a_off[0], ko);
+#pragma unroll
+    for (int j = 0; j < BI; ++j) {
+      const int g = wave * BI + j;  // ROWS_PER_LD-row group of the B stage
+      dma16((NB == 2 && g * ROWS_PER_LD >= BN) ? src.b1 : src.b0, sb + g * 1024, b_off[j], ko);
+    }
+  };
+  using frag_a_t = bf16x8_t[FML > 0 ? FML : 1];
+  using frag_b_t = bf16x8_t[NB][FN];
+  auto read_frags = [&](int kt, int step, frag_a_t& af, frag_b_t& bfr) __attribute__((always_inline)) {
+    const char* sa = smem + (kt % NST) * STAGE;
+    const char* sb = sa + BM * RB;
+    const int c = step * 2 + frag_c;
+#pragma unroll
+    for (int fm = 0; fm < FML; ++fm)
+      af[fm] = *reinterpret_cast<const bf16x8_t*>(sa + swz<RB>(wm * WTM + fm * 32 + frag_row, c));
+#pragma unroll
+    for (int h = 0; h < NB; ++h)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        bfr[h][fn] = *reinterpret_cast<const bf16x8_t*>(sb + swz<RB>(h * BN + wn * WTN + fn * 32 + frag_row, c));
+  };
+  auto mfmas = [&](const frag_a_t& af, const frag_b_t& bfr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int fm = 0; fm < FML; ++fm)
+#pragma unroll
+      for (int h = 0; h < NB; ++h)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[h][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[h][fn], acc[h][fm][fn], 0, 0, 0);
+  };
+  constexpr int NMF = FML * NB * FN;  // MFMAs per 16-wide step
+  constexpr int NRD = FML + NB * FN;  // fragment reads per 16-wide step
+  auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue(s);
+  asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_AHEAD, 15)) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  frag_a_t af[2];
+  frag_b_t bf[2];
+  if constexpr (FML > 0) read_frags(0, 0, af[0], bf[0]);
+  for (int kt = 0; kt < nk; ++kt) {
+    issue(kt + NST - 1);
+    if constexpr (FML > 0) {
+#pragma unroll
+      for (int ks = 0; ks + 1 < KS; ++ks) {
+        read_frags(kt, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+        mfmas(af[ks & 1], bf[ks & 1]);
+        if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, NLD, 0);  // the stage's loads first
+        interleave();
+      }
+    }
+    // stage kt+1 has landed (this wave's loads) and this wave's reads of
+    // stage kt are done, before any wave refills a slot
+    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_AHEAD, 0)) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if constexpr (FML > 0) {
+      if (kt + 1 < nk) read_frags(kt + 1, 0, af[KS & 1], bf[KS & 1]);
+      mfmas(af[(KS - 1) & 1], bf[(KS - 1) & 1]);
+      interleave();
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still target LDS when the workgroup ends
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int NST, int BK>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;  // B halves (gate, up)
   constexpr int BROWS = NB * BN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int A_LD = BM / 32, B_LD = BROWS / 32;  // 16-byte loads per thread per K tile
+  constexpr int RB = BK * 2;                                // bytes of one row of a stage
+  constexpr int ROWS_PER_LD = 1024 / RB;                    // rows one 1 KB direct load fills
+  constexpr int AI = BM / (4 * ROWS_PER_LD), BI = BROWS / (4 * ROWS_PER_LD);  // per wave per stage
   static_assert(WM * WN == 4, "4 waves per workgroup");
-  static_assert(FM >= 1 && FN >= 1 && BM % 32 == 0 && BROWS % 32 == 0, "tile shape");
+  static_assert(FM >= 1 && FN >= 1 && AI * 4 * ROWS_PER_LD == BM && BI * 4 * ROWS_PER_LD == BROWS, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BROWS) * kLdsLd];
+  __shared__ __attribute__((aligned(1024))) char smem[NST * (BM + BROWS) * RB];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave / WN, wn = wave % WN;
 
+  // ---- which (tile, N block) this workgroup computes ----
   const int n_blocks = (args.N + BN - 1) / BN;
-  const int tcount = args.tiles ? *args.tile_count : (args.dense_rows + BM - 1) / BM;
-  const int bid = blockIdx.x;
-  if (bid >= tcount * n_blocks) return;
-  const int tile = bid % tcount, nb = bid / tcount;
-  int e, nrows;
+  const int tcount = ROUTED ? *args.tile_count : (args.dense_rows + BM - 1) / BM;
+  const int W = tcount * n_blocks;
+  const int chunk = (W + kXcds - 1) / kXcds;
+  const int local = static_cast<int>(blockIdx.x) / kXcds;
+  if (local >= chunk) return;
+  const int w = (static_cast<int>(blockIdx.x) % kXcds) * chunk + local;
+  if (w >= W) return;
+  int e = 0, nrows, tile, nb;
   int64_t p0;
-  if (args.tiles) {
+  if constexpr (ROUTED) {
+    const int4 g = args.tiles[w / n_blocks];  // a tile of the expert group that owns item w
+    const int nt = g.x >> 10, first = g.w;
+    const int lw = w - first * n_blocks;
+    nb = lw / nt;
+    tile = first + lw % nt;
     const int4 t = args.tiles[tile];
-    e = t.x;
+    e = t.x & 1023;
     p0 = t.y;
     nrows = t.z;
   } else {
-    e = 0;
+    // dense: row tile outer, so the workgroups of one XCD share activation
+    // rows in L2 and stream the (small) weight matrix
+    nb = w % n_blocks;
+    tile = w / n_blocks;
     p0 = static_cast<int64_t>(tile) * BM;
     nrows = args.dense_rows - static_cast<int>(p0) < BM ? args.dense_rows - static_cast<int>(p0) : BM;
   }
   const int n0 = nb * BN;
   const int K = args.K;
 
-  // global source of each 16-byte chunk this thread stages (rows past the
-  // tile or past N are clamped onto valid rows; their results are dropped)
-  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
-  const uint16_t* a_src[A_LD];
+  // ---- byte offsets of the 16-byte chunks this lane fetches ----
+  // Direct load j of wave w fills rows ROWS_PER_LD (w * AI + j) + lane / CH of
+  // a stage; the lane's slot is chunk lane % CH, so it fetches the global chunk
+  // the swizzle maps there.  Rows past the tile are clamped onto its last row
+  // and rows past N onto row N-1: their products only reach output rows and
+  // columns that are dropped.
+  constexpr int CH = RB / 16;
+  uint32_t a_off[AI];
 #pragma unroll
-  for (int it = 0; it < A_LD; ++it) {
-    const int i = lrow + 32 * it;
-    const int64_t p = p0 + (i < nrows ? i : nrows - 1);
+  for (int j = 0; j < AI; ++j) {
+    const int row = ROWS_PER_LD * (wave * AI + j) + lane / CH;
+    const int c = (lane % CH) ^ ((row / (256 / RB)) & (CH - 1));
+    const int64_t p = p0 + (row < nrows ? row : nrows - 1);
     const int64_t arow = (p - args.a_sub) % args.a_mod;
-    a_src[it] = args.A + arow * args.lda + lcol;
+    a_off[j] = static_cast<uint32_t>((arow * args.lda + c * 8) * 2);
   }
-  const uint16_t* b_src[B_LD];
+  uint32_t b_off[BI];
 #pragma unroll
-  for (int it = 0; it < B_LD; ++it) {
-    const int i = lrow + 32 * it;
-    const int half = i / BN;
-    int n = n0 + (i - half * BN);
+  for (int j = 0; j < BI; ++j) {
+    const int row = ROWS_PER_LD * (wave * BI + j) + lane / CH;
+    const int c = (lane % CH) ^ ((row / (256 / RB)) & (CH - 1));
+    const int half = row / BN;
+    int n = n0 + (row - half * BN);
     n = n < args.N ? n : args.N - 1;
-    const uint16_t* base = (NB == 2 && half) ? args.B1 : args.B0;
-    b_src[it] = base + static_cast<int64_t>(e) * args.b_expert_stride + static_cast<int64_t>(n) * K + lcol;
+    b_off[j] = static_cast<uint32_t>((static_cast<int64_t>(n) * K + c * 8) * 2);
   }
-
-  u32x4_t ra[A_LD], rb[B_LD];
-#define MOE_GLOAD(kt)                                                                          \
-  do {                                                                                         \
-    _Pragma("unroll") for (int it = 0; it < A_LD; ++it) ra[it] =                               \
-        *reinterpret_cast<const u32x4_t*>(a_src[it] + (kt) * kBK);                               \
-    _Pragma("unroll") for (int it = 0; it < B_LD; ++it) rb[it] =                               \
-        *reinterpret_cast<const u32x4_t*>(b_src[it] + (kt) * kBK);                               \
-  } while (0)
-#define MOE_SSTORE(buf)                                                                        \
-  do {                                                                                         \
-    uint16_t* as_ = smem + (buf) * (BM + BROWS) * kLdsLd;                                      \
-    uint16_t* bs_ = as_ + BM * kLdsLd;                                                         \
-    _Pragma("unroll") for (int it = 0; it < A_LD; ++it)                                        \
-        *reinterpret_cast<u32x4_t*>(as_ + (lrow + 32 * it) * kLdsLd + lcol) = ra[it];            \
-    _Pragma("unroll") for (int it = 0; it < B_LD; ++it)                                        \
-        *reinterpret_cast<u32x4_t*>(bs_ + (lrow + 32 * it) * kLdsLd + lcol) = rb[it];            \
-  } while (0)
-
+  constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
+  TileSrc src;
+  src.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(args.A), 0, static_cast<int>(args.a_bytes),
+                                            kRsrcWord3);
+  const int b_bytes = args.N * K * 2;
+  src.b0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(args.B0 + static_cast<int64_t>(e) * args.b_expert_stride), 0, b_bytes, kRsrcWord3);
+  src.b1 = NB == 2 ? __builtin_amdgcn_make_buffer_rsrc(
+                         const_cast<uint16_t*>(args.B1 + static_cast<int64_t>(e) * args.b_expert_stride), 0, b_bytes,
+                         kRsrcWord3)
+                   : src.b0;
   f32x16_t acc[NB][FM][FN];
 #pragma unroll
   for (int h = 0; h < NB; ++h)
@@ -115,43 +277,35 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[h][fm][fn] = f32x16_t{};
 
-  const int nk = K / kBK;
-  MOE_GLOAD(0);
-  MOE_SSTORE(0);
-  __syncthreads();
-  const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) MOE_GLOAD(kt + 1);
-    const uint16_t* as = smem + cur * (BM + BROWS) * kLdsLd;
-    const uint16_t* bs = as + BM * kLdsLd;
-#pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      bf16x8_t af[FM], bfr[NB][FN];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        af[fm] = *reinterpret_cast<const bf16x8_t*>(as + (wm * WTM + fm * 32 + frag_row) * kLdsLd + kk + frag_k);
-#pragma unroll
-      for (int h = 0; h < NB; ++h)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          bfr[h][fn] = *reinterpret_cast<const bf16x8_t*>(
-              bs + (h * BN + wn * WTN + fn * 32 + frag_row) * kLdsLd + kk + frag_k);
-#pragma unroll
-      for (int h = 0; h < NB; ++h)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            acc[h][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[h][fn], acc[h][fm][fn], 0, 0, 0);
-    }
-    if (kt + 1 < nk) MOE_SSTORE(cur ^ 1);
-    __syncthreads();
+  // 32-row MFMA blocks of this wave that hold tile rows (wave-uniform); the
+  // K loop is instantiated per count so that its body is one straight block
+  int fm_live = (nrows - wm * WTM + 31) / 32;
+  fm_live = fm_live < 0 ? 0 : (fm_live > FM ? FM : fm_live);
+  const int nk = K / BK;
+  switch (fm_live) {
+#define MOE_CASE(n)                                                                       \
+  case n:                                                                                 \
+    if constexpr (n <= FM)                                                                \
+      k_loop_dma<BM, BN, WM, WN, NB, n, FM, FN, NST, BK, AI, BI>(smem, src, a_off, b_off, nk, nrows, tid, wm, wn, acc); \
+    break;
+    MOE_CASE(0)
+    MOE_CASE(1)
+    MOE_CASE(2)
+    MOE_CASE(3)
+    MOE_CASE(4)
+    MOE_CASE(5)
+    MOE_CASE(6)
+    MOE_CASE(7)
+    MOE_CASE(8)
+#undef MOE_CASE
+    default:
+      break;
   }
 
-  // epilogue: lane holds column (lane % 32) and rows 8*(r/4) + 4*(lane/32) + r%4
+  // ---- epilogue: lane holds column (lane % 32) and rows 8*(r/4) + 4*(lane/32) + r%4 ----
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
+    if (fm >= fm_live) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row_t = wm * WTM + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
@@ -175,24 +329,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
       }
     }
   }
-#undef MOE_GLOAD
-#undef MOE_SSTORE
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int NST = kStages, int BK = kStageK>
 hipError_t run(const GemmArgs& a, hipStream_t stream) {
-  const int tiles = a.tiles ? a.max_tiles : (a.dense_rows + BM - 1) / BM;
-  const int n_blocks = (a.N + BN - 1) / BN;
-  const int64_t grid = static_cast<int64_t>(tiles) * n_blocks;
+  const int64_t tiles = ROUTED ? a.max_tiles : (a.dense_rows + BM - 1) / BM;
+  const int64_t n_blocks = (a.N + BN - 1) / BN;
+  const int64_t work = tiles * n_blocks;
+  const int64_t grid = (work + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  gemm_kernel<BM, BN, WM, WN, EPI><<<static_cast<unsigned>(grid), 256, 0, stream>>>(a);
+  gemm_kernel<BM, BN, WM, WN, EPI, ROUTED, NST, BK><<<static_cast<unsigned>(grid), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-constexpr int kRoutedBM = 128;
+constexpr int kRoutedBM = 256;
 
 int gemm_routed_bm() { return kRoutedBM; }
 
@@ -203,14 +356,22 @@ int gemm_tiles_bound(int64_t rows, int groups, int bm) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t stream) {
-  if (a.K % kBK != 0 || a.N <= 0) return hipErrorInvalidValue;
+  if (a.K % kStageK != 0 || a.N <= 0) return hipErrorInvalidValue;
+  // buffer resources address at most 2^31 bytes per operand here
+  if (a.a_bytes <= 0 || a.a_bytes >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (static_cast<int64_t>(a.N) * a.K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const bool routed = a.tiles != nullptr;
   switch (epilogue) {
     case kEpiSwiGLU:
-      return run<kRoutedBM, 64, 2, 2, kEpiSwiGLU>(a, stream);
+      return routed ? run<kRoutedBM, 128, 2, 2, kEpiSwiGLU, true>(a, stream)
+                    : run<256, 128, 2, 2, kEpiSwiGLU, false>(a, stream);
     case kEpiBF16:
-      return run<kRoutedBM, 128, 2, 2, kEpiBF16>(a, stream);
+      return routed ? run<kRoutedBM, 256, 2, 2, kEpiBF16, true>(a, stream)
+                    : run<256, 256, 2, 2, kEpiBF16, false>(a, stream);
     case kEpiF32:
-      return run<kRoutedBM, 128, 2, 2, kEpiF32>(a, stream);
+      return routed ? run<kRoutedBM, 256, 2, 2, kEpiF32, true>(a, stream)
+                    : (a.N <= 256 ? run<128, 128, 2, 2, kEpiF32, false>(a, stream)
+                                  : run<256, 256, 2, 2, kEpiF32, false>(a, stream));
     default:
       return hipErrorInvalidValue;
   }

@@ -36,6 +36,7 @@ enum GemmEpilogue : int {
 
 struct GemmArgs {
   const uint16_t* A;  // bf16; tile position p reads row (p - a_sub) mod a_mod
+  int64_t a_bytes;    // extent of A in bytes (< 2^31)
   int64_t lda;
   int64_t a_sub;
   int64_t a_mod;

@@ -171,6 +171,7 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router
   if (x) {
     moe::GemmArgs g{};
     g.A = static_cast<const uint16_t*>(x);
+    g.a_bytes = shape->T * shape->D * 2;
     g.lda = shape->D;
     g.a_sub = 0;
     g.a_mod = INT64_MAX;
@@ -251,6 +252,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
   if (T > 0) {
     moe::GemmArgs g{};
     g.A = static_cast<const uint16_t*>(x_local);
+    g.a_bytes = static_cast<int64_t>(T) * D * 2;
     g.lda = D;
     g.a_sub = 0;
     g.a_mod = INT64_MAX;
@@ -268,6 +270,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     }
     moe::GemmArgs d{};
     d.A = h_sh;
+    d.a_bytes = static_cast<int64_t>(T) * Is * 2;
     d.lda = Is;
     d.a_sub = 0;
     d.a_mod = INT64_MAX;
@@ -293,6 +296,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     }
     moe::GemmArgs u{};
     u.A = ring;
+    u.a_bytes = C * D * 2;
     u.lda = D;
     u.a_sub = 0;
     u.a_mod = C;
@@ -314,6 +318,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     }
     moe::GemmArgs d{};
     d.A = h;
+    d.a_bytes = b * I * 2;
     d.lda = I;
     d.a_sub = p_begin;
     d.a_mod = INT64_MAX;

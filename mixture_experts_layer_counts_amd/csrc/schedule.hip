@@ -185,7 +185,9 @@ int sched_chunks(int NK) { return NK > 0 ? (NK + kSchedChunk - 1) / kSchedChunk 
 // ----------------------------------------------------------------------------
 // Tile lists: for minibatch m (positions m*b .. min(m*b+b, P)-1), every expert
 // segment that overlaps it is cut into row tiles of at most BM rows, in expert
-// order.  Entry = {expert, first position, rows, 0}.
+// order.  Entry = {expert | (tiles of this expert << 10), first position,
+// rows, index of this expert's first tile}; the GEMM kernels order their work
+// by it.
 // ----------------------------------------------------------------------------
 
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int L, int64_t b,
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     if (start + i >= max_tiles) break;
     const int64_t p0 = s_lo + static_cast<int64_t>(i) * BM;
     const int64_t rows = s_hi - p0 < BM ? s_hi - p0 : BM;
-    out[start + i] = make_int4(l, static_cast<int>(p0), static_cast<int>(rows), 0);
+    out[start + i] = make_int4(l | (n << 10), static_cast<int>(p0), static_cast<int>(rows), start);
   }
   if (l == 0) tile_count[m] = total < max_tiles ? total : max_tiles;
 }
