@@ -184,12 +184,13 @@ int sched_chunks(int NK) { return NK > 0 ? (NK + kSchedChunk - 1) / kSchedChunk 
 
 // ----------------------------------------------------------------------------
 // Tile lists: for minibatch m (positions m*b .. min(m*b+b, P)-1), every expert
-// segment that overlaps it is cut into row tiles of at most BM rows, in expert
-// order.  Entry = {expert | (tiles of this expert << 10), first position,
-// rows, index of this expert's first tile}; the GEMM kernels order their work
-// by it.
-// ----------------------------------------------------------------------------
-
+// segment that overlaps it is cut into n = ceil(rows / BM) row tiles of nearly
+// equal height (rounded up to 32 rows, the MFMA block), in expert order.  With
+// balanced heights the tiles of one segment run at the same pace, so the
+// workgroups that read the same expert weights stay together and share them in
+// L2 instead of re-fetching them from HBM.  Entry = {expert | (n << 10), first
+// position, rows, index of this expert's first tile}; the GEMM kernels order
+// their work by it.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int L, int64_t b,
                                                            int64_t max_rows, int BM, int max_tiles,
                                                            int4* __restrict__ tiles, int32_t* __restrict__ tile_count) {
@@ -208,11 +209,17 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   int total = 0;
   const int start = block_exclusive_scan_1024(n, &total);
   int4* out = tiles + static_cast<int64_t>(m) * max_tiles;
-  for (int i = 0; i < n; ++i) {
-    if (start + i >= max_tiles) break;
-    const int64_t p0 = s_lo + static_cast<int64_t>(i) * BM;
-    const int64_t rows = s_hi - p0 < BM ? s_hi - p0 : BM;
-    out[start + i] = make_int4(l | (n << 10), static_cast<int>(p0), static_cast<int>(rows), start);
+  if (n > 0) {
+    const int64_t len = s_hi - s_lo;
+    int64_t h = (len + n - 1) / n;
+    h = (h + 31) / 32 * 32;  // <= BM since BM is a multiple of 32
+    for (int i = 0; i < n; ++i) {
+      if (start + i >= max_tiles) break;
+      const int64_t p0 = s_lo + static_cast<int64_t>(i) * h;
+      const int64_t rows = s_hi - p0 < h ? s_hi - p0 : h;
+      if (rows <= 0) break;  // unreachable: n tiles of height h >= len / n cover the segment
+      out[start + i] = make_int4(l | (n << 10), static_cast<int>(p0), static_cast<int>(rows), start);
+    }
   }
   if (l == 0) tile_count[m] = total < max_tiles ? total : max_tiles;
 }
