@@ -73,4 +73,8 @@ hipError_t launch_combine(const uint16_t* Y, const float* shared_out, const floa
 
 hipError_t launch_clear_int(int* p, int n, hipStream_t stream);
 
+// MXFP8: rows x K bf16 -> E4M3 codes + one E8M0 scale per 32 elements along K.
+hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale,
+                                 hipStream_t stream);
+
 }  // namespace moe

@@ -344,13 +344,11 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
 }
 
 moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale, void* stream) {
-  (void)src;
-  (void)rows;
-  (void)K;
-  (void)q;
-  (void)scale;
-  (void)stream;
-  return MOE_ERR_UNSUPPORTED;
+  if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!src || !q || !scale) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_quantize_mxfp8(static_cast<const uint16_t*>(src), rows, K, q, scale,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_probe_begin(int32_t kernel_id, int32_t max_launches) {

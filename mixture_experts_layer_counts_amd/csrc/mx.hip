@@ -1,0 +1,70 @@
+// MXFP8 quantisation on gfx950 (MoK paper "Mixture-of-Kittens: MoE Megakernel
+// for NVL72s", §3.4 "MXFP8 Support": a dedicated kernel pre-quantises the
+// expert weights; activation quantisation is fused into the dispatch and the
+// gated activation).
+//
+// Format (OCP microscaling, E4M3 elements): blocks of 32 consecutive elements
+// along the contraction axis share a power-of-two scale 2^X stored as the byte
+// X + 127 (E8M0), X = floor(log2(amax)) - 8 (8 = exponent of the largest E4M3
+// normal, 448 = 1.75 * 2^8), clamped to [-127, 127]; an all-zero block has
+// X = -127.  Each element v / 2^X is rounded to the nearest E4M3FN value, ties
+// to even, saturating at +-448; the sign is kept when the value rounds to 0.
+// The rounding is done in integer arithmetic on the fp32 bits, so the result
+// does not depend on any hardware conversion mode.
+
+#include "common.h"
+#include "kernels.h"
+#include "mx.h"
+
+namespace moe {
+
+// One block of 32 bf16 values (64 bytes at `src`) -> 32 E4M3 bytes at `q` and
+// the E8M0 scale byte at `scale`.
+__device__ __forceinline__ void quantize_block32(const uint16_t* __restrict__ src, uint8_t* __restrict__ q,
+                                                 uint8_t* __restrict__ scale) {
+  const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4_t w = s[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int X = mx_scale_exponent(amax);
+  *scale = static_cast<uint8_t>(X + 127);
+  u32x4_t out[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) word |= static_cast<uint32_t>(e4m3_from_f32(ldexpf(v[4 * i + j], -X))) << (8 * j);
+    out[i >> 2][i & 3] = word;
+  }
+  u32x4_t* d = reinterpret_cast<u32x4_t*>(q);
+  d[0] = out[0];
+  d[1] = out[1];
+}
+
+__global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t blocks,
+                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= blocks) return;
+  quantize_block32(src + i * 32, q + i * 32, scale + i);
+}
+
+hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale,
+                                 hipStream_t stream) {
+  const int64_t blocks = rows * (K / 32);
+  if (blocks <= 0) return hipSuccess;
+  if ((blocks + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
+  quantize_mxfp8_kernel<<<static_cast<unsigned>((blocks + 255) / 256), 256, 0, stream>>>(src, blocks, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace moe
