@@ -68,7 +68,7 @@ __device__ __forceinline__ void k_loop_dma(char* smem, const TileSrc& src, const
   constexpr int NLD = AI + BI;
   constexpr int VM_AHEAD = (NST - 2) * NLD;  // loads allowed in flight when a stage must be complete
   static_assert(VM_AHEAD < 64, "vmcnt range");
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
   const int frag_row = lane & 31, frag_c = lane >> 5;
 
   auto issue = [&](int kt) __attribute__((always_inline)) {
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
 
   __shared__ __attribute__((aligned(1024))) char smem[NST * (BM + BROWS) * RB];
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
 
   // ---- which (tile, N block) this workgroup computes ----

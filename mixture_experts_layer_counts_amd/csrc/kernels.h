@@ -55,6 +55,32 @@ struct GemmArgs {
   int max_tiles;
 };
 
+// Grouped MXFP8 GEMM (routed only): E4M3 operands with one E8M0 scale per 32
+// elements along K, fp32 accumulate.  A row-major [a_rows][K] + [a_rows][K/32];
+// B [experts][N][K] + [experts][N][K/32].
+struct MxGemmArgs {
+  const uint8_t* A;  // tile position p reads row (p - a_sub) mod a_mod
+  const uint8_t* As;
+  int64_t a_rows;  // rows of A (a_rows * K < 2^31)
+  int64_t a_sub;
+  int64_t a_mod;
+  const uint8_t* B0;  // gate (SwiGLU) or the only operand
+  const uint8_t* B1;  // up (SwiGLU)
+  const uint8_t* Bs0;
+  const uint8_t* Bs1;
+  int N;
+  int K;
+  void* C;      // SwiGLU: E4M3 [.][ldc], scales to Cs [.][ldc/32]; BF16: bf16 [.][ldc]
+  uint8_t* Cs;  // output row = c_idx ? c_idx[p] : p - c_sub
+  int64_t ldc;
+  const int32_t* c_idx;
+  int64_t c_sub;
+  const int4* tiles;
+  const int32_t* tile_count;
+  int max_tiles;
+};
+hipError_t launch_gemm_mx(const MxGemmArgs& args, int epilogue, hipStream_t stream);
+
 // Tile rows of the routed GEMM kernels (tile lists are built with it).
 int gemm_routed_bm();
 hipError_t launch_gemm(const GemmArgs& args, int epilogue, hipStream_t stream);
@@ -70,6 +96,11 @@ hipError_t launch_gather(const uint16_t* x_src, int64_t src_rows, int D, int k, 
 hipError_t launch_combine(const uint16_t* Y, const float* shared_out, const float* gate, const int32_t* route_dst,
                           int64_t route_base, int T, int D, int k, bool by_route_dst, uint16_t* out, float* out32,
                           hipStream_t stream);
+
+// MX gather: ring_q[p mod C] / ring_s[p mod C] = MX(x_src[sched_src[p] / k]).
+hipError_t launch_gather_mx(const uint16_t* x_src, int64_t src_rows, int D, int k, const int32_t* sched_src,
+                            const int32_t* offsets, int L, int64_t p_begin, int64_t rows, int64_t ring_rows,
+                            uint8_t* ring_q, uint8_t* ring_s, int* err, hipStream_t stream);
 
 hipError_t launch_clear_int(int* p, int n, hipStream_t stream);
 

@@ -16,7 +16,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t err, ord_local, chunk_cnt, M, tiles, tile_count, ring, h, Y, h_shared, shared_out, total;
+  size_t err, ord_local, chunk_cnt, M, tiles, tile_count, ring, ring_s, h, h_s, Y, h_shared, shared_out, total;
   int64_t n_minibatches;
   int max_tiles;
   int64_t y_rows;
@@ -43,6 +43,8 @@ bool valid_shape(const moe_shape* s, moe_status* why) {
   if (s->num_src_ranks * s->T * s->k >= (int64_t(1) << 31)) return false;
   if (s->max_rows >= (int64_t(1) << 31) || s->T >= (int64_t(1) << 31)) return false;
   if (s->D > 65536 || s->I > 65536 || s->I_shared > 65536) return false;
+  // MXFP8 GEMM stages are 128 elements of K wide (D for up/gate, I for down)
+  if (s->precision == MOE_MXFP8 && (s->D % 128 || s->I % 128)) return false;
   *why = MOE_OK;
   return true;
 }
@@ -67,8 +69,15 @@ Layout layout_of(const moe_shape* s) {
   L.M = take(sizeof(int32_t) * R * Lx);
   L.tiles = take(sizeof(int4) * L.n_minibatches * L.max_tiles);
   L.tile_count = take(sizeof(int32_t) * std::max<int64_t>(L.n_minibatches, 1));
-  L.ring = take(sizeof(uint16_t) * s->ring_rows * s->D);
-  L.h = take(sizeof(uint16_t) * s->minibatch_rows * s->I);
+  if (s->precision == MOE_MXFP8) {  // E4M3 bytes + one E8M0 byte per 32 along K
+    L.ring = take(s->ring_rows * s->D);
+    L.ring_s = take(s->ring_rows * (s->D / 32));
+    L.h = take(s->minibatch_rows * s->I);
+    L.h_s = take(s->minibatch_rows * (s->I / 32));
+  } else {
+    L.ring = take(sizeof(uint16_t) * s->ring_rows * s->D);
+    L.h = take(sizeof(uint16_t) * s->minibatch_rows * s->I);
+  }
   L.Y = take(sizeof(uint16_t) * L.y_rows * s->D);
   L.h_shared = take(sizeof(uint16_t) * s->T * s->I_shared);
   L.shared_out = take(sizeof(float) * s->T * s->D);
@@ -120,6 +129,75 @@ moe_status check_ws(const moe_shape* s, const void* ws, size_t ws_bytes, Layout*
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < L->total) return MOE_ERR_WORKSPACE;
   return MOE_OK;
+}
+
+// One minibatch of the routed experts in MXFP8 (MoK paper §3.4 "MXFP8
+// Support"): the gather quantises x along D into the ring, the up/gate GEMM
+// quantises h along I in its epilogue, the down GEMM writes bf16 rows.
+hipError_t routed_minibatch_mx(const moe_shape* shape, const moe_weights* w, const void* x_src,
+                               const int32_t* sched_src, const int32_t* expert_offsets, const Layout& L, void* ws,
+                               int64_t m, int64_t p_begin, int64_t rows, hipStream_t s) {
+  const int D = static_cast<int>(shape->D), I = static_cast<int>(shape->I), k = static_cast<int>(shape->k);
+  const int Lx = static_cast<int>(shape->experts_per_rank);
+  const int64_t b = shape->minibatch_rows, C = shape->ring_rows, R = shape->num_src_ranks;
+  uint8_t* ring_q = at<uint8_t>(ws, L.ring);
+  uint8_t* ring_s = at<uint8_t>(ws, L.ring_s);
+  uint8_t* h_q = at<uint8_t>(ws, L.h);
+  uint8_t* h_s = at<uint8_t>(ws, L.h_s);
+  const int4* tiles = at<int4>(ws, L.tiles) + m * L.max_tiles;
+  const int32_t* tile_count = at<int32_t>(ws, L.tile_count) + m;
+  {
+    ProbeScope probe(MOE_K_GATHER, s);
+    const hipError_t e = moe::launch_gather_mx(static_cast<const uint16_t*>(x_src), R * shape->T, D, k, sched_src,
+                                               expert_offsets, Lx, p_begin, rows, C, ring_q, ring_s,
+                                               at<int>(ws, L.err), s);
+    if (e != hipSuccess) return e;
+  }
+  moe::MxGemmArgs u{};
+  u.A = ring_q;
+  u.As = ring_s;
+  u.a_rows = C;
+  u.a_sub = 0;
+  u.a_mod = C;
+  u.B0 = static_cast<const uint8_t*>(w->w_gate);
+  u.B1 = static_cast<const uint8_t*>(w->w_up);
+  u.Bs0 = w->s_gate;
+  u.Bs1 = w->s_up;
+  u.N = I;
+  u.K = D;
+  u.C = h_q;
+  u.Cs = h_s;
+  u.ldc = I;
+  u.c_sub = p_begin;
+  u.tiles = tiles;
+  u.tile_count = tile_count;
+  u.max_tiles = L.max_tiles;
+  {
+    ProbeScope probe(MOE_K_UP_GATE, s);
+    const hipError_t e = moe::launch_gemm_mx(u, moe::kEpiSwiGLU, s);
+    if (e != hipSuccess) return e;
+  }
+  moe::MxGemmArgs d{};
+  d.A = h_q;
+  d.As = h_s;
+  d.a_rows = b;
+  d.a_sub = p_begin;
+  d.a_mod = INT64_MAX;
+  d.B0 = static_cast<const uint8_t*>(w->w_down);
+  d.B1 = nullptr;
+  d.Bs0 = w->s_down;
+  d.Bs1 = nullptr;
+  d.N = D;
+  d.K = I;
+  d.C = at<uint16_t>(ws, L.Y);
+  d.ldc = D;
+  d.c_idx = (R == 1) ? sched_src : nullptr;
+  d.c_sub = 0;
+  d.tiles = tiles;
+  d.tile_count = tile_count;
+  d.max_tiles = L.max_tiles;
+  ProbeScope probe(MOE_K_DOWN, s);
+  return moe::launch_gemm_mx(d, moe::kEpiBF16, s);
 }
 
 }  // namespace
@@ -218,8 +296,9 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
   Layout L;
   const moe_status st = check_ws(shape, ws, ws_bytes, &L);
   if (st != MOE_OK) return st;
-  if (shape->precision != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool mx = shape->precision == MOE_MXFP8;
   if (!w || !w->w_gate || !w->w_up || !w->w_down || !w->ws_gate || !w->ws_up || !w->ws_down) return MOE_ERR_INVALID_ARG;
+  if (mx && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
   if (!expert_offsets || !route_dst || !topk_gate || !out) return MOE_ERR_INVALID_ARG;
   if (shape->T > 0 && !x_local) return MOE_ERR_INVALID_ARG;
   if (shape->max_rows > 0 && (!x_src || !sched_src)) return MOE_ERR_INVALID_ARG;
@@ -289,6 +368,10 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
   for (int64_t m = 0; m < L.n_minibatches; ++m) {
     const int64_t p_begin = m * b;
     const int64_t rows = std::min<int64_t>(b, shape->max_rows - p_begin);
+    if (mx) {
+      MOE_TRY_HIP(routed_minibatch_mx(shape, w, x_src, sched_src, expert_offsets, L, ws, m, p_begin, rows, s));
+      continue;
+    }
     {
       ProbeScope probe(MOE_K_GATHER, s);
       MOE_TRY_HIP(moe::launch_gather(static_cast<const uint16_t*>(x_src), R * shape->T, D, k, sched_src,

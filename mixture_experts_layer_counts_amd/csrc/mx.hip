@@ -67,4 +67,41 @@ hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t K, u
   return hipGetLastError();
 }
 
+// MX gather (§3.4: the activation quantisation rides on the dispatch).  As the
+// bf16 gather, schedule position p reads source row sched_src[p] / k and fills
+// ring slot p mod C, here as E4M3 bytes [C][D] and scale bytes [C][D/32]; one
+// thread quantises one 32-element block.
+__global__ __launch_bounds__(256) void gather_mx_kernel(const uint16_t* __restrict__ x_src, int64_t src_rows, int D,
+                                                        int k, const int32_t* __restrict__ sched_src,
+                                                        const int32_t* __restrict__ offsets, int L, int64_t p_begin,
+                                                        int64_t rows, int64_t ring_rows, uint8_t* __restrict__ ring_q,
+                                                        uint8_t* __restrict__ ring_s, int* err) {
+  const int nb = D / 32;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= rows * nb) return;
+  const int64_t p = p_begin + i / nb;
+  const int blk = static_cast<int>(i % nb);
+  if (p >= offsets[L]) return;
+  const int32_t route = sched_src[p];
+  const int64_t src_row = route / k;
+  if (route < 0 || src_row >= src_rows) {  // a table not built by the schedule kernels
+    if (blk == 0) raise_error(err, kErrExpertRange);
+    return;
+  }
+  const int64_t slot = p % ring_rows;
+  quantize_block32(x_src + src_row * D + blk * 32, ring_q + slot * D + blk * 32, ring_s + slot * nb + blk);
+}
+
+hipError_t launch_gather_mx(const uint16_t* x_src, int64_t src_rows, int D, int k, const int32_t* sched_src,
+                            const int32_t* offsets, int L, int64_t p_begin, int64_t rows, int64_t ring_rows,
+                            uint8_t* ring_q, uint8_t* ring_s, int* err, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (D % 32 != 0) return hipErrorInvalidValue;
+  const int64_t n = rows * (D / 32);
+  if ((n + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
+  gather_mx_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(
+      x_src, src_rows, D, k, sched_src, offsets, L, p_begin, rows, ring_rows, ring_q, ring_s, err);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -60,10 +60,13 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     q = np.maximum(e - 4, -9)  # spacing 2^(e-4) in a binade (4 significant bits), 2^-9 below 2^-6
     r = np.rint(a / np.ldexp(1.0, q)) * np.ldexp(1.0, q)
     r = np.minimum(r, E4M3_MAX)  # a tie just under 448 can only round to 448 itself
-    # code from value: search the positive half of the table (monotone on 0x00..0x7E)
-    pos = E4M3_VALUES[:0x7F]
-    code = np.searchsorted(pos, r).astype(np.uint8)
-    assert np.all(pos[code] == r)
+    # the code of r from the format's definition: below 2^-6 a subnormal
+    # m * 2^-9; otherwise r = (1 + m/8) * 2^(E-7) with biased exponent E
+    f, ex = np.frexp(r)  # r = f * 2^ex, f in [0.5, 1)
+    normal = r >= 2.0 ** -6
+    code = np.where(normal, ((ex + 6) << 3) | np.rint((2.0 * f - 1.0) * 8.0).astype(np.int64),
+                    np.rint(r * 2.0 ** 9).astype(np.int64)).astype(np.uint8)
+    assert np.all(E4M3_VALUES[code] == r)  # the table decodes it back exactly
     # the sign is kept also when the value rounds to zero (-0 is code 0x80)
     return np.where(sign, code | np.uint8(0x80), code).astype(np.uint8)
 

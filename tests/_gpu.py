@@ -34,10 +34,43 @@ def to_dev(inp, dev):
     return {n: t.to(dev) for n, t in inp.items()}
 
 
-def layer(w: synth.Workload, dev, b=None, C=None, R=1):
+def layer(w: synth.Workload, dev, b=None, C=None, R=1, precision="bf16"):
     from mixture_experts_layer_counts_amd import MoELayer, shape_for
-    return MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C),
-                    device=dev)
+    return MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
+                              precision=precision), device=dev)
+
+
+def mx_weights_dev(inp_dev):
+    """Routed weights MX-quantised on the GPU by moe_quantize_mxfp8 (the
+    product's own preprocessing); the shared expert stays bf16."""
+    from mixture_experts_layer_counts_amd import quantize_mxfp8
+    out = {n: inp_dev[n] for n in ("ws_gate", "ws_up", "ws_down")}
+    for n in ("gate", "up", "down"):
+        out["q_" + n], out["s_" + n] = quantize_mxfp8(inp_dev["w_" + n])
+    return out
+
+
+def oracle_mx_weights(inp, experts=None):
+    """The oracle's own MX quantisation of the bf16 routed weights (of the
+    given experts only, keyed by expert id, when ``experts`` is given), and
+    the bf16 shared weights.  Experts are quantised in a thread pool: numpy
+    releases the GIL, and each expert's arithmetic is the oracle's as is."""
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import bf16, mx
+    host = {n: synth.bits(inp[n]) for n in ("ws_gate", "ws_up", "ws_down")}
+    ids = list(range(inp["w_gate"].shape[0])) if experts is None else [int(e) for e in experts]
+    jobs = [(n, e) for n in ("gate", "up", "down") for e in ids]
+    rows = {(n, e): synth.bits(inp["w_" + n][e]) for n, e in jobs}
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        res = dict(zip(jobs, ex.map(lambda j: mx.quantize(bf16.to_f64(rows[j])), jobs)))
+    for n in ("gate", "up", "down"):
+        if experts is None:
+            host["q_" + n] = np.stack([res[(n, e)][0] for e in ids])
+            host["s_" + n] = np.stack([res[(n, e)][1] for e in ids])
+        else:
+            host["q_" + n] = {e: res[(n, e)][0] for e in ids}
+            host["s_" + n] = {e: res[(n, e)][1] for e in ids}
+    return host
 
 
 def rel_err(got, want):

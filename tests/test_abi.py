@@ -77,6 +77,29 @@ def test_invalid_shapes_are_rejected(lib, field, value, code):
     assert ws_bytes(lib, s)[0] == code
 
 
+def test_mxfp8_shapes(lib):
+    # MX GEMM stages are 128 elements of K wide: D and I must be multiples of 128
+    for D, I, code in ((128, 128, 0), (7168, 2048, 0), (128, 64, -2), (192, 128, -2)):
+        s = shape_for(T=64, D=D, I=I, E=8, k=2, I_shared=64, precision="mxfp8")
+        assert ws_bytes(lib, s)[0] == code
+    # the MX ring and h are E4M3 bytes plus one scale byte per 32
+    sb = shape_for(T=8192, D=7168, I=2048, E=384, k=8, minibatch_rows=65536, ring_rows=65536)
+    sm = shape_for(T=8192, D=7168, I=2048, E=384, k=8, minibatch_rows=65536, ring_rows=65536, precision="mxfp8")
+    saved = 65536 * 7168 * 2 - 65536 * (7168 + 224) + 65536 * 2048 * 2 - 65536 * (2048 + 64)
+    assert abs((ws_bytes(lib, sb)[1] - ws_bytes(lib, sm)[1]) - saved) < 4096
+
+
+def test_mxfp8_forward_needs_scales(lib):
+    s = shape_for(T=64, D=128, I=128, E=8, k=2, I_shared=64, precision="mxfp8")
+    st, n = ws_bytes(lib, s)
+    fake = ctypes.c_void_p(4096)  # never dereferenced: the call returns first
+    w = _lib.MoeWeights()
+    for f in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+        setattr(w, f, 4096)
+    assert lib.moe_forward(ctypes.byref(s), ctypes.byref(w), fake, fake, fake, fake, fake, fake, fake, None, fake,
+                           n, None) == -1
+
+
 def test_calls_validate_before_launching(lib):
     s = shape_for(T=64, D=128, I=64, E=8, k=2)
     st, n = ws_bytes(lib, s)

@@ -1,4 +1,5 @@
-"""GPU parity of the MXFP8 path: the quantiser is bit-exact with the oracle."""
+"""GPU parity of the MXFP8 path: the quantiser is bit-exact with the oracle,
+and the layer in MXFP8 is within 5e-2 * RMS of the oracle's MXFP8 layer."""
 
 import numpy as np
 import pytest
@@ -6,7 +7,8 @@ import torch
 
 import synth
 from oracle import bf16, mx
-from tests._gpu import need_gpu, say
+from oracle import moe as ref
+from tests._gpu import layer, mx_weights_dev, need_gpu, oracle_mx_weights, rel_err, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -44,3 +46,63 @@ def test_quantize_bit_exact(rows, K, seed):
     qo, so = mx.quantize(bf16.to_f64(synth.bits(x)))
     assert np.array_equal(s.cpu().numpy(), so)
     assert np.array_equal(q.cpu().numpy(), qo)
+
+
+# ---------------------------------------------------------------------------
+# The layer in MXFP8 (routed experts MX, shared expert bf16) against the oracle
+# at 5e-2 * RMS; MX needs D and I to be multiples of 128.
+# ---------------------------------------------------------------------------
+TOL_MX = 5e-2
+
+MX_CASES = [
+    ("tiny-mx", synth.Workload("tiny-mx", T=64, D=128, I=128, E=8, k=2, I_shared=64, seed=30, routing="gaussian"),
+     [(None, None), (16, 32), (128, 128)]),
+    ("ragged-mx", synth.Workload("ragged-mx", T=300, D=384, I=256, E=16, k=4, I_shared=128, seed=31,
+                                 routing="gaussian"), [(None, None), (100, 300), (256, 512)]),
+    ("skewed-mx", synth.Workload("skewed-mx", T=257, D=256, I=384, E=24, k=6, I_shared=192, seed=32, routing="zipf"),
+     [(None, None), (200, 400)]),
+    ("wide-mx", synth.Workload("wide-mx", T=1024, D=1024, I=512, E=48, k=8, I_shared=512, seed=33,
+                               routing="gaussian"), [(8192, 8192), (1000, 3000)]),
+]
+
+
+@pytest.mark.parametrize("name,w,bcs", MX_CASES, ids=[c[0] for c in MX_CASES])
+def test_mx_layer_parity_given_logits(name, w, bcs):
+    dev = need_gpu()
+    inp = synth.make_inputs(w)
+    inp_dev = to_dev(inp, dev)
+    say("mx_layer_parity", name, w)
+    wq = mx_weights_dev(inp_dev)
+    want = ref.forward(synth.bits(inp["x"]), oracle_mx_weights(inp), inp["logits"].numpy(), w.k, precision="mxfp8")
+    first = None
+    for b, C in bcs:
+        say("  b, C =", b, C)
+        m = layer(w, dev, b, C, precision="mxfp8")
+        r = m(inp_dev["x"], inp_dev["w_router"], wq, logits=inp_dev["logits"])
+        torch.cuda.synchronize()
+        assert m.device_error() == 0
+        assert np.array_equal(r["idx"].cpu().numpy(), want["idx"])
+        out32 = r["out32"].cpu()
+        err = rel_err(out32.numpy(), want["out"])
+        say("  max|err|/RMS =", err)
+        assert err <= TOL_MX
+        assert torch.equal(r["out"].cpu().view(torch.int16), out32.to(torch.bfloat16).view(torch.int16))
+        if first is None:
+            first = out32
+        else:  # minibatch and ring sizes do not change a bit
+            assert torch.equal(first.view(torch.int32), out32.view(torch.int32))
+
+
+def test_mx_zero_input_gives_zero():
+    dev = need_gpu()
+    w = synth.Workload("zero-mx", T=96, D=256, I=128, E=8, k=3, I_shared=64, seed=34, routing="gaussian")
+    inp = synth.make_inputs(w)
+    inp["x"].zero_()
+    inp_dev = to_dev(inp, dev)
+    say("mx_zero_input")
+    m = layer(w, dev, precision="mxfp8")
+    r = m(inp_dev["x"], inp_dev["w_router"], mx_weights_dev(inp_dev), logits=inp_dev["logits"])
+    torch.cuda.synchronize()
+    assert m.device_error() == 0
+    assert torch.all(r["out32"] == 0)
+
