@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer fwd tokens/sec + TFLOP/s (% MFMA peak), DSV3 shape, 1 MI355X"
 PEAK_BF16 = 2516.6e12   # MI355X dense bf16 MFMA, FLOP/s
+PEAK_FP8 = 5033.2e12    # MI355X dense fp8 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # MI355X HBM3E, bytes/s
 
 
@@ -40,12 +41,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dsv3", choices=["tiny", "mid", "dsv3"])
+    ap.add_argument("--workload", default="dsv3", choices=["tiny", "mid", "dsv3", "mx"])
+    ap.add_argument("--precision", default=None, choices=["bf16", "mxfp8"],
+                    help="routed-expert precision (default: mxfp8 for the mx workload, else bf16)")
     ap.add_argument("--minibatch", type=int, default=0, help="rows per minibatch b (0: all routed rows)")
     ap.add_argument("--ring", type=int, default=0, help="ring rows C (0: b)")
     ap.add_argument("--routing", default="x", choices=["x", "gaussian", "zipf"],
                     help="x: router projection from x; gaussian/zipf: given fp32 logits")
-    ap.add_argument("--cpu-sample", type=int, default=48, help="tokens of the oracle's timed CPU sample (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=-1,
+                    help="tokens of the oracle's timed CPU sample (0: skip; default 48, 4 in MXFP8)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy a MIB-MiB buffer 3 times with a plain device copy (a known-size "
@@ -81,17 +85,26 @@ def main():
     lib = _lib.load()
     dev = torch.device("cuda", 0)
     w = synth.workload(args.workload, routing=args.routing)
+    precision = args.precision or ("mxfp8" if args.workload == "mx" else "bf16")
+    mx = precision == "mxfp8"
     P = w.T * w.k
     b = args.minibatch or P
     C = args.ring or b
     log(f"workload {w.name}: T={w.T} D={w.D} I={w.I} E={w.E} k={w.k} I_shared={w.I_shared}; b={b} C={C}; "
-        f"routing={args.routing}; drawing inputs on {torch.cuda.get_device_name(0)}")
+        f"routing={args.routing}; {precision}; drawing inputs on {torch.cuda.get_device_name(0)}")
     t0 = time.time()
     inp = synth.make_inputs(w, device="cuda")
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
-    layer = MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C),
-                     device=dev)
+    weights = inp
+    if mx:  # routed weights quantised ahead of time (MoK paper §3.4), outside the timed region
+        from mixture_experts_layer_counts_amd import quantize_mxfp8
+        weights = {n: inp[n] for n in ("ws_gate", "ws_up", "ws_down")}
+        for n in ("gate", "up", "down"):
+            weights["q_" + n], weights["s_" + n] = quantize_mxfp8(inp["w_" + n])
+        torch.cuda.synchronize()
+    layer = MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
+                               precision=precision), device=dev)
     x, wr, logits_in = inp["x"], inp["w_router"], inp.get("logits")
     out = torch.empty((w.T, w.D), dtype=torch.bfloat16, device=dev)
 
@@ -101,7 +114,7 @@ def main():
         else:
             _, idx, gate = layer.route(x, wr)
         sched = layer.schedule(idx)
-        layer.forward(inp, x, x, gate, sched, out32=False, out=out)
+        layer.forward(weights, x, x, gate, sched, out32=False, out=out)
         return sched
 
     for _ in range(args.warmup):
@@ -144,34 +157,44 @@ def main():
                 kernels[name] = {"ms_per_step": round(tot.value / reps, 4), "launches_per_step": n.value // reps}
         log("breakdown:", json.dumps(kernels))
 
-    # roofline of the dominant kernel: algorithmic bytes and flops per launch
+    # roofline of the dominant kernel: algorithmic bytes and flops per launch.
+    # Per launch: the gate and up rows of every expert the minibatch touches,
+    # the minibatch's ring rows read once and its h rows written once (bf16,
+    # or E4M3 bytes plus one scale byte per 32 in MXFP8).
     counts = np.diff(offsets)
-    w_bytes_expert = 2 * w.I * w.D * 2          # gate + up rows of one expert, bf16
+    if mx:
+        w_bytes_expert = 2 * w.I * (w.D + w.D // 32)
+        a_row, h_row, peak_mma = w.D + w.D // 32, w.I + w.I // 32, PEAK_FP8
+    else:
+        w_bytes_expert = 2 * w.I * w.D * 2
+        a_row, h_row, peak_mma = w.D * 2, w.I * 2, PEAK_BF16
     launches = []
     for m in range(n_launch_per_step):
         lo, hi = m * b, min((m + 1) * b, P)
         touched = int(np.count_nonzero((offsets[:-1] < hi) & (offsets[1:] > lo) & (counts > 0)))
         rows = hi - lo
-        launches.append((touched * w_bytes_expert + rows * w.D * 2 + rows * w.I * 2, 2.0 * rows * 2 * w.I * w.D))
+        launches.append((touched * w_bytes_expert + rows * a_row + rows * h_row, 2.0 * rows * 2 * w.I * w.D))
     alg_bytes = float(np.mean([l[0] for l in launches]))
     alg_flops = float(np.mean([l[1] for l in launches]))
     t_dom = dom_ms * 1e-3
-    bound = "hbm" if alg_bytes / PEAK_HBM >= alg_flops / PEAK_BF16 else "mfma"
+    bound = "hbm" if alg_bytes / PEAK_HBM >= alg_flops / peak_mma else "mfma"
     if bound == "hbm":
         achieved, peak, unit = alg_bytes / t_dom / 1e9, PEAK_HBM / 1e9, "GB/s"
     else:
-        achieved, peak, unit = alg_flops / t_dom / 1e12, PEAK_BF16 / 1e12, "TFLOP/s"
+        achieved, peak, unit = alg_flops / t_dom / 1e12, peak_mma / 1e12, "TFLOP/s"
     traffic = None
     tr_path = os.path.join(ROOT, "profiles", f"traffic_{dominant}_{w.name}.json")
     if os.path.exists(tr_path):
         tr = json.load(open(tr_path))
-        if tr.get("src_digest") == src_digest("gemm.hip") and tr.get("minibatch_rows") == b:
+        src = "gemm_mx.hip" if mx else "gemm.hip"
+        if tr.get("src_digest") == src_digest(src) and tr.get("minibatch_rows") == b and \
+                tr.get("precision", "bf16") == precision:
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": alg_flops,
                 "ms_per_launch": round(dom_ms, 4),
-                "mfma_frac": round(alg_flops / t_dom / PEAK_BF16, 4),
+                "mfma_frac": round(alg_flops / t_dom / peak_mma, 4),
                 "hbm_frac": round(alg_bytes / t_dom / PEAK_HBM, 4)}
 
     flops = w.flops()
@@ -186,13 +209,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if not mx else "mxfp8 (e4m3 + e8m0/32) routed, bf16 shared",
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) bf16 weights drawn on the GPU)",
         "config": {"workload": f"{w.name}: T={w.T} D={w.D} I={w.I} E={w.E} top-{w.k} + 1 shared (I={w.I_shared})",
                    "minibatch_rows": b, "ring_rows": C,
                    "routing": "router projection from x" if logits_in is None else f"given {args.routing} logits"},
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-        "mfma_peak_frac": round(flops / (ms * 1e-3) / PEAK_BF16, 4),
+        "mfma_peak_frac": round(flops / (ms * 1e-3) / (PEAK_FP8 if mx else PEAK_BF16), 4),
         "roofline": roofline,
         "kernels": kernels,
     }
@@ -207,13 +230,18 @@ def main():
         result["copy_calibration_bytes"] = n
         del src, dst
 
-    if args.cpu_sample > 0:
-        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample)
+    n_cpu = args.cpu_sample if args.cpu_sample >= 0 else (4 if mx else 48)
+    if n_cpu > 0:
+        result["cpu_baseline"] = cpu_baseline(w, inp, n_cpu, precision)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, inp, n_tok):
-    """The oracle, as it stands, on the first n_tok tokens of the same workload."""
+def cpu_baseline(w, inp, n_tok, precision="bf16"):
+    """The oracle, as it stands, on the first n_tok tokens of the same workload.
+
+    In MXFP8 the oracle's own quantisation of the touched experts' weights is
+    done beforehand and not timed (the method quantises weights ahead of time).
+    """
     import numpy as np
     import torch
 
@@ -245,8 +273,19 @@ def cpu_baseline(w, inp, n_tok):
         sub = synth.bits(inp[n][torch.as_tensor(experts, device=inp[n].device)])
         arr = {int(e): sub[i] for i, e in enumerate(experts)}
         host[n] = _ExpertTable(arr)
+    if precision == "mxfp8":
+        from concurrent.futures import ThreadPoolExecutor
+
+        from oracle import bf16 as obf16
+        from oracle import mx as omx
+        jobs = [(n, int(e)) for n in ("gate", "up", "down") for e in experts]
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            res = dict(zip(jobs, ex.map(lambda j: omx.quantize(obf16.to_f64(host["w_" + j[0]][j[1]])), jobs)))
+        for n in ("gate", "up", "down"):
+            host["q_" + n] = _ExpertTable({int(e): res[(n, int(e))][0] for e in experts})
+            host["s_" + n] = _ExpertTable({int(e): res[(n, int(e))][1] for e in experts})
     t0 = time.perf_counter()
-    ref.forward(xb, host, lg, w.k, tokens=tok)
+    ref.forward(xb, host, lg, w.k, precision=precision, tokens=tok)
     t_fwd = time.perf_counter() - t0
     secs = t_route + t_fwd
     return {"value": round(n_tok / secs, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
