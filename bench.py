@@ -3,13 +3,24 @@
 
 One step = the whole hot path on one batch: moe_route (router GEMM from x,
 top-k, gates) + moe_schedule (Algorithm 1) + moe_forward (shared expert,
-gather into the ring, grouped up/gate + SwiGLU, grouped down, combine), on the
-DeepSeek-V3 layer shape by default (T=8192 tokens, D=7168, I=2048, 256 routed
-experts, top-8, one shared expert with I=2048; bf16; synthetic seeded inputs
-and random weights already resident in HBM).
+gather into the ring, grouped up/gate + SwiGLU, grouped down, combine).
 
-Prints ONE JSON line.  value = tokens/s; also TFLOP/s by the expert-FFN count
-6*T*(k+1)*D*I (MoK paper §4.1) and its fraction of the bf16 dense MFMA peak.
+Workloads (synthetic seeded inputs and random weights, resident in HBM):
+  dsv3  DeepSeek-V3 layer shape, all experts on one GPU: T=8192, D=7168,
+        I=2048, 256 routed experts, top-8, one shared expert (I=2048), bf16
+        (the default, and the headline line)
+  mx    the same with 384 routed experts in MXFP8 (E4M3 + E8M0 per 32 along K)
+  ep64  one rank's share at expert parallelism 64: 4 local experts receiving
+        32,768 routed rows of 64 source ranks with Zipf(1.2)-skewed counts,
+        the shared expert on the rank's 4,096 tokens
+  mid, tiny  small shapes
+
+Prints ONE JSON line.  value = local tokens/s; also TFLOP/s by the
+expert-FFN count 6*(routed rows + tokens)*D*I (MoK paper §4.1; 6*T*(k+1)*D*I
+when every expert is local) and its fraction of the dense MFMA peak of the
+routed precision, a roofline of the dominant kernel (up/gate + SwiGLU) timed
+with HIP events inside the timed region, a per-kernel breakdown with each
+kernel's algorithmic bytes and FLOP, and the CPU oracle timed on a sample.
 """
 
 from __future__ import annotations
@@ -37,11 +48,11 @@ def log(*a):
 
 
 def parse():
-    ap = argparse.ArgumentParser(description=__doc__)
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dsv3", choices=["tiny", "mid", "dsv3", "mx"])
+    ap.add_argument("--workload", default="dsv3", choices=["tiny", "mid", "dsv3", "mx", "ep64"])
     ap.add_argument("--precision", default=None, choices=["bf16", "mxfp8"],
                     help="routed-expert precision (default: mxfp8 for the mx workload, else bf16)")
     ap.add_argument("--minibatch", type=int, default=0, help="rows per minibatch b (0: all routed rows)")
@@ -49,7 +60,7 @@ def parse():
     ap.add_argument("--routing", default="x", choices=["x", "gaussian", "zipf"],
                     help="x: router projection from x; gaussian/zipf: given fp32 logits")
     ap.add_argument("--cpu-sample", type=int, default=-1,
-                    help="tokens of the oracle's timed CPU sample (0: skip; default 48, 4 in MXFP8)")
+                    help="tokens of the oracle's timed CPU sample (0: skip; default 48, 8 in MXFP8, 512 for ep64)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy a MIB-MiB buffer 3 times with a plain device copy (a known-size "
@@ -65,28 +76,17 @@ def src_digest(*names):
     return h.hexdigest()[:16]
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (expert parallelism across GPUs is "
-              "designed, not built); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+class Job:
+    """One benchmark configuration: its layer, inputs and step function."""
 
-    import numpy as np
-    import torch
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
 
-    import synth
-    from mixture_experts_layer_counts_amd import MoELayer, _lib, shape_for
 
-    if not os.path.exists(_lib.LIB_PATH):
-        from mixture_experts_layer_counts_amd import build
-        build.build()
-    lib = _lib.load()
-    dev = torch.device("cuda", 0)
+def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
+    """All experts on one GPU (R = 1)."""
     w = synth.workload(args.workload, routing=args.routing)
     precision = args.precision or ("mxfp8" if args.workload == "mx" else "bf16")
-    mx = precision == "mxfp8"
     P = w.T * w.k
     b = args.minibatch or P
     C = args.ring or b
@@ -94,15 +94,14 @@ def main():
         f"routing={args.routing}; {precision}; drawing inputs on {torch.cuda.get_device_name(0)}")
     t0 = time.time()
     inp = synth.make_inputs(w, device="cuda")
-    torch.cuda.synchronize()
-    log(f"inputs ready in {time.time() - t0:.1f}s")
     weights = inp
-    if mx:  # routed weights quantised ahead of time (MoK paper §3.4), outside the timed region
-        from mixture_experts_layer_counts_amd import quantize_mxfp8
+    if precision == "mxfp8":  # routed weights quantised ahead of time (MoK paper §3.4), outside the timed region
         weights = {n: inp[n] for n in ("ws_gate", "ws_up", "ws_down")}
         for n in ("gate", "up", "down"):
             weights["q_" + n], weights["s_" + n] = quantize_mxfp8(inp["w_" + n])
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda", 0)
     layer = MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
                                precision=precision), device=dev)
     x, wr, logits_in = inp["x"], inp["w_router"], inp.get("logits")
@@ -117,23 +116,129 @@ def main():
         layer.forward(weights, x, x, gate, sched, out32=False, out=out)
         return sched
 
-    for _ in range(args.warmup):
-        sched = step()
+    return Job(name=w.name, w=w, R=1, c=0, T=w.T, E_route=w.E, P=P, b=b, C=C, precision=precision, layer=layer,
+               inp=inp, step=step, routed_from_x=logits_in is None,
+               config={"workload": f"{w.name}: T={w.T} D={w.D} I={w.I} E={w.E} top-{w.k} + 1 shared "
+                                   f"(I={w.I_shared})", "minibatch_rows": b, "ring_rows": C,
+                       "routing": "router projection from x" if logits_in is None else f"given {args.routing} logits"})
+
+
+def setup_ep64(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
+    """One rank's share at EP = 64 (DeepSeek-V3 expert shape)."""
+    import numpy as np
+    R, N, k, L, c, E_total = 64, 4096, 8, 4, 0, 256
+    counts = synth.zipf_counts(32768, L, 1.2)
+    P = int(sum(counts))
+    precision = args.precision or "bf16"
+    w = synth.Workload("ep64", T=R * N, D=7168, I=2048, E=L, k=k, I_shared=2048, seed=50)
+    b = args.minibatch or P
+    C = args.ring or b
+    log(f"workload ep64: R={R} source ranks x N={N} tokens, top-{k} of {E_total}; rank {c} holds {L} experts "
+        f"receiving {P} rows (Zipf 1.2 counts {counts}); D={w.D} I={w.I}; b={b} C={C}; {precision}")
+    t0 = time.time()
+    inp = synth.make_inputs(w, device="cuda")  # x: the pooled token rows of all 64 ranks
+    A = torch.from_numpy(synth.ep_share_routes(R, N, k, E_total, c, L, counts, seed=50)).to("cuda")
+    wr = synth.make_inputs(synth.Workload("ep64-router", T=1, D=w.D, I=64, E=E_total, k=k, I_shared=64, seed=51),
+                           device="cuda", with_weights=False)["w_router"]
+    weights = inp
+    if precision == "mxfp8":
+        weights = {n: inp[n] for n in ("ws_gate", "ws_up", "ws_down")}
+        for n in ("gate", "up", "down"):
+            weights["q_" + n], weights["s_" + n] = quantize_mxfp8(inp["w_" + n])
     torch.cuda.synchronize()
-    if layer.device_error():
-        raise RuntimeError(f"device error word {layer.device_error():#x}")
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda", 0)
+    # routing of this rank's own tokens (router width E_total); the routes of
+    # all 64 ranks, this one's included, come from the Zipf-share generator
+    router = MoELayer(shape_for(N, w.D, w.I, E_total, k, I_shared=w.I_shared, minibatch_rows=1, ring_rows=1),
+                      device=dev)
+    layer = MoELayer(shape_for(N, w.D, w.I, E_total, k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
+                               precision=precision, R=R, rank=c, max_rows=P), device=dev)
+    x_pool = inp["x"]
+    x_local = x_pool[c * N:(c + 1) * N]
+    out = torch.empty((N, w.D), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        _, _, gate = router.route(x_local, wr)
+        sched = layer.schedule(A)
+        layer.forward(weights, x_pool, x_local, gate, sched, out32=False, out=out)
+        return sched
+
+    return Job(name="ep64", w=w, R=R, T=N, E_route=E_total, P=P, b=b, C=C, precision=precision, layer=layer,
+               inp=inp, step=step, routed_from_x=True, A=A, c=c, L=L, wr=wr, router=router,
+               config={"workload": f"ep64: one rank of 64 (4 local experts D={w.D} I={w.I}, {P} routed rows, "
+                                   f"Zipf(1.2) counts {counts}; shared expert on {N} tokens)",
+                       "minibatch_rows": b, "ring_rows": C, "routing": "router projection from x (local tokens); "
+                                                                       "routes of all ranks synthetic"})
+
+
+def kernel_model(job, offsets, sched_src):
+    """Algorithmic HBM bytes and FLOP of each kernel per step: every operand
+    read once and every result written once."""
+    import numpy as np
+    w, T, P, E = job.w, job.T, job.P, job.E_route
+    D, I, Is, k = w.D, w.I, w.I_shared, w.k
+    mx = job.precision == "mxfp8"
+    wb = 1.0 + 1.0 / 32 if mx else 2.0  # bytes per routed weight / activation element
+    counts = np.diff(offsets)
+    touched = int(np.count_nonzero(counts))
+    unique_src = len(np.unique(sched_src[:P] // k)) if P else 0
+    local_routes = int(np.count_nonzero(job.route_dst_local >= 0))
+    m = {
+        "router_gemm": (T * D * 2 + E * D * 2 + T * E * 4, 2.0 * T * E * D),
+        "topk": (T * E * 4 + T * k * 8, 0.0),
+        "schedule": (job.R * T * k * 8 + P * 4 + len(offsets) * 8, 0.0),
+        "tiles": (len(offsets) * 4, 0.0),
+        "shared_up": (T * D * 2 + 2 * Is * D * 2 + T * Is * 2, 4.0 * T * Is * D),
+        "shared_down": (T * Is * 2 + D * Is * 2 + T * D * 4, 2.0 * T * D * Is),
+        "gather": (unique_src * D * 2 + P * D * wb, 0.0),
+        "up_gate": (touched * 2 * I * D * wb + P * D * wb + P * I * wb, 4.0 * P * I * D),
+        "down": (touched * D * I * wb + P * I * wb + P * D * 2, 2.0 * P * D * I),
+        "combine": (local_routes * D * 2 + T * D * 4 + T * D * 2 + T * k * 8, 0.0),
+    }
+    return m
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (expert parallelism across GPUs is "
+              "designed, not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from mixture_experts_layer_counts_amd import MoELayer, _lib, quantize_mxfp8, shape_for
+
+    lib = _lib.load()  # fails loudly when the HIP library is not built
+    setup = setup_ep64 if args.workload == "ep64" else setup_single
+    job = setup(args, torch, synth, MoELayer, shape_for, quantize_mxfp8)
+    mx = job.precision == "mxfp8"
+    peak_mma = PEAK_FP8 if mx else PEAK_BF16
+
+    for _ in range(args.warmup):
+        sched = job.step()
+    torch.cuda.synchronize()
+    if job.layer.device_error():
+        raise RuntimeError(f"device error word {job.layer.device_error():#x}")
     offsets = sched["offsets"].cpu().numpy().astype(np.int64)
+    sched_src = sched["sched"].cpu().numpy().astype(np.int64)
+    rd = sched["route_dst"].cpu().numpy()
+    job.route_dst_local = rd[job.c * job.T * job.w.k:(job.c + 1) * job.T * job.w.k] if job.R > 1 else rd
     log(f"warmup done ({args.warmup} steps); per-expert rows min/max = "
         f"{int(np.diff(offsets).min())}/{int(np.diff(offsets).max())}")
 
     # timed region, with the dominant kernel bracketed by HIP events on its stream
     dominant = "up_gate"
-    n_launch_per_step = (P + b - 1) // b
+    n_launch_per_step = (job.P + job.b - 1) // job.b
     _lib.check("moe_probe_begin", lib.moe_probe_begin(_lib.KERNELS[dominant], args.steps * n_launch_per_step))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        job.step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     tot, n = ctypes.c_double(), ctypes.c_int32()
@@ -143,37 +248,43 @@ def main():
     log(f"timed {args.steps} steps: {ms:.3f} ms/step; {dominant}: {n.value} launches, {dom_ms:.3f} ms each")
 
     # per-kernel breakdown (separate untimed passes, one probe per kernel)
+    model = kernel_model(job, offsets, sched_src)
     kernels = {}
     if not args.no_breakdown:
         reps = max(3, min(args.steps, 10))
         for name, kid in _lib.KERNELS.items():
-            if name == "router_gemm" and logits_in is not None:
-                continue
             _lib.check("moe_probe_begin", lib.moe_probe_begin(kid, reps * max(n_launch_per_step, 1) + 4))
             for _ in range(reps):
-                step()
+                job.step()
             _lib.check("moe_probe_end", lib.moe_probe_end(ctypes.byref(tot), ctypes.byref(n)))
-            if n.value:
-                kernels[name] = {"ms_per_step": round(tot.value / reps, 4), "launches_per_step": n.value // reps}
+            if not n.value:
+                continue
+            t = tot.value / reps * 1e-3
+            nbytes, flops = model[name]
+            peak_k = peak_mma if name in ("up_gate", "down") else PEAK_BF16
+            e = {"ms_per_step": round(t * 1e3, 4), "launches_per_step": n.value // reps,
+                 "alg_bytes": int(nbytes), "GB_per_s": round(nbytes / t / 1e9, 1),
+                 "hbm_frac": round(nbytes / t / PEAK_HBM, 4)}
+            if flops:
+                e.update({"alg_flop": flops, "TFLOP_per_s": round(flops / t / 1e12, 1),
+                          "mfma_frac": round(flops / t / peak_k, 4)})
+            e["bound"] = "mfma" if flops / peak_k > nbytes / PEAK_HBM else "hbm"
+            kernels[name] = e
         log("breakdown:", json.dumps(kernels))
 
-    # roofline of the dominant kernel: algorithmic bytes and flops per launch.
-    # Per launch: the gate and up rows of every expert the minibatch touches,
-    # the minibatch's ring rows read once and its h rows written once (bf16,
-    # or E4M3 bytes plus one scale byte per 32 in MXFP8).
+    # roofline of the dominant kernel per launch: the gate and up rows of every
+    # expert the minibatch touches, its ring rows read once and its h rows
+    # written once (bf16, or E4M3 bytes plus one scale byte per 32 in MXFP8)
+    w = job.w
     counts = np.diff(offsets)
-    if mx:
-        w_bytes_expert = 2 * w.I * (w.D + w.D // 32)
-        a_row, h_row, peak_mma = w.D + w.D // 32, w.I + w.I // 32, PEAK_FP8
-    else:
-        w_bytes_expert = 2 * w.I * w.D * 2
-        a_row, h_row, peak_mma = w.D * 2, w.I * 2, PEAK_BF16
+    wb = 1.0 + 1.0 / 32 if mx else 2.0
     launches = []
     for m in range(n_launch_per_step):
-        lo, hi = m * b, min((m + 1) * b, P)
+        lo, hi = m * job.b, min((m + 1) * job.b, job.P)
         touched = int(np.count_nonzero((offsets[:-1] < hi) & (offsets[1:] > lo) & (counts > 0)))
         rows = hi - lo
-        launches.append((touched * w_bytes_expert + rows * a_row + rows * h_row, 2.0 * rows * 2 * w.I * w.D))
+        launches.append((touched * 2 * w.I * w.D * wb + rows * w.D * wb + rows * w.I * wb,
+                         2.0 * rows * 2 * w.I * w.D))
     alg_bytes = float(np.mean([l[0] for l in launches]))
     alg_flops = float(np.mean([l[1] for l in launches]))
     t_dom = dom_ms * 1e-3
@@ -183,12 +294,12 @@ def main():
     else:
         achieved, peak, unit = alg_flops / t_dom / 1e12, peak_mma / 1e12, "TFLOP/s"
     traffic = None
-    tr_path = os.path.join(ROOT, "profiles", f"traffic_{dominant}_{w.name}.json")
+    tr_path = os.path.join(ROOT, "profiles", f"traffic_{dominant}_{job.name}.json")
     if os.path.exists(tr_path):
         tr = json.load(open(tr_path))
         src = "gemm_mx.hip" if mx else "gemm.hip"
-        if tr.get("src_digest") == src_digest(src) and tr.get("minibatch_rows") == b and \
-                tr.get("precision", "bf16") == precision:
+        if tr.get("src_digest") == src_digest(src) and tr.get("minibatch_rows") == job.b and \
+                tr.get("precision", "bf16") == job.precision:
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -197,10 +308,10 @@ def main():
                 "mfma_frac": round(alg_flops / t_dom / peak_mma, 4),
                 "hbm_frac": round(alg_bytes / t_dom / PEAK_HBM, 4)}
 
-    flops = w.flops()
+    flops = 6.0 * (job.P + job.T) * w.D * w.I
     result = {
         "metric": METRIC,
-        "value": round(w.T / (ms * 1e-3), 1),
+        "value": round(job.T / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -209,51 +320,67 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if not mx else "mxfp8 (e4m3 + e8m0/32) routed, bf16 shared",
+        "dtype": "mxfp8 (e4m3 + e8m0/32) routed, bf16 shared" if mx else "bf16",
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) bf16 weights drawn on the GPU)",
-        "config": {"workload": f"{w.name}: T={w.T} D={w.D} I={w.I} E={w.E} top-{w.k} + 1 shared (I={w.I_shared})",
-                   "minibatch_rows": b, "ring_rows": C,
-                   "routing": "router projection from x" if logits_in is None else f"given {args.routing} logits"},
+        "config": job.config,
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-        "mfma_peak_frac": round(flops / (ms * 1e-3) / (PEAK_FP8 if mx else PEAK_BF16), 4),
+        "mfma_peak_frac": round(flops / (ms * 1e-3) / peak_mma, 4),
+        "routed_rows_per_s": round(job.P / (ms * 1e-3), 1),
         "roofline": roofline,
         "kernels": kernels,
     }
 
     if args.calibrate_copy > 0:
-        n = args.calibrate_copy << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
+        nb = args.calibrate_copy << 20
+        src_t = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+        dst_t = torch.empty_like(src_t)
         for _ in range(3):
-            dst.copy_(src)
+            dst_t.copy_(src_t)
         torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = n
-        del src, dst
+        result["copy_calibration_bytes"] = nb
+        del src_t, dst_t
 
-    n_cpu = args.cpu_sample if args.cpu_sample >= 0 else (4 if mx else 48)
+    n_cpu = args.cpu_sample if args.cpu_sample >= 0 else (512 if job.name == "ep64" else (8 if mx else 48))
     if n_cpu > 0:
-        result["cpu_baseline"] = cpu_baseline(w, inp, n_cpu, precision)
+        result["cpu_baseline"] = (cpu_baseline_ep(job, n_cpu) if job.name == "ep64"
+                                  else cpu_baseline(job, n_cpu))
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, inp, n_tok, precision="bf16"):
-    """The oracle, as it stands, on the first n_tok tokens of the same workload.
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(os.cpu_count())
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: numpy's default pool
+        return os.cpu_count()
 
-    In MXFP8 the oracle's own quantisation of the touched experts' weights is
-    done beforehand and not timed (the method quantises weights ahead of time).
-    """
+
+def _oracle_mx(host, experts):
+    """The oracle's own MX quantisation of the given experts (not timed: the
+    method quantises weights ahead of time)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import bf16 as obf16
+    from oracle import mx as omx
+    jobs = [(n, int(e)) for n in ("gate", "up", "down") for e in experts]
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        res = dict(zip(jobs, ex.map(lambda j: omx.quantize(obf16.to_f64(host["w_" + j[0]][j[1]])), jobs)))
+    for n in ("gate", "up", "down"):
+        host["q_" + n] = _ExpertTable({int(e): res[(n, int(e))][0] for e in experts})
+        host["s_" + n] = _ExpertTable({int(e): res[(n, int(e))][1] for e in experts})
+
+
+def cpu_baseline(job, n_tok):
+    """The oracle, as it stands, on the first n_tok tokens of the same workload."""
     import numpy as np
     import torch
 
     import synth
     from oracle import moe as ref
 
-    try:
-        from threadpoolctl import threadpool_info, threadpool_limits
-        threadpool_limits(os.cpu_count())
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: numpy's default pool
-        threads = os.cpu_count()
+    w, inp = job.w, job.inp
+    threads = _threads()
     tok = np.arange(n_tok)
     xb = synth.bits(inp["x"][:n_tok])
     wrb = synth.bits(inp["w_router"])
@@ -271,27 +398,43 @@ def cpu_baseline(w, inp, n_tok, precision="bf16"):
             "ws_down": synth.bits(inp["ws_down"])}
     for n in ("w_gate", "w_up", "w_down"):
         sub = synth.bits(inp[n][torch.as_tensor(experts, device=inp[n].device)])
-        arr = {int(e): sub[i] for i, e in enumerate(experts)}
-        host[n] = _ExpertTable(arr)
-    if precision == "mxfp8":
-        from concurrent.futures import ThreadPoolExecutor
-
-        from oracle import bf16 as obf16
-        from oracle import mx as omx
-        jobs = [(n, int(e)) for n in ("gate", "up", "down") for e in experts]
-        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
-            res = dict(zip(jobs, ex.map(lambda j: omx.quantize(obf16.to_f64(host["w_" + j[0]][j[1]])), jobs)))
-        for n in ("gate", "up", "down"):
-            host["q_" + n] = _ExpertTable({int(e): res[(n, int(e))][0] for e in experts})
-            host["s_" + n] = _ExpertTable({int(e): res[(n, int(e))][1] for e in experts})
+        host[n] = _ExpertTable({int(e): sub[i] for i, e in enumerate(experts)})
+    if job.precision == "mxfp8":
+        _oracle_mx(host, experts)
     t0 = time.perf_counter()
-    ref.forward(xb, host, lg, w.k, precision=precision, tokens=tok)
-    t_fwd = time.perf_counter() - t0
-    secs = t_route + t_fwd
+    ref.forward(xb, host, lg, w.k, precision=job.precision, tokens=tok)
+    secs = t_route + time.perf_counter() - t0
     return {"value": round(n_tok / secs, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n_tok} tokens of the {w.name} workload ({len(experts)} distinct routed experts + "
                       f"the shared expert), numpy fp64 on {platform.processor() or platform.machine()}, "
                       f"os.cpu_count()={os.cpu_count()}; {secs:.1f}s"}
+
+
+def cpu_baseline_ep(job, n_tok):
+    """The oracle's EP share on n_tok local tokens' worth of work: their router
+    projection, their output, and P/T routed rows per token (the first rows of
+    the schedule), so that tokens/s compares with the GPU's local tokens/s."""
+    import numpy as np
+
+    import synth
+    from oracle import moe as ref
+
+    w, inp = job.w, job.inp
+    threads = _threads()
+    k, T, c = w.k, job.T, job.c
+    n_rows = int(round(n_tok * job.P / T))
+    A = job.A.cpu().numpy()
+    host = {n: synth.bits(inp[n]) for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+    x_pool = synth.bits(inp["x"])
+    g = np.full((T, k), 1.0 / k)
+    t0 = time.perf_counter()
+    ref.router_logits(x_pool[c * T:c * T + n_tok], synth.bits(job.wr))
+    ref.ep_share_forward(x_pool, host, A, c, job.L, k, g, positions=np.arange(n_rows), tokens=np.arange(n_tok))
+    secs = time.perf_counter() - t0
+    return {"value": round(n_tok / secs, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_tok} local tokens of the ep64 share (their router projection and output, plus the "
+                      f"first {n_rows} of the {job.P} routed rows), numpy fp64 on "
+                      f"{platform.processor() or platform.machine()}, os.cpu_count()={os.cpu_count()}; {secs:.1f}s"}
 
 
 class _ExpertTable:

@@ -176,6 +176,19 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Where moe_forward leaves the routed output rows inside the workspace (bf16,
+ * row stride D): with R == 1, [T*k, D] indexed by route t*k + s; with R > 1,
+ * the outbox [max_rows, D] indexed by schedule position p (rows >= P are not
+ * written): the rows this rank returns to their source ranks, where the
+ * table read as {dst_rank, dst_index} places them (MoK paper §3.1).  *rows
+ * receives the device address, *n_rows the row count.  Host-only arithmetic
+ * on ws: no device access, no synchronisation.  The rows are valid after
+ * moe_forward and until the next call that uses the same workspace.
+ */
+moe_status moe_routed_rows(const moe_shape* shape, const void* ws, size_t ws_bytes, const void** rows,
+                           int64_t* n_rows);
+
+/*
  * MX quantisation along rows (MoK paper §3.4, "MXFP8 Support": weights are
  * pre-quantised by a dedicated kernel).  src [rows, K] bf16, K a multiple of
  * 32 -> q [rows, K] E4M3FN and scale [rows, K/32] E8M0: per block of 32,

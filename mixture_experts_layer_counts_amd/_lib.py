@@ -51,6 +51,8 @@ _SIGS = {
     "moe_schedule": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_forward": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_routed_rows": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_size_t, ctypes.POINTER(_P),
+                                       ctypes.POINTER(ctypes.c_int64)]),
     "moe_quantize_mxfp8": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]),
     "moe_get_device_error": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_size_t, _P,
                                             ctypes.POINTER(ctypes.c_int32)]),

@@ -161,6 +161,15 @@ class MoELayer:
         out, out32 = self.forward(weights, x, x, gate, sched)
         return {"logits": lg, "idx": idx, "gate": gate, "out": out, "out32": out32, **sched}
 
+    def routed_rows(self) -> torch.Tensor:
+        """The routed output rows moe_forward left in the workspace (a view,
+        bf16 [n, D]): by route t*k+s when R == 1, by schedule position when R > 1."""
+        addr, n = ctypes.c_void_p(), ctypes.c_int64()
+        _lib.check("moe_routed_rows", self.lib.moe_routed_rows(ctypes.byref(self.shape), _ptr(self.ws), self.ws_bytes,
+                                                               ctypes.byref(addr), ctypes.byref(n)))
+        off, D = addr.value - self.ws.data_ptr(), self.shape.D
+        return self.ws[off:off + n.value * D * 2].view(torch.bfloat16).view(n.value, D)
+
     def device_error(self) -> int:
         code = ctypes.c_int32(0)
         _lib.check("moe_get_device_error", self.lib.moe_get_device_error(

@@ -426,6 +426,17 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
                                         D, k, R > 1, static_cast<uint16_t*>(out), out32, s));
 }
 
+moe_status moe_routed_rows(const moe_shape* shape, const void* ws, size_t ws_bytes, const void** rows,
+                           int64_t* n_rows) {
+  Layout L;
+  const moe_status st = check_ws(shape, ws, ws_bytes, &L);
+  if (st != MOE_OK) return st;
+  if (!rows || !n_rows) return MOE_ERR_INVALID_ARG;
+  *rows = static_cast<const char*>(ws) + L.Y;
+  *n_rows = L.y_rows;
+  return MOE_OK;
+}
+
 moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale, void* stream) {
   if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;

@@ -245,6 +245,73 @@ def forward(x_bits: np.ndarray, weights: Dict[str, np.ndarray], logits_f32: np.n
     return {"idx": idx, "gates": g, "Y": Y, "shared": sh, "out": combine(sh, g[tok], Y)}
 
 
+# ----------------------------------------------------------------------------
+# One rank's share under expert parallelism (§2.1, Fig. 2; §3.1)
+# ----------------------------------------------------------------------------
+
+def _expert_rows(x: np.ndarray, weights: Dict[str, np.ndarray], experts: np.ndarray,
+                 precision: str) -> np.ndarray:
+    """f_{experts[i]}(x[i]) for rows x (fp64, already MX-rounded in MXFP8
+    mode), with h and the output row stored as the method stores them."""
+    out = np.zeros_like(x)
+    h_store = "bf16" if precision == "bf16" else "mx"
+    for e in np.unique(experts):
+        rows = np.nonzero(experts == e)[0]
+        wg, wu, wd = _expert_weights(weights, int(e), precision)
+        out[rows] = ffn(x[rows], wg, wu, wd, h_store=h_store, y_store="bf16")
+    return out
+
+
+def ep_share_forward(x_src_bits: np.ndarray, weights: Dict[str, np.ndarray], A: np.ndarray, c: int, L: int,
+                     k: int, gates_local: np.ndarray, precision: str = "bf16",
+                     positions: Optional[np.ndarray] = None,
+                     tokens: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Rank c's part of the layer when the routed experts are spread over R
+    ranks, L per rank (rank c holds global experts c*L .. c*L+L-1).
+
+    x_src_bits [R*N, D]: token rows of every source rank (rank r's token t is
+      row r*N + t); rank c's own tokens are rows c*N .. c*N+N-1.
+    weights: rank c's experts, indexed by local expert l = global - c*L, and
+      the shared expert.
+    A [R, N*k]: the global expert of each route (route j of rank r is slot
+      j % k of token j // k); gates_local [N, k]: the gates of rank c's tokens.
+
+    Returns the schedule of the routes rank c receives (Algorithm 1) and
+      rows [len(positions), D]: at schedule position p, the output of the route
+        (r, j) it holds, f_{A[r,j]}(x_src[r*N + j//k]) stored in bf16: what
+        rank c sends back to rank r, where route_dst read as a destination
+        index places it (§3.1 table reuse);
+      out [len(tokens), D]: for rank c's own token t, f_shared(x_t) plus the
+        gate-weighted rows of its slots whose expert lives on rank c (the rows
+        of the other slots are added where they arrive).
+    """
+    A = np.asarray(A, dtype=np.int64)
+    R, NK = A.shape
+    N = NK // k
+    sch = schedule(A, c, L)
+    P = int(sch["offsets"][-1])
+    pos = np.arange(P) if positions is None else np.asarray(positions, dtype=np.int64)
+    route = sch["sched"][pos]
+    r, j = route // NK, route % NK
+    x_rows = _bf16.to_f64(x_src_bits[r * N + j // k])
+    if precision == "mxfp8":
+        x_rows = _mx.round_f64(x_rows)
+    rows = _expert_rows(x_rows, weights, A[r, j] - c * L, precision)
+
+    tok = np.arange(N) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    x_local = x_src_bits[c * N:(c + 1) * N]
+    sh = shared_output(x_local, weights, tok)
+    sel = A[c].reshape(N, k)[tok]
+    ti, si = np.nonzero((sel >= c * L) & (sel < c * L + L))
+    xl = _bf16.to_f64(x_local[tok[ti]])
+    if precision == "mxfp8":
+        xl = _mx.round_f64(xl)
+    Y = np.zeros((len(tok), k, x_src_bits.shape[1]), dtype=np.float64)
+    Y[ti, si] = _expert_rows(xl, weights, sel[ti, si] - c * L, precision)
+    out = combine(sh, np.asarray(gates_local, dtype=np.float64)[tok], Y)
+    return {**sch, "positions": pos, "rows": rows, "out": out}
+
+
 def layer_flops(T: int, D: int, I: int, k: int) -> float:
     """Expert-FFN FLOP of one forward, 6*T*(k+1)*D*I (§4.1)."""
     return 6.0 * T * (k + 1) * D * I
