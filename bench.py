@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=-1,
                     help="tokens of the oracle's timed CPU sample (0: skip; default 48, 8 in MXFP8, 512 for ep64)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
+    ap.add_argument("--sweep", default="", metavar="B[:C],...",
+                    help="after the main run, time the step at these minibatch sizes b (ring C, default b) and "
+                         "report them under 'granularity_sweep'")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy a MIB-MiB buffer 3 times with a plain device copy (a known-size "
                          "reference for hardware byte counters)")
@@ -102,22 +105,26 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
     dev = torch.device("cuda", 0)
-    layer = MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
-                               precision=precision), device=dev)
     x, wr, logits_in = inp["x"], inp["w_router"], inp.get("logits")
     out = torch.empty((w.T, w.D), dtype=torch.bfloat16, device=dev)
 
-    def step():
-        if logits_in is not None:
-            _, idx, gate = layer.route(None, None, logits_in)
-        else:
-            _, idx, gate = layer.route(x, wr)
-        sched = layer.schedule(idx)
-        layer.forward(weights, x, x, gate, sched, out32=False, out=out)
-        return sched
+    def make(b, C):
+        layer = MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
+                                   precision=precision), device=dev)
 
+        def step():
+            if logits_in is not None:
+                _, idx, gate = layer.route(None, None, logits_in)
+            else:
+                _, idx, gate = layer.route(x, wr)
+            sched = layer.schedule(idx)
+            layer.forward(weights, x, x, gate, sched, out32=False, out=out)
+            return sched
+        return layer, step
+
+    layer, step = make(b, C)
     return Job(name=w.name, w=w, R=1, c=0, T=w.T, E_route=w.E, P=P, b=b, C=C, precision=precision, layer=layer,
-               inp=inp, step=step, routed_from_x=logits_in is None,
+               inp=inp, step=step, make=make, routed_from_x=logits_in is None,
                config={"workload": f"{w.name}: T={w.T} D={w.D} I={w.I} E={w.E} top-{w.k} + 1 shared "
                                    f"(I={w.I_shared})", "minibatch_rows": b, "ring_rows": C,
                        "routing": "router projection from x" if logits_in is None else f"given {args.routing} logits"})
@@ -152,20 +159,24 @@ def setup_ep64(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
     # all 64 ranks, this one's included, come from the Zipf-share generator
     router = MoELayer(shape_for(N, w.D, w.I, E_total, k, I_shared=w.I_shared, minibatch_rows=1, ring_rows=1),
                       device=dev)
-    layer = MoELayer(shape_for(N, w.D, w.I, E_total, k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
-                               precision=precision, R=R, rank=c, max_rows=P), device=dev)
     x_pool = inp["x"]
     x_local = x_pool[c * N:(c + 1) * N]
     out = torch.empty((N, w.D), dtype=torch.bfloat16, device=dev)
 
-    def step():
-        _, _, gate = router.route(x_local, wr)
-        sched = layer.schedule(A)
-        layer.forward(weights, x_pool, x_local, gate, sched, out32=False, out=out)
-        return sched
+    def make(b, C):
+        layer = MoELayer(shape_for(N, w.D, w.I, E_total, k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
+                                   precision=precision, R=R, rank=c, max_rows=P), device=dev)
 
+        def step():
+            _, _, gate = router.route(x_local, wr)
+            sched = layer.schedule(A)
+            layer.forward(weights, x_pool, x_local, gate, sched, out32=False, out=out)
+            return sched
+        return layer, step
+
+    layer, step = make(b, C)
     return Job(name="ep64", w=w, R=R, T=N, E_route=E_total, P=P, b=b, C=C, precision=precision, layer=layer,
-               inp=inp, step=step, routed_from_x=True, A=A, c=c, L=L, wr=wr, router=router,
+               inp=inp, step=step, make=make, routed_from_x=True, A=A, c=c, L=L, wr=wr, router=router,
                config={"workload": f"ep64: one rank of 64 (4 local experts D={w.D} I={w.I}, {P} routed rows, "
                                    f"Zipf(1.2) counts {counts}; shared expert on {N} tokens)",
                        "minibatch_rows": b, "ring_rows": C, "routing": "router projection from x (local tokens); "
@@ -330,6 +341,9 @@ def main():
         "kernels": kernels,
     }
 
+    if args.sweep:
+        result["granularity_sweep"] = sweep(job, args, torch)
+
     if args.calibrate_copy > 0:
         nb = args.calibrate_copy << 20
         src_t = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
@@ -345,6 +359,35 @@ def main():
         result["cpu_baseline"] = (cpu_baseline_ep(job, n_cpu) if job.name == "ep64"
                                   else cpu_baseline(job, n_cpu))
     print(json.dumps(result), flush=True)
+
+
+def sweep(job, args, torch):
+    """Step time at other minibatch sizes b and ring sizes C (MoK paper §3.2:
+    finer minibatches overlap better but pay per-minibatch overheads)."""
+    out = []
+    job.layer = None  # release the main workspace first
+    for item in args.sweep.split(","):
+        b, _, C = item.partition(":")
+        b = min(int(b), job.P)
+        C = int(C) if C else b
+        layer, step = job.make(b, C)
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = max(3, args.steps // 2)
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / n
+        if layer.device_error():
+            raise RuntimeError(f"device error word {layer.device_error():#x} at b={b} C={C}")
+        out.append({"minibatch_rows": b, "ring_rows": C, "minibatches": (job.P + b - 1) // b,
+                    "ms_per_step": round(ms, 4), "tokens_per_s": round(job.T / (ms * 1e-3), 1)})
+        log(f"sweep b={b} C={C}: {ms:.3f} ms/step")
+        del layer, step
+        torch.cuda.empty_cache()
+    return out
 
 
 def _threads():
