@@ -8,12 +8,13 @@
 // one expert sit contiguously, so no local reordering precedes the GEMMs).
 //
 // Tiling.  A workgroup of 4 waves computes a BM x BN output tile with
-// v_mfma_f32_32x32x16_bf16; each wave owns a (BM/2) x (BN/2) quadrant.  Both
-// operands are K-contiguous (activation rows and weight rows), so each lane
-// feeds the matrix core with one 16-byte LDS read per operand.  K tiles of 64
-// are staged through LDS, double-buffered, with the next tile's global loads
-// in flight while the current one is multiplied.  The K loop always runs from
-// k = 0 in the same order and there is no split-K, so a row's result does not
+// v_mfma_f32_32x32x16_bf16; the waves form a 2 x 2 grid, and the 32-row MFMA
+// blocks of the tile are dealt to the two row groups in turn.  Both operands
+// are K-contiguous (activation rows and weight rows), so each lane feeds the
+// matrix core with one 16-byte LDS read per operand.  K tiles of 64 are staged
+// through LDS by direct loads: activation rows one stage ahead, weight rows
+// two stages ahead (they stream from HBM).  The K loop always runs from k = 0
+// in the same order and there is no split-K, so a row's result does not
 // depend on the tile or minibatch it falls in.
 //
 // Work order (routed).  The 256 MI355X CUs sit in 8 XCDs, each with its own
@@ -42,46 +43,61 @@ namespace moe {
 namespace {
 
 constexpr int kStageK = 64;  // K elements per pipeline stage (one 128-byte line per row)
-constexpr int kStages = 2;   // LDS ring depth
 
-// The K loop of one workgroup: an NST-stage LDS ring of BK-wide K tiles fed
-// by direct buffer->LDS loads (lane l's 16 bytes land at base + 16 l, so one
-// wave instruction fills 1 KB of a stage; each lane fetches the global chunk
-// the swizzle maps to its slot).  Stage kt+NST-1 is requested at the top of
-// step kt.  The 16-wide K steps of a stage run back to back with the next
-// step's fragments read under the current MFMAs; before the last step's MFMAs
-// the wave waits for stage kt+1 and passes the one barrier of the step, so
-// that stage kt+1's first fragments are read under them.  FML = 32-row MFMA
-// blocks of this wave that hold tile rows (the rest of the quadrant lies past
-// the tile and is skipped).
-template <int BM, int BN, int WM, int WN, int NB, int FML, int FM, int FN, int NST, int BK, int AI, int BI>
-__device__ __forceinline__ void k_loop_dma(char* smem, const TileSrc& src, const uint32_t (&a_off)[AI],
-                                           const uint32_t (&b_off)[BI], int nk, int a_rows, int tid, int wm, int wn,
-                                           f32x16_t (&acc)[NB][FM][FN]) {
-  constexpr int RB = BK * 2;  // bytes of one row of a stage
+// Row of the tile held by 32-row MFMA block fm of a wave in row group wm:
+// blocks are dealt to the WM row groups in turn, so that a partly filled
+// tile keeps every wave busy.
+template <int WM>
+__device__ __forceinline__ int tile_row(int wm, int fm) {
+  return (fm * WM + wm) * 32;
+}
+
+// The K loop of one workgroup.  BK-wide K tiles are staged through two LDS
+// rings fed by direct buffer->LDS loads (lane l's 16 bytes land at base + 16 l,
+// so one wave instruction fills 1 KB; each lane fetches the global chunk the
+// swizzle maps to its slot): activation rows in 2 slots, one stage ahead, and
+// weight rows in 3 slots, two stages ahead, since weights stream from HBM and
+// need the longer lead.  At the top of step kt the wave requests A(kt+1) and
+// B(kt+2), spread under the first two K sub-steps' MFMAs.  The 16-wide K
+// sub-steps run back to back with the next sub-step's fragments read under
+// the current MFMAs; before the last sub-step's MFMAs the wave waits for
+// A(kt+1) and B(kt+1) (B(kt+2) may stay in flight) and passes the one barrier
+// of the step, so stage kt+1's first fragments are read under them.  FML =
+// 32-row MFMA blocks of this wave that hold tile rows.
+template <int BM, int BN, int WM, int WN, int NB, int FML, int FM, int FN, int BK, int AI, int BI>
+__device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uint32_t (&a_off)[AI],
+                                       const uint32_t (&b_off)[BI], int nk, int a_rows, int tid, int wm, int wn,
+                                       f32x16_t (&acc)[NB][FM][FN]) {
+  constexpr int NSA = 2, NSB = 3;  // ring slots
+  constexpr int RB = BK * 2;        // bytes of one row of a stage
   constexpr int BROWS = NB * BN;
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int STAGE = (BM + BROWS) * RB;
-  constexpr int KS = BK / 16;  // 16-wide K steps per stage
+  constexpr int WTN = BN / WN;
+  constexpr int KS = BK / 16;  // 16-wide K sub-steps per stage
+  static_assert(KS >= 3, "loads are spread under the first two sub-steps");
   constexpr int ROWS_PER_LD = 1024 / RB;
   static_assert(AI * ROWS_PER_LD * 4 == BM && BI * ROWS_PER_LD * 4 == BROWS, "DMA instructions per wave per stage");
-  constexpr int NLD = AI + BI;
-  constexpr int VM_AHEAD = (NST - 2) * NLD;  // loads allowed in flight when a stage must be complete
-  static_assert(VM_AHEAD < 64, "vmcnt range");
+  static_assert(BI < 16, "vmcnt range");
+  constexpr int ASLOT = BM * RB, BSLOT = BROWS * RB;
+  char* const sa0 = smem;
+  char* const sb0 = smem + NSA * ASLOT;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
   const int frag_row = lane & 31, frag_c = lane >> 5;
 
-  auto issue = [&](int kt) __attribute__((always_inline)) {
-    const int buf = kt % NST;
-    const int ko = (kt < nk ? kt : nk - 1) * RB;  // past the end: the last stage again, into a free slot
-    char* sa = smem + buf * STAGE;
-    char* sb = sa + BM * RB;
+  // past the last stage the loads repeat it (into a free slot), so that every
+  // step issues the same number of loads
+  auto issue_a = [&](int kt) __attribute__((always_inline)) {
+    const int ko = (kt < nk ? kt : nk - 1) * RB;
+    char* sa = sa0 + (kt % NSA) * ASLOT;
     // A row groups past the tile are not fetched (their rows only feed dropped
-    // outputs); a dummy reload of the group's first row keeps the per-wave load
+    // outputs); a reload of the group's first row keeps the per-wave load
     // count, which the vmcnt waits rely on, the same for every wave
 #pragma unroll
     for (int j = 0; j < AI; ++j)
       dma16(src.a, sa + (wave * AI + j) * 1024, (wave * AI + j) * ROWS_PER_LD < a_rows ? a_off[j] : a_off[0], ko);
+  };
+  auto issue_b = [&](int kt) __attribute__((always_inline)) {
+    const int ko = (kt < nk ? kt : nk - 1) * RB;
+    char* sb = sb0 + (kt % NSB) * BSLOT;
 #pragma unroll
     for (int j = 0; j < BI; ++j) {
       const int g = wave * BI + j;  // ROWS_PER_LD-row group of the B stage
@@ -91,12 +107,12 @@ __device__ __forceinline__ void k_loop_dma(char* smem, const TileSrc& src, const
   using frag_a_t = bf16x8_t[FML > 0 ? FML : 1];
   using frag_b_t = bf16x8_t[NB][FN];
   auto read_frags = [&](int kt, int step, frag_a_t& af, frag_b_t& bfr) __attribute__((always_inline)) {
-    const char* sa = smem + (kt % NST) * STAGE;
-    const char* sb = sa + BM * RB;
+    const char* sa = sa0 + (kt % NSA) * ASLOT;
+    const char* sb = sb0 + (kt % NSB) * BSLOT;
     const int c = step * 2 + frag_c;
 #pragma unroll
     for (int fm = 0; fm < FML; ++fm)
-      af[fm] = *reinterpret_cast<const bf16x8_t*>(sa + swz<RB>(wm * WTM + fm * 32 + frag_row, c));
+      af[fm] = *reinterpret_cast<const bf16x8_t*>(sa + swz<RB>(tile_row<WM>(wm, fm) + frag_row, c));
 #pragma unroll
     for (int h = 0; h < NB; ++h)
 #pragma unroll
@@ -112,50 +128,57 @@ __device__ __forceinline__ void k_loop_dma(char* smem, const TileSrc& src, const
         for (int fn = 0; fn < FN; ++fn)
           acc[h][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[h][fn], acc[h][fm][fn], 0, 0, 0);
   };
-  constexpr int NMF = FML * NB * FN;  // MFMAs per 16-wide step
-  constexpr int NRD = FML + NB * FN;  // fragment reads per 16-wide step
-  auto interleave = [&]() __attribute__((always_inline)) {
+  constexpr int NMF = FML * NB * FN;  // MFMAs per 16-wide sub-step
+  constexpr int NRD = FML + NB * FN;  // fragment reads per 16-wide sub-step
+  // one fragment read under each MFMA; in sub-steps 0 and 1 also one load
+  // (A loads, then B loads) under each MFMA
+  auto interleave = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NMF; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (ks == 0 && i < AI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (ks == 1 && i < BI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   };
 
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue(s);
-  asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_AHEAD, 15)) : "memory");
+  issue_a(0);
+  issue_b(0);
+  issue_b(1);
+  asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI, 15)) : "memory");  // A(0), B(0) landed
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   frag_a_t af[2];
   frag_b_t bf[2];
   if constexpr (FML > 0) read_frags(0, 0, af[0], bf[0]);
   for (int kt = 0; kt < nk; ++kt) {
-    issue(kt + NST - 1);
+    issue_a(kt + 1);
+    issue_b(kt + 2);
     if constexpr (FML > 0) {
 #pragma unroll
       for (int ks = 0; ks + 1 < KS; ++ks) {
         read_frags(kt, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
         mfmas(af[ks & 1], bf[ks & 1]);
-        if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, NLD, 0);  // the stage's loads first
-        interleave();
+        interleave(ks);
       }
     }
-    // stage kt+1 has landed (this wave's loads) and this wave's reads of
-    // stage kt are done, before any wave refills a slot
-    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_AHEAD, 0)) : "memory");
+    // A(kt+1) and B(kt+1) have landed (this wave's loads; B(kt+2) may still
+    // be in flight) and this wave's reads of stage kt are done, before any
+    // wave refills a slot
+    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI, 0)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if constexpr (FML > 0) {
-      if (kt + 1 < nk) read_frags(kt + 1, 0, af[KS & 1], bf[KS & 1]);
+      // past the last stage this reads the repeated stage, and is not used
+      read_frags(kt + 1, 0, af[KS & 1], bf[KS & 1]);
       mfmas(af[(KS - 1) & 1], bf[(KS - 1) & 1]);
-      interleave();
+      interleave(KS);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still target LDS when the workgroup ends
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int NST, int BK>
+template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;  // B halves (gate, up)
   constexpr int BROWS = NB * BN;
@@ -167,7 +190,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
   static_assert(WM * WN == 4, "4 waves per workgroup");
   static_assert(FM >= 1 && FN >= 1 && AI * 4 * ROWS_PER_LD == BM && BI * 4 * ROWS_PER_LD == BROWS, "tile shape");
 
-  __shared__ __attribute__((aligned(1024))) char smem[NST * (BM + BROWS) * RB];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BM * RB + 3 * BROWS * RB];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
@@ -251,14 +274,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
 
   // 32-row MFMA blocks of this wave that hold tile rows (wave-uniform); the
   // K loop is instantiated per count so that its body is one straight block
-  int fm_live = (nrows - wm * WTM + 31) / 32;
+  int fm_live = ((nrows + 31) / 32 - wm + WM - 1) / WM;
   fm_live = fm_live < 0 ? 0 : (fm_live > FM ? FM : fm_live);
   const int nk = K / BK;
   switch (fm_live) {
 #define MOE_CASE(n)                                                                       \
   case n:                                                                                 \
     if constexpr (n <= FM)                                                                \
-      k_loop_dma<BM, BN, WM, WN, NB, n, FM, FN, NST, BK, AI, BI>(smem, src, a_off, b_off, nk, nrows, tid, wm, wn, acc); \
+      k_loop<BM, BN, WM, WN, NB, n, FM, FN, BK, AI, BI>(smem, src, a_off, b_off, nk, nrows, tid, wm, wn, acc); \
     break;
     MOE_CASE(0)
     MOE_CASE(1)
@@ -280,7 +303,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
     if (fm >= fm_live) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row_t = wm * WTM + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const int row_t = tile_row<WM>(wm, fm) + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
       if (row_t >= nrows) continue;
       const int64_t p = p0 + row_t;
       const int64_t crow = args.c_idx ? static_cast<int64_t>(args.c_idx[p]) : p - args.c_sub;
@@ -303,7 +326,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int NST = kStages, int BK = kStageK>
+template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK = kStageK>
 hipError_t run(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles = ROUTED ? a.max_tiles : (a.dense_rows + BM - 1) / BM;
   const int64_t n_blocks = (a.N + BN - 1) / BN;
@@ -311,7 +334,7 @@ hipError_t run(const GemmArgs& a, hipStream_t stream) {
   const int64_t grid = (work + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  gemm_kernel<BM, BN, WM, WN, EPI, ROUTED, NST, BK><<<static_cast<unsigned>(grid), 256, 0, stream>>>(a);
+  gemm_kernel<BM, BN, WM, WN, EPI, ROUTED, BK><<<static_cast<unsigned>(grid), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
