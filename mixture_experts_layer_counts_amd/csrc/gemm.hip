@@ -297,32 +297,69 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
       break;
   }
 
-  // ---- epilogue: lane holds column (lane % 32) and rows 8*(r/4) + 4*(lane/32) + r%4 ----
+  // ---- epilogue, staged through LDS so that rows leave in 16-byte pieces ----
+  // The MFMA layout gives lane l column l % 32 of rows 8*(r/4) + 4*(l/32) +
+  // r%4; written straight out that is a 2- or 4-byte store per lane.  The
+  // tile (or, for fp32 outputs, a band of it) is first written to LDS row by
+  // row, then copied out by all 256 threads in 16-byte chunks of whole rows.
+  constexpr int ESZ = (EPI == kEpiF32) ? 4 : 2;  // bytes per output element
+  constexpr int CS = BN * ESZ + 16;              // LDS row stride of the staged tile (padded against bank conflicts)
+  constexpr int LDS_BYTES = 2 * BM * RB + 3 * BROWS * RB;
+  constexpr int FMP_FIT = LDS_BYTES / CS / (WM * 32);  // 32-row blocks per row group that fit at once
+  constexpr int FMP = FMP_FIT < FM ? FMP_FIT : FM;
+  static_assert(FMP >= 1 && FM % FMP == 0, "epilogue bands");
+  constexpr int BAND = FMP * WM * 32;         // tile rows per band
+  constexpr int CPR = BN * ESZ / 16;          // 16-byte chunks per staged row
+  constexpr int EPC = 16 / ESZ;               // elements per chunk
+  const bool vec_ok = ((args.ldc * ESZ) % 16 == 0) && (reinterpret_cast<uintptr_t>(args.C) % 16 == 0);
+  __syncthreads();  // every wave is done with the K loop's LDS
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    if (fm >= fm_live) continue;
+  for (int band = 0; band < FM / FMP; ++band) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row_t = tile_row<WM>(wm, fm) + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      if (row_t >= nrows) continue;
-      const int64_t p = p0 + row_t;
-      const int64_t crow = args.c_idx ? static_cast<int64_t>(args.c_idx[p]) : p - args.c_sub;
+    for (int fm = band * FMP; fm < (band + 1) * FMP; ++fm) {
+      if (fm >= fm_live) continue;  // wave-uniform
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int col = n0 + wn * WTN + fn * 32 + (lane & 31);
-        if (col >= args.N) continue;
-        float v = acc[0][fm][fn][r];
-        if constexpr (EPI == kEpiSwiGLU) {
-          const float u = acc[NB - 1][fm][fn][r];
-          v = v / (1.0f + __expf(-v)) * u;
-        }
-        if constexpr (EPI == kEpiF32) {
-          static_cast<float*>(args.C)[crow * args.ldc + col] = v;
-        } else {
-          static_cast<uint16_t*>(args.C)[crow * args.ldc + col] = f32_to_bf16(v);
+      for (int r = 0; r < 16; ++r) {
+        const int row_b = tile_row<WM>(wm, fm) - band * BAND + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col_l = wn * WTN + fn * 32 + (lane & 31);
+          float v = acc[0][fm][fn][r];
+          if constexpr (EPI == kEpiSwiGLU) {
+            const float u = acc[NB - 1][fm][fn][r];
+            v = v / (1.0f + __expf(-v)) * u;
+          }
+          if constexpr (EPI == kEpiF32) {
+            *reinterpret_cast<float*>(smem + row_b * CS + col_l * 4) = v;
+          } else {
+            *reinterpret_cast<uint16_t*>(smem + row_b * CS + col_l * 2) = f32_to_bf16(v);
+          }
         }
       }
     }
+    __syncthreads();
+    const int band_rows = min(BAND, nrows - band * BAND);
+    for (int idx = tid; idx < band_rows * CPR; idx += 256) {
+      const int row_b = idx / CPR, ch = idx - row_b * CPR;
+      const int col = n0 + ch * EPC;
+      if (col >= args.N) continue;
+      const int64_t p = p0 + band * BAND + row_b;
+      const int64_t crow = args.c_idx ? static_cast<int64_t>(args.c_idx[p]) : p - args.c_sub;
+      const char* src_l = smem + row_b * CS + ch * 16;
+      char* dst = static_cast<char*>(args.C) + (crow * args.ldc + col) * ESZ;
+      if (vec_ok && col + EPC <= args.N) {
+        *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src_l);
+      } else {
+        const int n_el = min(EPC, args.N - col);
+        for (int e = 0; e < n_el; ++e) {
+          if constexpr (ESZ == 4)
+            reinterpret_cast<float*>(dst)[e] = reinterpret_cast<const float*>(src_l)[e];
+          else
+            reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src_l)[e];
+        }
+      }
+    }
+    if (band + 1 < FM / FMP) __syncthreads();  // the next band reuses the LDS
   }
 }
 
