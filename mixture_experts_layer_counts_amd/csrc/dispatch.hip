@@ -46,6 +46,44 @@ hipError_t launch_gather(const uint16_t* x_src, int64_t src_rows, int D, int k, 
   return hipGetLastError();
 }
 
+// The same placement walked from the source side, for one GPU (R = 1) when a
+// single minibatch holds every routed row: one wave per token reads the row
+// once and writes it to the ring slots of the token's k routes (route_dst is
+// the inverse of the schedule table), instead of reading it k times.
+__global__ __launch_bounds__(256) void gather_src_kernel(const uint16_t* __restrict__ x, int T, int D, int k,
+                                                         const int32_t* __restrict__ route_dst, int64_t P,
+                                                         int64_t ring_rows, uint16_t* __restrict__ ring, int* err) {
+  const int t = static_cast<int>(blockIdx.x) * 4 + static_cast<int>(threadIdx.x) / kWave;
+  if (t >= T) return;
+  int64_t slot[16];
+  bool ok = true;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    if (s < k) {
+      const int32_t p = route_dst[static_cast<int64_t>(t) * k + s];
+      ok = ok && p >= 0 && p < P;
+      slot[s] = (p >= 0 && p < P) ? p % ring_rows : -1;
+    }
+  }
+  if (!ok && lane_id() == 0) raise_error(err, kErrExpertRange);  // a table not built by the schedule kernels
+  const uint4* __restrict__ src = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * D);
+  const int n = D / 8;
+  for (int c = lane_id(); c < n; c += kWave) {
+    const uint4 v = src[c];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s < k && slot[s] >= 0) reinterpret_cast<uint4*>(ring + slot[s] * D)[c] = v;
+  }
+}
+
+hipError_t launch_gather_src(const uint16_t* x, int T, int D, int k, const int32_t* route_dst, int64_t P,
+                             int64_t ring_rows, uint16_t* ring, int* err, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  gather_src_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, stream>>>(x, T, D, k, route_dst, P, ring_rows,
+                                                                           ring, err);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ Y, const float* __restrict__ sh,
                                                       const float* __restrict__ gate,
                                                       const int32_t* __restrict__ route_dst, int64_t route_base,

@@ -13,18 +13,21 @@
 // supplies row l % 32; its 32 bytes are K[16h, 16h+16) and K[32+16h, 32+16h+16)
 // of the 64-wide step, and its scale byte is that row's scale of K block h.
 //
-// The pipeline is the bf16 kernel's: 256 x BN tiles, 4 waves, an LDS ring of
-// two K stages fed by direct buffer->LDS loads, the same XOR swizzle of the
-// 128-byte stage rows, the same expert-major XCD-aware work order over the
-// balanced tile list.  A stage holds 128 K elements (one 128-byte line per
-// row, two MFMA steps) plus a 4-byte scale word per row, itself loaded by
-// 4-byte direct loads.  The K loop always runs from k = 0 in the same order,
-// so a row's result does not depend on the tile or minibatch it falls in.
+// The pipeline is the bf16 kernel's: 256 x BN tiles, 4 waves, K stages of
+// 128 bytes per row (two MFMA steps) in two LDS rings fed by direct
+// buffer->LDS loads (activation rows one stage ahead, weight rows two), the
+// same XOR swizzle, the same expert-major XCD-aware work order over the
+// balanced tile list, 32-row blocks dealt to the wave row groups in turn.
+// Each lane loads the scale words of its own fragment rows (4 bytes = the 4
+// K blocks of a stage) straight into registers, one stage ahead.  The K loop
+// always runs from k = 0 in the same order, so a row's result does not
+// depend on the tile or minibatch it falls in.
 //
-// Epilogues: SwiGLU with MX quantisation of h along I (a row's 32-column
-// block lives in the 32 lanes of one half-wave, which reduce its largest
-// magnitude by shuffles), and a plain bf16 store for the down projection,
-// scattered to the row of the route it came from.
+// Epilogues, staged through LDS so that rows leave in 16-byte stores: SwiGLU
+// with MX quantisation of h along I (a row's 32-column block lives in the 32
+// lanes of one half-wave, which reduce its largest magnitude by shuffles),
+// and bf16 for the down projection, scattered to the row of the route it
+// came from.
 
 #include "common.h"
 #include "gemm_common.h"
@@ -35,21 +38,14 @@ namespace moe {
 
 namespace {
 
-constexpr int kMxBM = 256;     // tile rows (must match the tile lists, built with gemm_routed_bm())
+constexpr int kMxBM = 256;      // tile rows (must match the tile lists, built with gemm_routed_bm())
 constexpr int kMxStageK = 128;  // K elements (bytes) per stage row
-constexpr int kMxStages = 2;
 constexpr int kRB = kMxStageK;  // bytes of one stage row
-constexpr int kSB = 4;          // scale bytes of one stage row (128 / 32)
+constexpr int kNSA = 2, kNSB = 3;  // ring slots: activation rows, weight rows
 
 struct MxSrc {
   __amdgpu_buffer_rsrc_t a, b0, b1, as, bs0, bs1;
 };
-
-// One direct 4-byte-per-lane load into LDS: lane l's word lands at lds + 4 l.
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voffset, int soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 4, voffset, soffset, 0,
-                                           0);
-}
 
 __device__ __forceinline__ f32x16_t mfma_mx(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
@@ -59,90 +55,95 @@ __device__ __forceinline__ i32x8_t cat8(u32x4_t lo, u32x4_t hi) {
   return reinterpret_cast<i32x8_t>(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// The K loop of one workgroup (see the bf16 kernel for the ring protocol).
-// Per stage and wave: AI + BI 1 KB data loads and two 256-byte scale loads
-// (A rows 64 w .. 64 w + 63, B rows likewise).
+// Row of the tile held by 32-row MFMA block fm of a wave in row group wm.
+__device__ __forceinline__ int mx_tile_row(int wm, int fm) { return (fm * 2 + wm) * 32; }
+
+// Per-lane scale sources: the byte offset of the scale row of each fragment
+// row this lane supplies (A: block fm; B: half h, block fn).
+template <int FM, int NB, int FN>
+struct MxScaleOff {
+  uint32_t a[FM];
+  uint32_t b[NB][FN];
+};
+
+template <int FML, int NB, int FN>
+struct MxScales {  // one stage's scale words (4 K blocks) of this lane's fragment rows
+  uint32_t a[FML > 0 ? FML : 1];
+  uint32_t b[NB][FN];
+};
+
+// The K loop of one workgroup (the bf16 kernel's ring protocol).  Per stage
+// and wave: AI + BI 1 KB direct loads and FML + NB*FN 4-byte scale loads.
 template <int BN, int NB, int FML, int FM, int FN, int AI, int BI>
 __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const uint32_t (&a_off)[AI],
-                                          const uint32_t (&b_off)[BI], uint32_t as_off, uint32_t bs_off, int nk,
+                                          const uint32_t (&b_off)[BI], const MxScaleOff<FM, NB, FN>& so, int nk,
                                           int a_rows, int tid, int wm, int wn, f32x16_t (&acc)[NB][FM][FN]) {
   constexpr int BM = kMxBM, BROWS = NB * BN;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
-  constexpr int DATA = (BM + BROWS) * kRB;
-  constexpr int STAGE = DATA + (BM + BROWS) * kSB;
+  constexpr int WTN = BN / 2;
+  constexpr int ASLOT = BM * kRB, BSLOT = BROWS * kRB;
   constexpr int ROWS_PER_LD = 1024 / kRB;
   static_assert(AI * ROWS_PER_LD * 4 == BM && BI * ROWS_PER_LD * 4 == BROWS, "data loads per wave per stage");
-  static_assert(BM == 4 * 64 && BROWS == 4 * 64, "one scale load per wave per operand");
-  constexpr int NLD = AI + BI + 2;
-  constexpr int VM_AHEAD = (kMxStages - 2) * NLD;
+  static_assert(BI < 16, "vmcnt range");
+  char* const sa0 = smem;
+  char* const sb0 = smem + kNSA * ASLOT;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
   const int frag_row = lane & 31, frag_h = lane >> 5;
 
-  auto issue = [&](int kt) __attribute__((always_inline)) {
-    const int buf = kt % kMxStages;
+  // past the last stage the loads repeat it (into a free slot), so that every
+  // step issues the same number of loads
+  auto issue_a = [&](int kt, MxScales<FML, NB, FN>& sc) __attribute__((always_inline)) {
     const int kc = kt < nk ? kt : nk - 1;
-    char* sa = smem + buf * STAGE;
-    char* sb = sa + BM * kRB;
-    char* ssa = sa + DATA;
-    char* ssb = ssa + BM * kSB;
+    char* sa = sa0 + (kt % kNSA) * ASLOT;
 #pragma unroll
     for (int j = 0; j < AI; ++j)
       dma16(src.a, sa + (wave * AI + j) * 1024, (wave * AI + j) * ROWS_PER_LD < a_rows ? a_off[j] : a_off[0],
             kc * kRB);
+    // the scale words of stage kt (A and B) ride with the A loads
+#pragma unroll
+    for (int fm = 0; fm < FML; ++fm) sc.a[fm] = __builtin_amdgcn_raw_buffer_load_b32(src.as, so.a[fm], kc * 4, 0);
+#pragma unroll
+    for (int h = 0; h < NB; ++h)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        sc.b[h][fn] = __builtin_amdgcn_raw_buffer_load_b32(h ? src.bs1 : src.bs0, so.b[h][fn], kc * 4, 0);
+  };
+  auto issue_b = [&](int kt) __attribute__((always_inline)) {
+    const int kc = kt < nk ? kt : nk - 1;
+    char* sb = sb0 + (kt % kNSB) * BSLOT;
 #pragma unroll
     for (int j = 0; j < BI; ++j) {
       const int g = wave * BI + j;
       dma16((NB == 2 && g * ROWS_PER_LD >= BN) ? src.b1 : src.b0, sb + g * 1024, b_off[j], kc * kRB);
     }
-    dma4(src.as, ssa + wave * 256, as_off, kc * kSB);
-    dma4((NB == 2 && wave >= 2) ? src.bs1 : src.bs0, ssb + wave * 256, bs_off, kc * kSB);
   };
 
   struct Frags {
     i32x8_t a[FML > 0 ? FML : 1];
     i32x8_t b[NB][FN];
   };
-  struct Scales {  // the stage's scale words of this lane's fragment rows (both steps)
-    uint32_t a[FML > 0 ? FML : 1];
-    uint32_t b[NB][FN];
-  };
   auto read_frags = [&](int kt, int step, Frags& f) __attribute__((always_inline)) {
-    const char* sa = smem + (kt % kMxStages) * STAGE;
-    const char* sb = sa + BM * kRB;
+    const char* sa = sa0 + (kt % kNSA) * ASLOT;
+    const char* sb = sb0 + (kt % kNSB) * BSLOT;
     const int c0 = step * 4 + frag_h, c1 = c0 + 2;
 #pragma unroll
     for (int fm = 0; fm < FML; ++fm) {
-      const int row = wm * WTM + fm * 32 + frag_row;
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz<kRB>(row, c0));
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sa + swz<kRB>(row, c1));
-      f.a[fm] = cat8(lo, hi);
+      const int row = mx_tile_row(wm, fm) + frag_row;
+      f.a[fm] = cat8(*reinterpret_cast<const u32x4_t*>(sa + swz<kRB>(row, c0)),
+                     *reinterpret_cast<const u32x4_t*>(sa + swz<kRB>(row, c1)));
     }
 #pragma unroll
     for (int h = 0; h < NB; ++h)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int row = h * BN + wn * WTN + fn * 32 + frag_row;
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sb + swz<kRB>(row, c0));
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sb + swz<kRB>(row, c1));
-        f.b[h][fn] = cat8(lo, hi);
+        f.b[h][fn] = cat8(*reinterpret_cast<const u32x4_t*>(sb + swz<kRB>(row, c0)),
+                          *reinterpret_cast<const u32x4_t*>(sb + swz<kRB>(row, c1)));
       }
-  };
-  auto read_scales = [&](int kt, Scales& sc) __attribute__((always_inline)) {
-    const char* ssa = smem + (kt % kMxStages) * STAGE + DATA;
-    const char* ssb = ssa + BM * kSB;
-#pragma unroll
-    for (int fm = 0; fm < FML; ++fm)
-      sc.a[fm] = *reinterpret_cast<const uint32_t*>(ssa + (wm * WTM + fm * 32 + frag_row) * kSB);
-#pragma unroll
-    for (int h = 0; h < NB; ++h)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        sc.b[h][fn] = *reinterpret_cast<const uint32_t*>(ssb + (h * BN + wn * WTN + fn * 32 + frag_row) * kSB);
   };
   // v_perm selector that replicates byte (2 step + h) of a scale word into all
   // four bytes: the K block of this lane's half of the step
   const uint32_t rep0 = (0 + frag_h) * 0x01010101u, rep1 = (2 + frag_h) * 0x01010101u;
-  auto mfmas = [&](const Frags& f, const Scales& sc, int step) __attribute__((always_inline)) {
+  auto mfmas = [&](const Frags& f, const MxScales<FML, NB, FN>& sc, int step) __attribute__((always_inline)) {
     const uint32_t rep = step ? rep1 : rep0;
 #pragma unroll
     for (int fm = 0; fm < FML; ++fm) {
@@ -158,47 +159,53 @@ __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const ui
   };
   constexpr int NMF = FML * NB * FN;
   constexpr int NRD = 2 * (FML + NB * FN);  // two 16-byte halves per fragment
-  auto interleave = [&]() __attribute__((always_inline)) {
+  constexpr int NSC = FML + NB * FN;        // scale loads per stage
+  // fragment reads spread under the MFMAs; in step 0 also the A and scale
+  // loads, one per MFMA
+  auto interleave = [&](int step, bool loads) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NMF; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (2 * NMF <= NRD || (i & 1) == 0)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (loads && step == 0 && i < AI + NSC) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   };
 
-#pragma unroll
-  for (int s = 0; s < kMxStages - 1; ++s) issue(s);
-  asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_AHEAD, 15)) : "memory");
+  MxScales<FML, NB, FN> sc_cur, sc_next;
+  issue_a(0, sc_cur);
+  issue_b(0);
+  issue_b(1);
+  asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI, 15)) : "memory");  // A(0), scales(0), B(0) landed
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   Frags f[2];
-  Scales sc;
-  if constexpr (FML > 0) {
-    read_frags(0, 0, f[0]);
-    read_scales(0, sc);
-  }
+  if constexpr (FML > 0) read_frags(0, 0, f[0]);
   for (int kt = 0; kt < nk; ++kt) {
-    issue(kt + kMxStages - 1);
+    issue_a(kt + 1, sc_next);
     if constexpr (FML > 0) {
       read_frags(kt, 1, f[1]);
-      mfmas(f[0], sc, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, NLD, 0);
-      interleave();
+      mfmas(f[0], sc_cur, 0);
+      interleave(0, true);
     }
-    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_AHEAD, 0)) : "memory");
+    issue_b(kt + 2);
+    // A(kt+1), its scales and B(kt+1) have landed (B(kt+2) may still be in
+    // flight) and this wave's reads of stage kt are done
+    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI, 0)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if constexpr (FML > 0) {
-      // stage kt+1's first fragments (on the last step: a duplicate of the
-      // last stage, loaded by the clamped issue above, and never used)
-      const Scales cur = sc;
+      // stage kt+1's first fragments (past the last stage: the repeated
+      // stage, never used)
       read_frags(kt + 1, 0, f[0]);
-      read_scales(kt + 1, sc);
-      mfmas(f[1], cur, 1);
-      interleave();
+      mfmas(f[1], sc_cur, 1);
+      interleave(1, false);
     }
+    sc_cur = sc_next;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still target LDS when the workgroup ends
 }
 
 template <int BN, int EPI>
@@ -206,13 +213,13 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxGemmArgs args) {
   constexpr int BM = kMxBM;
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
   constexpr int BROWS = NB * BN;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int WTN = BN / 2;
+  constexpr int FM = BM / 2 / 32, FN = WTN / 32;
   constexpr int ROWS_PER_LD = 1024 / kRB;
   constexpr int AI = BM / (4 * ROWS_PER_LD), BI = BROWS / (4 * ROWS_PER_LD);
-  constexpr int STAGE = (BM + BROWS) * (kRB + kSB);
+  constexpr int LDS_BYTES = kNSA * BM * kRB + kNSB * BROWS * kRB;
 
-  __shared__ __attribute__((aligned(1024))) char smem[kMxStages * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / 2, wn = wave % 2;
@@ -235,6 +242,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxGemmArgs args) {
   const int n0 = nb * BN;
   const int K = args.K, KS = K / 32;
 
+  // ---- byte offsets of the 16-byte chunks this lane fetches ----
   constexpr int CH = kRB / 16;
   uint32_t a_off[AI];
 #pragma unroll
@@ -255,19 +263,23 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxGemmArgs args) {
     n = n < args.N ? n : args.N - 1;
     b_off[j] = static_cast<uint32_t>(static_cast<int64_t>(n) * K + c * 16);
   }
-  // scale words: wave w loads the words of A rows 64 w + lane and of B stage
-  // rows 64 w + lane (the gate half for waves 0-1 and the up half for 2-3
-  // when NB == 2)
-  uint32_t as_off, bs_off;
-  {
-    const int row = wave * 64 + lane;
+  // ---- scale rows of this lane's fragment rows (rows past the tile or N are
+  // clamped; their products only reach dropped outputs) ----
+  MxScaleOff<FM, NB, FN> so;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int row = mx_tile_row(wm, fm) + (lane & 31);
     const int64_t p = p0 + (row < nrows ? row : nrows - 1);
-    as_off = static_cast<uint32_t>(((p - args.a_sub) % args.a_mod) * KS);
-    const int half = row / BN;
-    int n = n0 + (row - half * BN);
-    n = n < args.N ? n : args.N - 1;
-    bs_off = static_cast<uint32_t>(static_cast<int64_t>(n) * KS);
+    so.a[fm] = static_cast<uint32_t>(((p - args.a_sub) % args.a_mod) * KS);
   }
+#pragma unroll
+  for (int h = 0; h < NB; ++h)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      int n = n0 + wn * WTN + fn * 32 + (lane & 31);
+      n = n < args.N ? n : args.N - 1;
+      so.b[h][fn] = static_cast<uint32_t>(static_cast<int64_t>(n) * KS);
+    }
   constexpr int kRsrcWord3 = 0x00020000;
   MxSrc src;
   src.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(args.A), 0, static_cast<int>(args.a_rows * K),
@@ -296,14 +308,15 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxGemmArgs args) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[h][fm][fn] = f32x16_t{};
 
-  int fm_live = (nrows - wm * WTM + 31) / 32;
+  // 32-row MFMA blocks of this wave that hold tile rows (wave-uniform)
+  int fm_live = ((nrows + 31) / 32 - wm + 1) / 2;
   fm_live = fm_live < 0 ? 0 : (fm_live > FM ? FM : fm_live);
   const int nk = K / kMxStageK;
   switch (fm_live) {
 #define MOE_CASE(n)                                                                                         \
   case n:                                                                                                   \
     if constexpr (n <= FM)                                                                                  \
-      k_loop_mx<BN, NB, n, FM, FN, AI, BI>(smem, src, a_off, b_off, as_off, bs_off, nk, nrows, tid, wm, wn, acc); \
+      k_loop_mx<BN, NB, n, FM, FN, AI, BI>(smem, src, a_off, b_off, so, nk, nrows, tid, wm, wn, acc);       \
     break;
     MOE_CASE(0)
     MOE_CASE(1)
@@ -315,18 +328,23 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxGemmArgs args) {
       break;
   }
 
-  // ---- epilogue: lane holds column (lane % 32) and rows 8*(r/4) + 4*(lane/32) + r%4 ----
+  // ---- epilogue, staged through LDS so that rows leave in 16-byte pieces ----
+  constexpr int ESZ = (EPI == kEpiSwiGLU) ? 1 : 2;  // E4M3 h, or bf16 rows
+  constexpr int CS = BN * ESZ + 16;                 // LDS row stride of the staged tile
+  static_assert(BM * CS <= LDS_BYTES, "staged tile fits");
+  constexpr int CPR = BN * ESZ / 16;
+  constexpr int EPC = 16 / ESZ;
+  __syncthreads();  // every wave is done with the K loop's LDS
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     if (fm >= fm_live) continue;  // wave-uniform
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
-      const int col = n0 + wn * WTN + fn * 32 + (lane & 31);
+      const int col_l = wn * WTN + fn * 32 + (lane & 31);
       const bool col_ok = n0 + wn * WTN + fn * 32 < args.N;  // N % 32 == 0: a 32-column block is all in or out
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row_t = wm * WTM + fm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int64_t p = p0 + row_t;
+        const int row_t = mx_tile_row(wm, fm) + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         if constexpr (EPI == kEpiSwiGLU) {
           const float gv = acc[0][fm][fn][r], uv = acc[1][fm][fn][r];
           const float v = gv / (1.0f + __expf(-gv)) * uv;
@@ -335,19 +353,24 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxGemmArgs args) {
 #pragma unroll
           for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
           const int X = mx_scale_exponent(amax);
-          if (row_t < nrows && col_ok) {
-            const int64_t crow = p - args.c_sub;
-            static_cast<uint8_t*>(args.C)[crow * args.ldc + col] = e4m3_from_f32(ldexpf(v, -X));
-            if ((lane & 31) == 0) args.Cs[crow * (args.ldc / 32) + col / 32] = static_cast<uint8_t>(X + 127);
-          }
+          *reinterpret_cast<uint8_t*>(smem + row_t * CS + col_l) = e4m3_from_f32(ldexpf(v, -X));
+          if (row_t < nrows && col_ok && (lane & 31) == 0)
+            args.Cs[(p0 + row_t - args.c_sub) * (args.ldc / 32) + (n0 + col_l) / 32] = static_cast<uint8_t>(X + 127);
         } else {
-          if (row_t < nrows && col_ok) {
-            const int64_t crow = args.c_idx ? static_cast<int64_t>(args.c_idx[p]) : p - args.c_sub;
-            static_cast<uint16_t*>(args.C)[crow * args.ldc + col] = f32_to_bf16(acc[0][fm][fn][r]);
-          }
+          *reinterpret_cast<uint16_t*>(smem + row_t * CS + col_l * 2) = f32_to_bf16(acc[0][fm][fn][r]);
         }
       }
     }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nrows * CPR; idx += 256) {
+    const int row = idx / CPR, ch = idx - row * CPR;
+    const int col = n0 + ch * EPC;
+    if (col >= args.N) continue;  // N % 32 == 0: a chunk is all in or out
+    const int64_t p = p0 + row;
+    const int64_t crow = args.c_idx ? static_cast<int64_t>(args.c_idx[p]) : p - args.c_sub;
+    *reinterpret_cast<u32x4_t*>(static_cast<char*>(args.C) + (crow * args.ldc + col) * ESZ) =
+        *reinterpret_cast<const u32x4_t*>(smem + row * CS + ch * 16);
   }
 }
 
@@ -371,11 +394,14 @@ hipError_t launch_gemm_mx(const MxGemmArgs& a, int epilogue, hipStream_t stream)
   // buffer resources address at most 2^31 bytes per operand here
   if (a.a_rows * a.K >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   if (static_cast<int64_t>(a.N) * a.K >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  // 16-byte output stores: the base and the row strides keep 16-byte alignment
+  if (reinterpret_cast<uintptr_t>(a.C) % 16 != 0) return hipErrorInvalidValue;
   switch (epilogue) {
     case kEpiSwiGLU:
       if (!a.Cs || a.ldc % 32 != 0) return hipErrorInvalidValue;
       return run_mx<128, kEpiSwiGLU>(a, stream);
     case kEpiBF16:
+      if (a.ldc % 8 != 0) return hipErrorInvalidValue;
       return run_mx<256, kEpiBF16>(a, stream);
     default:
       return hipErrorInvalidValue;

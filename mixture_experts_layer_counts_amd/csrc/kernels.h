@@ -102,6 +102,13 @@ hipError_t launch_gather_mx(const uint16_t* x_src, int64_t src_rows, int D, int 
                             const int32_t* offsets, int L, int64_t p_begin, int64_t rows, int64_t ring_rows,
                             uint8_t* ring_q, uint8_t* ring_s, int* err, hipStream_t stream);
 
+// Source-side gathers for R = 1 when one minibatch holds every routed row:
+// each token row is read once and written to its k ring slots.
+hipError_t launch_gather_src(const uint16_t* x, int T, int D, int k, const int32_t* route_dst, int64_t P,
+                             int64_t ring_rows, uint16_t* ring, int* err, hipStream_t stream);
+hipError_t launch_gather_src_mx(const uint16_t* x, int T, int D, int k, const int32_t* route_dst, int64_t P,
+                                int64_t ring_rows, uint8_t* ring_q, uint8_t* ring_s, int* err, hipStream_t stream);
+
 hipError_t launch_clear_int(int* p, int n, hipStream_t stream);
 
 // MXFP8: rows x K bf16 -> E4M3 codes + one E8M0 scale per 32 elements along K.

@@ -135,8 +135,8 @@ moe_status check_ws(const moe_shape* s, const void* ws, size_t ws_bytes, Layout*
 // Support"): the gather quantises x along D into the ring, the up/gate GEMM
 // quantises h along I in its epilogue, the down GEMM writes bf16 rows.
 hipError_t routed_minibatch_mx(const moe_shape* shape, const moe_weights* w, const void* x_src,
-                               const int32_t* sched_src, const int32_t* expert_offsets, const Layout& L, void* ws,
-                               int64_t m, int64_t p_begin, int64_t rows, hipStream_t s) {
+                               const int32_t* sched_src, const int32_t* expert_offsets, const int32_t* route_dst,
+                               const Layout& L, void* ws, int64_t m, int64_t p_begin, int64_t rows, hipStream_t s) {
   const int D = static_cast<int>(shape->D), I = static_cast<int>(shape->I), k = static_cast<int>(shape->k);
   const int Lx = static_cast<int>(shape->experts_per_rank);
   const int64_t b = shape->minibatch_rows, C = shape->ring_rows, R = shape->num_src_ranks;
@@ -148,9 +148,12 @@ hipError_t routed_minibatch_mx(const moe_shape* shape, const moe_weights* w, con
   const int32_t* tile_count = at<int32_t>(ws, L.tile_count) + m;
   {
     ProbeScope probe(MOE_K_GATHER, s);
-    const hipError_t e = moe::launch_gather_mx(static_cast<const uint16_t*>(x_src), R * shape->T, D, k, sched_src,
-                                               expert_offsets, Lx, p_begin, rows, C, ring_q, ring_s,
-                                               at<int>(ws, L.err), s);
+    const hipError_t e =
+        (R == 1 && L.n_minibatches == 1)
+            ? moe::launch_gather_src_mx(static_cast<const uint16_t*>(x_src), static_cast<int>(shape->T), D, k,
+                                        route_dst, shape->max_rows, C, ring_q, ring_s, at<int>(ws, L.err), s)
+            : moe::launch_gather_mx(static_cast<const uint16_t*>(x_src), R * shape->T, D, k, sched_src,
+                                    expert_offsets, Lx, p_begin, rows, C, ring_q, ring_s, at<int>(ws, L.err), s);
     if (e != hipSuccess) return e;
   }
   moe::MxGemmArgs u{};
@@ -369,13 +372,18 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     const int64_t p_begin = m * b;
     const int64_t rows = std::min<int64_t>(b, shape->max_rows - p_begin);
     if (mx) {
-      MOE_TRY_HIP(routed_minibatch_mx(shape, w, x_src, sched_src, expert_offsets, L, ws, m, p_begin, rows, s));
+      MOE_TRY_HIP(
+          routed_minibatch_mx(shape, w, x_src, sched_src, expert_offsets, route_dst, L, ws, m, p_begin, rows, s));
       continue;
     }
     {
       ProbeScope probe(MOE_K_GATHER, s);
-      MOE_TRY_HIP(moe::launch_gather(static_cast<const uint16_t*>(x_src), R * shape->T, D, k, sched_src,
-                                     expert_offsets, Lx, p_begin, rows, C, ring, at<int>(ws, L.err), s));
+      if (R == 1 && L.n_minibatches == 1)  // one minibatch holds every row: read each token once
+        MOE_TRY_HIP(moe::launch_gather_src(static_cast<const uint16_t*>(x_src), T, D, k, route_dst, shape->max_rows,
+                                           C, ring, at<int>(ws, L.err), s));
+      else
+        MOE_TRY_HIP(moe::launch_gather(static_cast<const uint16_t*>(x_src), R * shape->T, D, k, sched_src,
+                                       expert_offsets, Lx, p_begin, rows, C, ring, at<int>(ws, L.err), s));
     }
     moe::GemmArgs u{};
     u.A = ring;

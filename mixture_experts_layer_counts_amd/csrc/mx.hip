@@ -18,10 +18,10 @@
 
 namespace moe {
 
-// One block of 32 bf16 values (64 bytes at `src`) -> 32 E4M3 bytes at `q` and
-// the E8M0 scale byte at `scale`.
-__device__ __forceinline__ void quantize_block32(const uint16_t* __restrict__ src, uint8_t* __restrict__ q,
-                                                 uint8_t* __restrict__ scale) {
+// One block of 32 bf16 values (64 bytes at `src`) -> 32 E4M3 bytes (in two
+// 16-byte words) and the E8M0 scale byte (returned).
+__device__ __forceinline__ uint8_t quantize_block32_words(const uint16_t* __restrict__ src, u32x4_t& lo,
+                                                          u32x4_t& hi) {
   const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src);
   float v[32];
 #pragma unroll
@@ -37,18 +37,26 @@ __device__ __forceinline__ void quantize_block32(const uint16_t* __restrict__ sr
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const int X = mx_scale_exponent(amax);
-  *scale = static_cast<uint8_t>(X + 127);
-  u32x4_t out[2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     uint32_t word = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) word |= static_cast<uint32_t>(e4m3_from_f32(ldexpf(v[4 * i + j], -X))) << (8 * j);
-    out[i >> 2][i & 3] = word;
+    if (i < 4)
+      lo[i] = word;
+    else
+      hi[i - 4] = word;
   }
+  return static_cast<uint8_t>(X + 127);
+}
+
+__device__ __forceinline__ void quantize_block32(const uint16_t* __restrict__ src, uint8_t* __restrict__ q,
+                                                 uint8_t* __restrict__ scale) {
+  u32x4_t lo, hi;
+  *scale = quantize_block32_words(src, lo, hi);
   u32x4_t* d = reinterpret_cast<u32x4_t*>(q);
-  d[0] = out[0];
-  d[1] = out[1];
+  d[0] = lo;
+  d[1] = hi;
 }
 
 __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t blocks,
@@ -101,6 +109,45 @@ hipError_t launch_gather_mx(const uint16_t* x_src, int64_t src_rows, int D, int 
   if ((n + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
   gather_mx_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(
       x_src, src_rows, D, k, sched_src, offsets, L, p_begin, rows, ring_rows, ring_q, ring_s, err);
+  return hipGetLastError();
+}
+
+// MX gather from the source side (R = 1, one minibatch holding every routed
+// row): one thread quantises one 32-element block of a token once and writes
+// it to the ring slots of the token's k routes.
+__global__ __launch_bounds__(256) void gather_src_mx_kernel(const uint16_t* __restrict__ x, int T, int D, int k,
+                                                            const int32_t* __restrict__ route_dst, int64_t P,
+                                                            int64_t ring_rows, uint8_t* __restrict__ ring_q,
+                                                            uint8_t* __restrict__ ring_s, int* err) {
+  const int nb = D / 32;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(T) * nb) return;
+  const int64_t t = i / nb;
+  const int blk = static_cast<int>(i % nb);
+  u32x4_t lo, hi;
+  const uint8_t sc = quantize_block32_words(x + t * D + blk * 32, lo, hi);
+  for (int s = 0; s < k; ++s) {
+    const int32_t p = route_dst[t * k + s];
+    if (p < 0 || p >= P) {  // a table not built by the schedule kernels
+      if (blk == 0) raise_error(err, kErrExpertRange);
+      continue;
+    }
+    const int64_t slot = p % ring_rows;
+    u32x4_t* d = reinterpret_cast<u32x4_t*>(ring_q + slot * D + blk * 32);
+    d[0] = lo;
+    d[1] = hi;
+    ring_s[slot * nb + blk] = sc;
+  }
+}
+
+hipError_t launch_gather_src_mx(const uint16_t* x, int T, int D, int k, const int32_t* route_dst, int64_t P,
+                                int64_t ring_rows, uint8_t* ring_q, uint8_t* ring_s, int* err, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  if (D % 32 != 0) return hipErrorInvalidValue;
+  const int64_t n = static_cast<int64_t>(T) * (D / 32);
+  if ((n + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
+  gather_src_mx_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(x, T, D, k, route_dst, P,
+                                                                                   ring_rows, ring_q, ring_s, err);
   return hipGetLastError();
 }
 
