@@ -198,13 +198,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
   // ---- which (tile, N block) this workgroup computes ----
   const int n_blocks = (args.N + BN - 1) / BN;
   const int tcount = ROUTED ? *args.tile_count : (args.dense_rows + BM - 1) / BM;
-  const int W = tcount * n_blocks;
+  const int S = ROUTED ? 1 : args.k_splits;  // K ranges (dense only), each with its own output plane
+  const int W = tcount * n_blocks * S;
   const int chunk = (W + kXcds - 1) / kXcds;
   const int local = static_cast<int>(blockIdx.x) / kXcds;
   if (local >= chunk) return;
   const int w = (static_cast<int>(blockIdx.x) % kXcds) * chunk + local;
   if (w >= W) return;
-  int e = 0, nrows, tile, nb;
+  int e = 0, nrows, tile, nb, ks = 0;
   int64_t p0;
   if constexpr (ROUTED) {
     const int4 g = args.tiles[w / n_blocks];  // a tile of the expert group that owns item w
@@ -218,14 +219,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
     nrows = t.z;
   } else {
     // dense: row tile outer, so the workgroups of one XCD share activation
-    // rows in L2 and stream the (small) weight matrix
-    nb = w % n_blocks;
-    tile = w / n_blocks;
+    // rows in L2 and stream the (small) weight matrix; the K ranges of one
+    // output tile are neighbours
+    ks = w % S;
+    nb = (w / S) % n_blocks;
+    tile = w / S / n_blocks;
     p0 = static_cast<int64_t>(tile) * BM;
     nrows = args.dense_rows - static_cast<int>(p0) < BM ? args.dense_rows - static_cast<int>(p0) : BM;
   }
   const int n0 = nb * BN;
   const int K = args.K;
+  const int k0 = ks * (K / S);  // first K element of this workgroup's range
+  char* const cbase = static_cast<char*>(args.C) + ks * args.c_split_stride * (EPI == kEpiF32 ? 4 : 2);
 
   // ---- byte offsets of the 16-byte chunks this lane fetches ----
   // Direct load j of wave w fills rows ROWS_PER_LD (w * AI + j) + lane / CH of
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
     const int c = (lane % CH) ^ ((row / (256 / RB)) & (CH - 1));
     const int64_t p = p0 + (row < nrows ? row : nrows - 1);
     const int64_t arow = (p - args.a_sub) % args.a_mod;
-    a_off[j] = static_cast<uint32_t>((arow * args.lda + c * 8) * 2);
+    a_off[j] = static_cast<uint32_t>((arow * args.lda + k0 + c * 8) * 2);
   }
   uint32_t b_off[BI];
 #pragma unroll
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
     const int half = row / BN;
     int n = n0 + (row - half * BN);
     n = n < args.N ? n : args.N - 1;
-    b_off[j] = static_cast<uint32_t>((static_cast<int64_t>(n) * K + c * 8) * 2);
+    b_off[j] = static_cast<uint32_t>((static_cast<int64_t>(n) * K + k0 + c * 8) * 2);
   }
   constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
   TileSrc src;
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
   // K loop is instantiated per count so that its body is one straight block
   int fm_live = ((nrows + 31) / 32 - wm + WM - 1) / WM;
   fm_live = fm_live < 0 ? 0 : (fm_live > FM ? FM : fm_live);
-  const int nk = K / BK;
+  const int nk = K / S / BK;
   switch (fm_live) {
 #define MOE_CASE(n)                                                                       \
   case n:                                                                                 \
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
   constexpr int BAND = FMP * WM * 32;         // tile rows per band
   constexpr int CPR = BN * ESZ / 16;          // 16-byte chunks per staged row
   constexpr int EPC = 16 / ESZ;               // elements per chunk
-  const bool vec_ok = ((args.ldc * ESZ) % 16 == 0) && (reinterpret_cast<uintptr_t>(args.C) % 16 == 0);
+  const bool vec_ok = ((args.ldc * ESZ) % 16 == 0) && (reinterpret_cast<uintptr_t>(cbase) % 16 == 0);
   __syncthreads();  // every wave is done with the K loop's LDS
 #pragma unroll
   for (int band = 0; band < FM / FMP; ++band) {
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
       const int64_t p = p0 + band * BAND + row_b;
       const int64_t crow = args.c_idx ? static_cast<int64_t>(args.c_idx[p]) : p - args.c_sub;
       const char* src_l = smem + row_b * CS + ch * 16;
-      char* dst = static_cast<char*>(args.C) + (crow * args.ldc + col) * ESZ;
+      char* dst = cbase + (crow * args.ldc + col) * ESZ;
       if (vec_ok && col + EPC <= args.N) {
         *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src_l);
       } else {
@@ -367,7 +372,7 @@ template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK = kStageK
 hipError_t run(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles = ROUTED ? a.max_tiles : (a.dense_rows + BM - 1) / BM;
   const int64_t n_blocks = (a.N + BN - 1) / BN;
-  const int64_t work = tiles * n_blocks;
+  const int64_t work = tiles * n_blocks * (ROUTED ? 1 : a.k_splits);
   const int64_t grid = (work + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
@@ -388,11 +393,12 @@ int gemm_tiles_bound(int64_t rows, int groups, int bm) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t stream) {
-  if (a.K % kStageK != 0 || a.N <= 0) return hipErrorInvalidValue;
+  const bool routed = a.tiles != nullptr;
+  if (a.N <= 0 || a.k_splits < 1 || (routed && a.k_splits != 1)) return hipErrorInvalidValue;
+  if (a.K % (kStageK * a.k_splits) != 0) return hipErrorInvalidValue;
   // buffer resources address at most 2^31 bytes per operand here
   if (a.a_bytes <= 0 || a.a_bytes >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   if (static_cast<int64_t>(a.N) * a.K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  const bool routed = a.tiles != nullptr;
   switch (epilogue) {
     case kEpiSwiGLU:
       return routed ? run<kRoutedBM, 128, 2, 2, kEpiSwiGLU, true>(a, stream)
@@ -402,7 +408,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t stream) {
                     : run<256, 256, 2, 2, kEpiBF16, false>(a, stream);
     case kEpiF32:
       return routed ? run<kRoutedBM, 256, 2, 2, kEpiF32, true>(a, stream)
-                    : (a.N <= 256 ? run<128, 128, 2, 2, kEpiF32, false>(a, stream)
+                    : ((a.N <= 256 || a.k_splits > 1) ? run<128, 128, 2, 2, kEpiF32, false>(a, stream)
                                   : run<256, 256, 2, 2, kEpiF32, false>(a, stream));
     default:
       return hipErrorInvalidValue;

@@ -15,8 +15,11 @@ struct SchedScratch {
 
 int sched_chunks(int NK);
 
-hipError_t launch_topk_gate(const float* logits, int T, int E, int k, int32_t* idx, float* gate, int* err,
-                            hipStream_t stream);
+// Top-k and gates from `parts` fp32 planes [T, E] (stride part_stride
+// elements), summed in plane order; with parts > 1 the sums are written to
+// `logits`.
+hipError_t launch_topk_gate(const float* planes, int parts, int64_t part_stride, float* logits, int T, int E, int k,
+                            int32_t* idx, float* gate, int* err, hipStream_t stream);
 
 hipError_t launch_schedule(const int32_t* routes, int R, int NK, int c, int L, int E_total, int64_t max_rows,
                            int32_t* counts, int32_t* offsets, int32_t* sched_src, int32_t* route_dst,
@@ -53,6 +56,8 @@ struct GemmArgs {
   const int32_t* tile_count;  // routed: number of valid tiles
   int dense_rows;
   int max_tiles;
+  int k_splits;            // dense only: K is cut into this many equal ranges, one output plane each
+  int64_t c_split_stride;  // elements between the output planes of the K ranges
 };
 
 // Grouped MXFP8 GEMM (routed only): E4M3 operands with one E8M0 scale per 32

@@ -16,7 +16,9 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t err, ord_local, chunk_cnt, M, tiles, tile_count, ring, ring_s, h, h_s, Y, h_shared, shared_out, total;
+  size_t err, ord_local, chunk_cnt, M, tiles, tile_count, ring, ring_s, h, h_s, Y, h_shared, shared_out, router_parts,
+      total;
+  int router_splits;
   int64_t n_minibatches;
   int max_tiles;
   int64_t y_rows;
@@ -49,8 +51,20 @@ bool valid_shape(const moe_shape* s, moe_status* why) {
   return true;
 }
 
+// K ranges of the router GEMM: with few output tiles (T/128 x E/128 well
+// under the 256 CUs) the K axis is cut into equal ranges whose partial
+// logits the top-k kernel adds in a fixed order.
+int router_splits(const moe_shape* s) {
+  const int64_t tiles = ((s->T + 127) / 128) * ((s->E_total + 127) / 128);
+  const int64_t stages = s->D / 64;
+  int S = 1;
+  while (S < 4 && tiles * S < 512 && stages % (2 * S) == 0) S *= 2;
+  return S;
+}
+
 Layout layout_of(const moe_shape* s) {
   Layout L{};
+  L.router_splits = router_splits(s);
   const int64_t R = s->num_src_ranks, NK = s->T * s->k, Lx = s->experts_per_rank;
   const int bm = moe::gemm_routed_bm();
   L.n_minibatches = s->max_rows > 0 ? (s->max_rows + s->minibatch_rows - 1) / s->minibatch_rows : 0;
@@ -81,6 +95,7 @@ Layout layout_of(const moe_shape* s) {
   L.Y = take(sizeof(uint16_t) * L.y_rows * s->D);
   L.h_shared = take(sizeof(uint16_t) * s->T * s->I_shared);
   L.shared_out = take(sizeof(float) * s->T * s->D);
+  L.router_parts = take(L.router_splits > 1 ? sizeof(float) * L.router_splits * s->T * s->E_total : 0);
   L.total = off;
   return L;
 }
@@ -251,6 +266,7 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router
   if (T == 0) return MOE_OK;
   if (x) {
     moe::GemmArgs g{};
+    g.k_splits = 1;
     g.A = static_cast<const uint16_t*>(x);
     g.a_bytes = shape->T * shape->D * 2;
     g.lda = shape->D;
@@ -261,8 +277,10 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router
     g.b_expert_stride = 0;
     g.N = E;
     g.K = static_cast<int>(shape->D);
-    g.C = logits;
+    g.C = L.router_splits > 1 ? static_cast<void*>(at<float>(ws, L.router_parts)) : static_cast<void*>(logits);
     g.ldc = E;
+    g.k_splits = L.router_splits;
+    g.c_split_stride = static_cast<int64_t>(T) * E;
     g.c_idx = nullptr;
     g.c_sub = 0;
     g.tiles = nullptr;
@@ -272,7 +290,10 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router
     MOE_TRY_HIP(moe::launch_gemm(g, moe::kEpiF32, s));
   }
   ProbeScope probe(MOE_K_TOPK, s);
-  return hip_status(moe::launch_topk_gate(logits, T, E, k, topk_idx, topk_gate, at<int>(ws, L.err), s));
+  const bool parts = x && L.router_splits > 1;
+  return hip_status(moe::launch_topk_gate(parts ? at<float>(ws, L.router_parts) : logits,
+                                          parts ? L.router_splits : 1, static_cast<int64_t>(T) * E, logits, T, E, k,
+                                          topk_idx, topk_gate, at<int>(ws, L.err), s));
 }
 
 moe_status moe_schedule(const moe_shape* shape, const int32_t* routes, int32_t* expert_counts,
@@ -333,6 +354,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
   //    it needs no dispatch, so it goes first)
   if (T > 0) {
     moe::GemmArgs g{};
+    g.k_splits = 1;
     g.A = static_cast<const uint16_t*>(x_local);
     g.a_bytes = static_cast<int64_t>(T) * D * 2;
     g.lda = D;
@@ -351,6 +373,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
       MOE_TRY_HIP(moe::launch_gemm(g, moe::kEpiSwiGLU, s));
     }
     moe::GemmArgs d{};
+    d.k_splits = 1;
     d.A = h_sh;
     d.a_bytes = static_cast<int64_t>(T) * Is * 2;
     d.lda = Is;
@@ -386,6 +409,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
                                        expert_offsets, Lx, p_begin, rows, C, ring, at<int>(ws, L.err), s));
     }
     moe::GemmArgs u{};
+    u.k_splits = 1;
     u.A = ring;
     u.a_bytes = C * D * 2;
     u.lda = D;
@@ -408,6 +432,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
       MOE_TRY_HIP(moe::launch_gemm(u, moe::kEpiSwiGLU, s));
     }
     moe::GemmArgs d{};
+    d.k_splits = 1;
     d.A = h;
     d.a_bytes = b * I * 2;
     d.lda = I;

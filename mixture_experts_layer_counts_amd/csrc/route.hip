@@ -17,14 +17,18 @@
 namespace moe {
 
 // EPL = logits per lane (ceil(E / 64)), so the row lives in registers.
+// The router GEMM may leave the logits as `parts` partial sums over K ranges
+// (planes part_stride apart); they are added here in plane order, a fixed
+// order, and the sums written back to `logits`.
 template <int EPL>
-__global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict__ logits, int T, int E,
-                                                        int k, int32_t* __restrict__ idx,
+__global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict__ planes, int parts,
+                                                        int64_t part_stride, float* __restrict__ logits, int T,
+                                                        int E, int k, int32_t* __restrict__ idx,
                                                         float* __restrict__ gate, int* err) {
   const int token = blockIdx.x * 4 + static_cast<int>(threadIdx.x) / kWave;
   if (token >= T) return;
   const int lane = lane_id();
-  const float* row = logits + static_cast<int64_t>(token) * E;
+  const float* row = planes + static_cast<int64_t>(token) * E;
 
   float v[EPL];
   bool bad = false;
@@ -34,6 +38,8 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
     float x = -INFINITY;
     if (e < E) {
       x = row[e];
+      for (int pp = 1; pp < parts; ++pp) x += row[pp * part_stride + e];
+      if (parts > 1) logits[static_cast<int64_t>(token) * E + e] = x;
       if (!__builtin_isfinite(x)) {
         bad = true;
         if (__builtin_isnan(x)) x = -INFINITY;
@@ -101,23 +107,24 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
   }
 }
 
-hipError_t launch_topk_gate(const float* logits, int T, int E, int k, int32_t* idx, float* gate, int* err,
-                            hipStream_t stream) {
+hipError_t launch_topk_gate(const float* planes, int parts, int64_t part_stride, float* logits, int T, int E, int k,
+                            int32_t* idx, float* gate, int* err, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
+  if (parts < 1) return hipErrorInvalidValue;
   const dim3 grid((T + 3) / 4), block(256);
   const int epl = (E + kWave - 1) / kWave;
   if (epl <= 1)
-    topk_gate_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, k, idx, gate, err);
+    topk_gate_kernel<1><<<grid, block, 0, stream>>>(planes, parts, part_stride, logits, T, E, k, idx, gate, err);
   else if (epl <= 2)
-    topk_gate_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, k, idx, gate, err);
+    topk_gate_kernel<2><<<grid, block, 0, stream>>>(planes, parts, part_stride, logits, T, E, k, idx, gate, err);
   else if (epl <= 4)
-    topk_gate_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, k, idx, gate, err);
+    topk_gate_kernel<4><<<grid, block, 0, stream>>>(planes, parts, part_stride, logits, T, E, k, idx, gate, err);
   else if (epl <= 6)
-    topk_gate_kernel<6><<<grid, block, 0, stream>>>(logits, T, E, k, idx, gate, err);
+    topk_gate_kernel<6><<<grid, block, 0, stream>>>(planes, parts, part_stride, logits, T, E, k, idx, gate, err);
   else if (epl <= 8)
-    topk_gate_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, k, idx, gate, err);
+    topk_gate_kernel<8><<<grid, block, 0, stream>>>(planes, parts, part_stride, logits, T, E, k, idx, gate, err);
   else if (epl <= 16)
-    topk_gate_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, k, idx, gate, err);
+    topk_gate_kernel<16><<<grid, block, 0, stream>>>(planes, parts, part_stride, logits, T, E, k, idx, gate, err);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
