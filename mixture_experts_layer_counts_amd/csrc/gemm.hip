@@ -42,7 +42,23 @@ namespace moe {
 
 namespace {
 
-constexpr int kStageK = 64;  // K elements per pipeline stage (one 128-byte line per row)
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+#ifndef MOE_GEMM_NSB
+#define MOE_GEMM_NSB 3
+#endif
+constexpr int kStageK = MOE_GEMM_BK;  // K elements per pipeline stage
+constexpr int kNSA = 2;               // LDS ring slots: activation rows (one stage ahead)
+constexpr int kNSB = MOE_GEMM_NSB;    // weight rows (kNSB - 1 stages ahead)
+
+// Largest divisor of fm that is at most fit (the 32-row blocks per row group
+// of one epilogue band).
+constexpr int band_blocks(int fm, int fit) {
+  int b = fit < fm ? fit : fm;
+  while (b > 1 && fm % b != 0) --b;
+  return b;
+}
 
 // Row of the tile held by 32-row MFMA block fm of a wave in row group wm:
 // blocks are dealt to the WM row groups in turn, so that a partly filled
@@ -68,15 +84,15 @@ template <int BM, int BN, int WM, int WN, int NB, int FML, int FM, int FN, int B
 __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uint32_t (&a_off)[AI],
                                        const uint32_t (&b_off)[BI], int nk, int a_rows, int tid, int wm, int wn,
                                        f32x16_t (&acc)[NB][FM][FN]) {
-  constexpr int NSA = 2, NSB = 3;  // ring slots
-  constexpr int RB = BK * 2;        // bytes of one row of a stage
+  constexpr int NSA = kNSA, NSB = kNSB;  // ring slots
+  constexpr int RB = BK * 2;              // bytes of one row of a stage
   constexpr int BROWS = NB * BN;
   constexpr int WTN = BN / WN;
   constexpr int KS = BK / 16;  // 16-wide K sub-steps per stage
-  static_assert(KS >= 3, "loads are spread under the first two sub-steps");
+  static_assert(KS >= 2, "loads are spread under the sub-steps before the barrier");
   constexpr int ROWS_PER_LD = 1024 / RB;
   static_assert(AI * ROWS_PER_LD * 4 == BM && BI * ROWS_PER_LD * 4 == BROWS, "DMA instructions per wave per stage");
-  static_assert(BI < 16, "vmcnt range");
+  static_assert(BI * (NSB - 2) < 64, "vmcnt range");
   constexpr int ASLOT = BM * RB, BSLOT = BROWS * RB;
   char* const sa0 = smem;
   char* const sb0 = smem + NSA * ASLOT;
@@ -137,15 +153,19 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
     for (int i = 0; i < NMF; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (ks == 0 && i < AI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      if (ks == 1 && i < BI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (KS > 2) {
+        if (ks == 0 && i < AI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (ks == 1 && i < BI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      } else if (ks == 0 && i < AI + BI) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
     }
   };
 
   issue_a(0);
-  issue_b(0);
-  issue_b(1);
-  asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI, 15)) : "memory");  // A(0), B(0) landed
+#pragma unroll
+  for (int j = 0; j < NSB - 1; ++j) issue_b(j);
+  asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI * (NSB - 2), 15)) : "memory");  // A(0), B(0) landed
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   frag_a_t af[2];
@@ -153,7 +173,7 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
   if constexpr (FML > 0) read_frags(0, 0, af[0], bf[0]);
   for (int kt = 0; kt < nk; ++kt) {
     issue_a(kt + 1);
-    issue_b(kt + 2);
+    issue_b(kt + NSB - 1);
     if constexpr (FML > 0) {
 #pragma unroll
       for (int ks = 0; ks + 1 < KS; ++ks) {
@@ -165,7 +185,7 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
     // A(kt+1) and B(kt+1) have landed (this wave's loads; B(kt+2) may still
     // be in flight) and this wave's reads of stage kt are done, before any
     // wave refills a slot
-    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI, 0)) : "memory");
+    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI * (NSB - 2), 0)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if constexpr (FML > 0) {
@@ -190,7 +210,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
   static_assert(WM * WN == 4, "4 waves per workgroup");
   static_assert(FM >= 1 && FN >= 1 && AI * 4 * ROWS_PER_LD == BM && BI * 4 * ROWS_PER_LD == BROWS, "tile shape");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BM * RB + 3 * BROWS * RB];
+  __shared__ __attribute__((aligned(1024))) char smem[kNSA * BM * RB + kNSB * BROWS * RB];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
@@ -309,9 +329,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
   // row, then copied out by all 256 threads in 16-byte chunks of whole rows.
   constexpr int ESZ = (EPI == kEpiF32) ? 4 : 2;  // bytes per output element
   constexpr int CS = BN * ESZ + 16;              // LDS row stride of the staged tile (padded against bank conflicts)
-  constexpr int LDS_BYTES = 2 * BM * RB + 3 * BROWS * RB;
+  constexpr int LDS_BYTES = kNSA * BM * RB + kNSB * BROWS * RB;
   constexpr int FMP_FIT = LDS_BYTES / CS / (WM * 32);  // 32-row blocks per row group that fit at once
-  constexpr int FMP = FMP_FIT < FM ? FMP_FIT : FM;
+  constexpr int FMP = band_blocks(FM, FMP_FIT);
   static_assert(FMP >= 1 && FM % FMP == 0, "epilogue bands");
   constexpr int BAND = FMP * WM * 32;         // tile rows per band
   constexpr int CPR = BN * ESZ / 16;          // 16-byte chunks per staged row
