@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--routing", default="x", choices=["x", "gaussian", "zipf"],
                     help="x: router projection from x; gaussian/zipf: given fp32 logits")
     ap.add_argument("--cpu-sample", type=int, default=-1,
-                    help="tokens of the oracle's timed CPU sample (0: skip; default 48, 8 in MXFP8, 512 for ep64)")
+                    help="tokens of the oracle's timed CPU sample (0: skip; default 48, 8 in MXFP8, 4096 for ep64)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
     ap.add_argument("--sweep", default="", metavar="B[:C],...",
                     help="after the main run, time the step at these minibatch sizes b (ring C, default b) and "
@@ -354,7 +354,7 @@ def main():
         result["copy_calibration_bytes"] = nb
         del src_t, dst_t
 
-    n_cpu = args.cpu_sample if args.cpu_sample >= 0 else (512 if job.name == "ep64" else (8 if mx else 48))
+    n_cpu = args.cpu_sample if args.cpu_sample >= 0 else (4096 if job.name == "ep64" else (8 if mx else 48))
     if n_cpu > 0:
         result["cpu_baseline"] = (cpu_baseline_ep(job, n_cpu) if job.name == "ep64"
                                   else cpu_baseline(job, n_cpu))
