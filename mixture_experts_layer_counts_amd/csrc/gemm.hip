@@ -7,9 +7,10 @@
 // expert-contiguous row tiles of the ring buffer (§3.1, condition 3: rows of
 // one expert sit contiguously, so no local reordering precedes the GEMMs).
 //
-// Tiling.  A workgroup of 4 waves computes a BM x BN output tile with
-// v_mfma_f32_32x32x16_bf16; the waves form a 2 x 2 grid, and the 32-row MFMA
-// blocks of the tile are dealt to the two row groups in turn.  Both operands
+// Tiling.  A workgroup of 8 waves (two per SIMD, so that one wave's MFMAs
+// issue while the other waits on a load or the barrier) computes a BM x BN
+// output tile with v_mfma_f32_32x32x16_bf16; the waves form a 4 x 2 grid, and
+// the 32-row MFMA blocks of the tile are dealt to the four row groups in turn.  Both operands
 // are K-contiguous (activation rows and weight rows), so each lane feeds the
 // matrix core with one 16-byte LDS read per operand.  K tiles of 64 are staged
 // through LDS by direct loads: activation rows one stage ahead, weight rows
@@ -45,6 +46,10 @@ namespace {
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
 #endif
+// Workgroups of 8 waves (4 row groups x 2 column groups, two waves per SIMD):
+// while one wave of a SIMD waits on a load or a barrier the other issues its
+// MFMAs.  Each wave owns a 64 x 128 quadrant (128 accumulator registers).
+constexpr int kWM = 4, kWN = 2;
 #ifndef MOE_GEMM_NSB
 #define MOE_GEMM_NSB 3
 #endif
@@ -91,7 +96,8 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
   constexpr int KS = BK / 16;  // 16-wide K sub-steps per stage
   static_assert(KS >= 2, "loads are spread under the sub-steps before the barrier");
   constexpr int ROWS_PER_LD = 1024 / RB;
-  static_assert(AI * ROWS_PER_LD * 4 == BM && BI * ROWS_PER_LD * 4 == BROWS, "DMA instructions per wave per stage");
+  static_assert(AI * ROWS_PER_LD * WM * WN == BM && BI * ROWS_PER_LD * WM * WN == BROWS,
+                "DMA instructions per wave per stage");
   static_assert(BI * (NSB - 2) < 64, "vmcnt range");
   constexpr int ASLOT = BM * RB, BSLOT = BROWS * RB;
   char* const sa0 = smem;
@@ -199,16 +205,16 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args) {
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;  // B halves (gate, up)
   constexpr int BROWS = NB * BN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int RB = BK * 2;                                // bytes of one row of a stage
   constexpr int ROWS_PER_LD = 1024 / RB;                    // rows one 1 KB direct load fills
-  constexpr int AI = BM / (4 * ROWS_PER_LD), BI = BROWS / (4 * ROWS_PER_LD);  // per wave per stage
-  static_assert(WM * WN == 4, "4 waves per workgroup");
-  static_assert(FM >= 1 && FN >= 1 && AI * 4 * ROWS_PER_LD == BM && BI * 4 * ROWS_PER_LD == BROWS, "tile shape");
+  constexpr int NW = WM * WN;                                                     // waves per workgroup
+  constexpr int AI = BM / (NW * ROWS_PER_LD), BI = BROWS / (NW * ROWS_PER_LD);  // per wave per stage
+  static_assert(FM >= 1 && FN >= 1 && AI * NW * ROWS_PER_LD == BM && BI * NW * ROWS_PER_LD == BROWS, "tile shape");
 
   __shared__ __attribute__((aligned(1024))) char smem[kNSA * BM * RB + kNSB * BROWS * RB];
 
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
   // The MFMA layout gives lane l column l % 32 of rows 8*(r/4) + 4*(l/32) +
   // r%4; written straight out that is a 2- or 4-byte store per lane.  The
   // tile (or, for fp32 outputs, a band of it) is first written to LDS row by
-  // row, then copied out by all 256 threads in 16-byte chunks of whole rows.
+  // row, then copied out by all threads in 16-byte chunks of whole rows.
   constexpr int ESZ = (EPI == kEpiF32) ? 4 : 2;  // bytes per output element
   constexpr int CS = BN * ESZ + 16;              // LDS row stride of the staged tile (padded against bank conflicts)
   constexpr int LDS_BYTES = kNSA * BM * RB + kNSB * BROWS * RB;
@@ -364,7 +370,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs args) {
     }
     __syncthreads();
     const int band_rows = min(BAND, nrows - band * BAND);
-    for (int idx = tid; idx < band_rows * CPR; idx += 256) {
+    for (int idx = tid; idx < band_rows * CPR; idx += 64 * NW) {
       const int row_b = idx / CPR, ch = idx - row_b * CPR;
       const int col = n0 + ch * EPC;
       if (col >= args.N) continue;
@@ -396,7 +402,7 @@ hipError_t run(const GemmArgs& a, hipStream_t stream) {
   const int64_t grid = (work + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  gemm_kernel<BM, BN, WM, WN, EPI, ROUTED, BK><<<static_cast<unsigned>(grid), 256, 0, stream>>>(a);
+  gemm_kernel<BM, BN, WM, WN, EPI, ROUTED, BK><<<static_cast<unsigned>(grid), 64 * WM * WN, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -421,15 +427,15 @@ hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t stream) {
   if (static_cast<int64_t>(a.N) * a.K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   switch (epilogue) {
     case kEpiSwiGLU:
-      return routed ? run<kRoutedBM, 128, 2, 2, kEpiSwiGLU, true>(a, stream)
-                    : run<256, 128, 2, 2, kEpiSwiGLU, false>(a, stream);
+      return routed ? run<kRoutedBM, 128, kWM, kWN, kEpiSwiGLU, true>(a, stream)
+                    : run<256, 128, kWM, kWN, kEpiSwiGLU, false>(a, stream);
     case kEpiBF16:
-      return routed ? run<kRoutedBM, 256, 2, 2, kEpiBF16, true>(a, stream)
-                    : run<256, 256, 2, 2, kEpiBF16, false>(a, stream);
+      return routed ? run<kRoutedBM, 256, kWM, kWN, kEpiBF16, true>(a, stream)
+                    : run<256, 256, kWM, kWN, kEpiBF16, false>(a, stream);
     case kEpiF32:
-      return routed ? run<kRoutedBM, 256, 2, 2, kEpiF32, true>(a, stream)
-                    : ((a.N <= 256 || a.k_splits > 1) ? run<128, 128, 2, 2, kEpiF32, false>(a, stream)
-                                  : run<256, 256, 2, 2, kEpiF32, false>(a, stream));
+      return routed ? run<kRoutedBM, 256, kWM, kWN, kEpiF32, true>(a, stream)
+                    : ((a.N <= 256 || a.k_splits > 1) ? run<128, 128, kWM, kWN, kEpiF32, false>(a, stream)
+                                  : run<256, 256, kWM, kWN, kEpiF32, false>(a, stream));
     default:
       return hipErrorInvalidValue;
   }
