@@ -42,6 +42,10 @@ constexpr int kMxBM = 256;      // tile rows (must match the tile lists, built w
 constexpr int kMxStageK = 128;  // K elements (bytes) per stage row
 constexpr int kRB = kMxStageK;  // bytes of one stage row
 constexpr int kNSA = 2, kNSB = 3;  // ring slots: activation rows, weight rows
+// 4 waves (2 x 2), one per SIMD: unlike the bf16 kernel, 8 waves measured
+// slower here (more scale-word loads and fragment reads per MFMA)
+constexpr int kWM = 2, kWN = 2;
+constexpr int kNW = kWM * kWN;
 
 struct MxSrc {
   __amdgpu_buffer_rsrc_t a, b0, b1, as, bs0, bs1;
@@ -56,7 +60,7 @@ __device__ __forceinline__ i32x8_t cat8(u32x4_t lo, u32x4_t hi) {
 }
 
 // Row of the tile held by 32-row MFMA block fm of a wave in row group wm.
-__device__ __forceinline__ int mx_tile_row(int wm, int fm) { return (fm * 2 + wm) * 32; }
+__device__ __forceinline__ int mx_tile_row(int wm, int fm) { return (fm * kWM + wm) * 32; }
 
 // Per-lane scale sources: the byte offset of the scale row of each fragment
 // row this lane supplies (A: block fm; B: half h, block fn).
@@ -79,10 +83,10 @@ __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const ui
                                           const uint32_t (&b_off)[BI], const MxScaleOff<FM, NB, FN>& so, int nk,
                                           int a_rows, int tid, int wm, int wn, f32x16_t (&acc)[NB][FM][FN]) {
   constexpr int BM = kMxBM, BROWS = NB * BN;
-  constexpr int WTN = BN / 2;
+  constexpr int WTN = BN / kWN;
   constexpr int ASLOT = BM * kRB, BSLOT = BROWS * kRB;
   constexpr int ROWS_PER_LD = 1024 / kRB;
-  static_assert(AI * ROWS_PER_LD * 4 == BM && BI * ROWS_PER_LD * 4 == BROWS, "data loads per wave per stage");
+  static_assert(AI * ROWS_PER_LD * kNW == BM && BI * ROWS_PER_LD * kNW == BROWS, "data loads per wave per stage");
   static_assert(BI < 16, "vmcnt range");
   char* const sa0 = smem;
   char* const sb0 = smem + kNSA * ASLOT;
@@ -209,20 +213,20 @@ __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const ui
 }
 
 template <int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_mx_kernel(const MxGemmArgs args) {
+__global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args) {
   constexpr int BM = kMxBM;
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
   constexpr int BROWS = NB * BN;
-  constexpr int WTN = BN / 2;
-  constexpr int FM = BM / 2 / 32, FN = WTN / 32;
+  constexpr int WTN = BN / kWN;
+  constexpr int FM = BM / kWM / 32, FN = WTN / 32;
   constexpr int ROWS_PER_LD = 1024 / kRB;
-  constexpr int AI = BM / (4 * ROWS_PER_LD), BI = BROWS / (4 * ROWS_PER_LD);
+  constexpr int AI = BM / (kNW * ROWS_PER_LD), BI = BROWS / (kNW * ROWS_PER_LD);
   constexpr int LDS_BYTES = kNSA * BM * kRB + kNSB * BROWS * kRB;
 
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / kWN, wn = wave % kWN;
 
   const int n_blocks = (args.N + BN - 1) / BN;
   const int W = *args.tile_count * n_blocks;
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxGemmArgs args) {
       for (int fn = 0; fn < FN; ++fn) acc[h][fm][fn] = f32x16_t{};
 
   // 32-row MFMA blocks of this wave that hold tile rows (wave-uniform)
-  int fm_live = ((nrows + 31) / 32 - wm + 1) / 2;
+  int fm_live = ((nrows + 31) / 32 - wm + kWM - 1) / kWM;
   fm_live = fm_live < 0 ? 0 : (fm_live > FM ? FM : fm_live);
   const int nk = K / kMxStageK;
   switch (fm_live) {
@@ -363,7 +367,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const MxGemmArgs args) {
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < nrows * CPR; idx += 256) {
+  for (int idx = tid; idx < nrows * CPR; idx += 64 * kNW) {
     const int row = idx / CPR, ch = idx - row * CPR;
     const int col = n0 + ch * EPC;
     if (col >= args.N) continue;  // N % 32 == 0: a chunk is all in or out
@@ -381,7 +385,7 @@ hipError_t run_mx(const MxGemmArgs& a, hipStream_t stream) {
   const int64_t grid = (work + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  gemm_mx_kernel<BN, EPI><<<static_cast<unsigned>(grid), 256, 0, stream>>>(a);
+  gemm_mx_kernel<BN, EPI><<<static_cast<unsigned>(grid), 64 * kNW, 0, stream>>>(a);
   return hipGetLastError();
 }
 
