@@ -99,9 +99,11 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
     inp = synth.make_inputs(w, device="cuda")
     weights = inp
     if precision == "mxfp8":  # routed weights quantised ahead of time (MoK paper §3.4), outside the timed region
+        from mixture_experts_layer_counts_amd import pack_mxfp8_scales
         weights = {n: inp[n] for n in ("ws_gate", "ws_up", "ws_down")}
         for n in ("gate", "up", "down"):
-            weights["q_" + n], weights["s_" + n] = quantize_mxfp8(inp["w_" + n])
+            q, sc = quantize_mxfp8(inp["w_" + n])
+            weights["q_" + n], weights["s_" + n] = q, pack_mxfp8_scales(sc)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
     dev = torch.device("cuda", 0)
@@ -149,9 +151,11 @@ def setup_ep64(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
                            device="cuda", with_weights=False)["w_router"]
     weights = inp
     if precision == "mxfp8":
+        from mixture_experts_layer_counts_amd import pack_mxfp8_scales
         weights = {n: inp[n] for n in ("ws_gate", "ws_up", "ws_down")}
         for n in ("gate", "up", "down"):
-            weights["q_" + n], weights["s_" + n] = quantize_mxfp8(inp["w_" + n])
+            q, sc = quantize_mxfp8(inp["w_" + n])
+            weights["q_" + n], weights["s_" + n] = q, pack_mxfp8_scales(sc)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
     dev = torch.device("cuda", 0)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -95,7 +95,9 @@ typedef struct {
 
 /* Expert weights, all K-contiguous (each output row is a contiguous K vector):
  *   routed  w_gate, w_up [L, I, D]; w_down [L, D, I]   (bf16, or e4m3 for MXFP8)
- *           s_gate, s_up [L, I, D/32]; s_down [L, D, I/32]   (E8M0, MXFP8 only)
+ *           s_gate, s_up [L, D/128, I, 4]; s_down [L, I/128, D, 4]   (E8M0,
+ *           MXFP8 only): stage-major scales, as moe_mxfp8_pack_scales writes
+ *           them from the row-major [L, N, K/32] of moe_quantize_mxfp8
  *   shared  ws_gate, ws_up [I_shared, D]; ws_down [D, I_shared]   (bf16) */
 typedef struct {
   const void *w_gate, *w_up, *w_down;
@@ -197,6 +199,19 @@ moe_status moe_routed_rows(const moe_shape* shape, const void* ws, size_t ws_byt
  */
 moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale,
                               void* stream);
+
+/*
+ * MX scales into the layout moe_forward reads (the same scales, moved; MoK
+ * paper §3.4, "MXFP8 Support": the weights are prepared once, ahead of the
+ * layer).  scale [groups, rows, K/32] row-major (moe_quantize_mxfp8's layout)
+ * -> packed [groups, K/128, rows, 4]: the byte of row r, 32-wide K block j of
+ * group g lands at ((g*(K/128) + j/4)*rows + r)*4 + j%4, so that the scale
+ * words of consecutive rows for one 128-wide K stage are adjacent.  K must be
+ * a multiple of 128; both pointers 4-byte aligned and not the same buffer.
+ * Byte moves only (bit-exact).
+ */
+moe_status moe_mxfp8_pack_scales(const uint8_t* scale, int64_t groups, int64_t rows, int64_t K, uint8_t* packed,
+                                 void* stream);
 
 /* Read the sticky device error word (MOE_DEVERR_* bits).  SYNCHRONISES the
  * stream: diagnostics only, never on the hot path. */

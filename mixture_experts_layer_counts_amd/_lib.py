@@ -54,6 +54,7 @@ _SIGS = {
     "moe_routed_rows": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_size_t, ctypes.POINTER(_P),
                                        ctypes.POINTER(ctypes.c_int64)]),
     "moe_quantize_mxfp8": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]),
+    "moe_mxfp8_pack_scales": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P]),
     "moe_get_device_error": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_size_t, _P,
                                             ctypes.POINTER(ctypes.c_int32)]),
     "moe_probe_begin": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32]),

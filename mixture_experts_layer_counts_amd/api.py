@@ -2,7 +2,7 @@
 
 Torch supplies device memory and the current HIP stream; the C calls do all
 of the work.  Names follow include/moe.h: ``route``, ``schedule``,
-``forward`` and ``quantize_mxfp8``.
+``forward``, ``quantize_mxfp8`` and ``pack_mxfp8_scales``.
 """
 
 from __future__ import annotations
@@ -133,7 +133,7 @@ class MoELayer:
             for n, qn, sn, shp in (("w_gate", "q_gate", "s_gate", (L, I, D)), ("w_up", "q_up", "s_up", (L, I, D)),
                                    ("w_down", "q_down", "s_down", (L, D, I))):
                 _need(weights[qn], qn, torch.uint8, shp, dev)
-                _need(weights[sn], sn, torch.uint8, shp[:-1] + (shp[-1] // 32,), dev)
+                _need(weights[sn], sn, torch.uint8, (L, shp[2] // 128, shp[1], 4), dev)
                 setattr(w, n, _ptr(weights[qn]))
                 setattr(w, sn, _ptr(weights[sn]))
         for n, shp in (("ws_gate", (Is, D)), ("ws_up", (Is, D)), ("ws_down", (D, Is))):
@@ -188,3 +188,18 @@ def quantize_mxfp8(src: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     sc = torch.empty(src.shape[:-1] + (K // 32,), dtype=torch.uint8, device=src.device)
     _lib.check("moe_quantize_mxfp8", lib.moe_quantize_mxfp8(_ptr(src), rows, K, _ptr(q), _ptr(sc), _stream()))
     return q, sc
+
+
+def pack_mxfp8_scales(scale: torch.Tensor) -> torch.Tensor:
+    """Row-major MX scales [G, N, K/32] -> the stage-major [G, K/128, N, 4]
+    that ``forward`` reads (moe_mxfp8_pack_scales)."""
+    lib = _lib.load()
+    if scale.dtype != torch.uint8 or not scale.is_contiguous() or scale.device.type != "cuda" or scale.dim() != 3:
+        raise ValueError("scale must be a contiguous uint8 [G, N, K/32] device tensor")
+    G, N, KS = scale.shape
+    if KS % 4:
+        raise ValueError("K must be a multiple of 128")
+    packed = torch.empty((G, KS // 4, N, 4), dtype=torch.uint8, device=scale.device)
+    _lib.check("moe_mxfp8_pack_scales", lib.moe_mxfp8_pack_scales(_ptr(scale), G, N, KS * 32, _ptr(packed),
+                                                                  _stream()))
+    return packed

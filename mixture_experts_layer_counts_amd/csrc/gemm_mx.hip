@@ -4,8 +4,9 @@
 // Support": the routed experts run on MXFP8 operands; weights are quantised
 // ahead of time and activations inside the dispatch (the gather) and inside
 // the gated activation (the up/gate epilogue).  Operands are E4M3 bytes with
-// one E8M0 scale per 32 consecutive elements along K, stored row-major as
-// [rows][K] bytes and [rows][K/32] scale bytes.
+// one E8M0 scale per 32 consecutive elements along K: data row-major [rows][K],
+// scales stage-major [K/128][rows][4] (the 4 scale bytes of a row's 128-wide K
+// stage form one word, and the words of consecutive rows are adjacent).
 //
 // The matrix core does the block scaling itself: v_mfma_scale_f32_32x32x64_f8f6f4
 // multiplies a 32x64 E4M3 block of A by a 64x32 block of B with one scale per
@@ -19,7 +20,10 @@
 // same XOR swizzle, the same expert-major XCD-aware work order over the
 // balanced tile list, 32-row blocks dealt to the wave row groups in turn.
 // Each lane loads the scale words of its own fragment rows (4 bytes = the 4
-// K blocks of a stage) straight into registers, one stage ahead.  The K loop
+// K blocks of a stage) straight into registers, one stage ahead; with the
+// stage-major scale layout the 32 rows of a fragment share one 128-byte line
+// (row-major scales would touch 32 lines per load and cost about a quarter of
+// the up/gate kernel's time).  The K loop
 // always runs from k = 0 in the same order, so a row's result does not
 // depend on the tile or minibatch it falls in.
 //
@@ -81,7 +85,8 @@ struct MxScales {  // one stage's scale words (4 K blocks) of this lane's fragme
 template <int BN, int NB, int FML, int FM, int FN, int AI, int BI>
 __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const uint32_t (&a_off)[AI],
                                           const uint32_t (&b_off)[BI], const MxScaleOff<FM, NB, FN>& so, int nk,
-                                          int a_rows, int tid, int wm, int wn, f32x16_t (&acc)[NB][FM][FN]) {
+                                          int a_rows, int as_stage, int bs_stage, int tid, int wm, int wn,
+                                          f32x16_t (&acc)[NB][FM][FN]) {
   constexpr int BM = kMxBM, BROWS = NB * BN;
   constexpr int WTN = BN / kWN;
   constexpr int ASLOT = BM * kRB, BSLOT = BROWS * kRB;
@@ -104,12 +109,12 @@ __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const ui
             kc * kRB);
     // the scale words of stage kt (A and B) ride with the A loads
 #pragma unroll
-    for (int fm = 0; fm < FML; ++fm) sc.a[fm] = __builtin_amdgcn_raw_buffer_load_b32(src.as, so.a[fm], kc * 4, 0);
+    for (int fm = 0; fm < FML; ++fm) sc.a[fm] = __builtin_amdgcn_raw_buffer_load_b32(src.as, so.a[fm], kc * as_stage, 0);
 #pragma unroll
     for (int h = 0; h < NB; ++h)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        sc.b[h][fn] = __builtin_amdgcn_raw_buffer_load_b32(h ? src.bs1 : src.bs0, so.b[h][fn], kc * 4, 0);
+        sc.b[h][fn] = __builtin_amdgcn_raw_buffer_load_b32(h ? src.bs1 : src.bs0, so.b[h][fn], kc * bs_stage, 0);
   };
   auto issue_b = [&](int kt) __attribute__((always_inline)) {
     const int kc = kt < nk ? kt : nk - 1;
@@ -267,14 +272,15 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args
     n = n < args.N ? n : args.N - 1;
     b_off[j] = static_cast<uint32_t>(static_cast<int64_t>(n) * K + c * 16);
   }
-  // ---- scale rows of this lane's fragment rows (rows past the tile or N are
-  // clamped; their products only reach dropped outputs) ----
+  // ---- scale words of this lane's fragment rows in stage 0 (rows past the
+  // tile or N are clamped; their products only reach dropped outputs); stage
+  // kc's word sits kc * rows * 4 bytes further ----
   MxScaleOff<FM, NB, FN> so;
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     const int row = mx_tile_row(wm, fm) + (lane & 31);
     const int64_t p = p0 + (row < nrows ? row : nrows - 1);
-    so.a[fm] = static_cast<uint32_t>(((p - args.a_sub) % args.a_mod) * KS);
+    so.a[fm] = static_cast<uint32_t>(((p - args.a_sub) % args.a_mod) * 4);
   }
 #pragma unroll
   for (int h = 0; h < NB; ++h)
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args
     for (int fn = 0; fn < FN; ++fn) {
       int n = n0 + wn * WTN + fn * 32 + (lane & 31);
       n = n < args.N ? n : args.N - 1;
-      so.b[h][fn] = static_cast<uint32_t>(static_cast<int64_t>(n) * KS);
+      so.b[h][fn] = static_cast<uint32_t>(n * 4);
     }
   constexpr int kRsrcWord3 = 0x00020000;
   MxSrc src;
@@ -316,11 +322,13 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args
   int fm_live = ((nrows + 31) / 32 - wm + kWM - 1) / kWM;
   fm_live = fm_live < 0 ? 0 : (fm_live > FM ? FM : fm_live);
   const int nk = K / kMxStageK;
+  const int as_stage = static_cast<int>(args.a_rows * 4), bs_stage = args.N * 4;
   switch (fm_live) {
 #define MOE_CASE(n)                                                                                         \
   case n:                                                                                                   \
     if constexpr (n <= FM)                                                                                  \
-      k_loop_mx<BN, NB, n, FM, FN, AI, BI>(smem, src, a_off, b_off, so, nk, nrows, tid, wm, wn, acc);       \
+      k_loop_mx<BN, NB, n, FM, FN, AI, BI>(smem, src, a_off, b_off, so, nk, nrows, as_stage, bs_stage, tid, \
+                                            wm, wn, acc);                                                \
     break;
     MOE_CASE(0)
     MOE_CASE(1)
@@ -359,7 +367,8 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args
           const int X = mx_scale_exponent(amax);
           *reinterpret_cast<uint8_t*>(smem + row_t * CS + col_l) = e4m3_from_f32(ldexpf(v, -X));
           if (row_t < nrows && col_ok && (lane & 31) == 0)
-            args.Cs[(p0 + row_t - args.c_sub) * (args.ldc / 32) + (n0 + col_l) / 32] = static_cast<uint8_t>(X + 127);
+            args.Cs[(((n0 + col_l) / kMxStageK) * args.cs_rows + (p0 + row_t - args.c_sub)) * 4 +
+                    ((n0 + col_l) / 32) % 4] = static_cast<uint8_t>(X + 127);
         } else {
           *reinterpret_cast<uint16_t*>(smem + row_t * CS + col_l * 2) = f32_to_bf16(acc[0][fm][fn][r]);
         }
@@ -402,7 +411,9 @@ hipError_t launch_gemm_mx(const MxGemmArgs& a, int epilogue, hipStream_t stream)
   if (reinterpret_cast<uintptr_t>(a.C) % 16 != 0) return hipErrorInvalidValue;
   switch (epilogue) {
     case kEpiSwiGLU:
-      if (!a.Cs || a.ldc % 32 != 0) return hipErrorInvalidValue;
+      // h scales are stage-major [ldc/128][cs_rows][4]
+      if (!a.Cs || a.ldc % kMxStageK != 0 || a.cs_rows <= 0 || a.cs_rows * a.ldc >= (int64_t(1) << 31))
+        return hipErrorInvalidValue;
       return run_mx<128, kEpiSwiGLU>(a, stream);
     case kEpiBF16:
       if (a.ldc % 8 != 0) return hipErrorInvalidValue;

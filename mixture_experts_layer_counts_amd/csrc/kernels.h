@@ -61,8 +61,9 @@ struct GemmArgs {
 };
 
 // Grouped MXFP8 GEMM (routed only): E4M3 operands with one E8M0 scale per 32
-// elements along K, fp32 accumulate.  A row-major [a_rows][K] + [a_rows][K/32];
-// B [experts][N][K] + [experts][N][K/32].
+// elements along K, fp32 accumulate.  Data row-major, scales stage-major (the
+// byte of row r, K block j at ((j / 4) * rows + r) * 4 + j % 4): A [a_rows][K]
+// + [K/128][a_rows][4]; B per expert [N][K] + [K/128][N][4].
 struct MxGemmArgs {
   const uint8_t* A;  // tile position p reads row (p - a_sub) mod a_mod
   const uint8_t* As;
@@ -75,8 +76,9 @@ struct MxGemmArgs {
   const uint8_t* Bs1;
   int N;
   int K;
-  void* C;      // SwiGLU: E4M3 [.][ldc], scales to Cs [.][ldc/32]; BF16: bf16 [.][ldc]
+  void* C;      // SwiGLU: E4M3 [.][ldc], scales to Cs [ldc/128][cs_rows][4]; BF16: bf16 [.][ldc]
   uint8_t* Cs;  // output row = c_idx ? c_idx[p] : p - c_sub
+  int64_t cs_rows;
   int64_t ldc;
   const int32_t* c_idx;
   int64_t c_sub;
@@ -102,7 +104,8 @@ hipError_t launch_combine(const uint16_t* Y, const float* shared_out, const floa
                           int64_t route_base, int T, int D, int k, bool by_route_dst, uint16_t* out, float* out32,
                           hipStream_t stream);
 
-// MX gather: ring_q[p mod C] / ring_s[p mod C] = MX(x_src[sched_src[p] / k]).
+// MX gather: ring_q[p mod C] / ring_s[p mod C] = MX(x_src[sched_src[p] / k]),
+// scales stage-major [D/128][C][4].
 hipError_t launch_gather_mx(const uint16_t* x_src, int64_t src_rows, int D, int k, const int32_t* sched_src,
                             const int32_t* offsets, int L, int64_t p_begin, int64_t rows, int64_t ring_rows,
                             uint8_t* ring_q, uint8_t* ring_s, int* err, hipStream_t stream);
@@ -118,6 +121,9 @@ hipError_t launch_clear_int(int* p, int n, hipStream_t stream);
 
 // MXFP8: rows x K bf16 -> E4M3 codes + one E8M0 scale per 32 elements along K.
 hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale,
+                                 hipStream_t stream);
+// Row-major scales [groups][rows][K/32] -> stage-major [groups][K/128][rows][4].
+hipError_t launch_pack_mx_scales(const uint8_t* scale, int64_t groups, int64_t rows, int64_t K, uint8_t* packed,
                                  hipStream_t stream);
 
 }  // namespace moe

@@ -185,6 +185,7 @@ hipError_t routed_minibatch_mx(const moe_shape* shape, const moe_weights* w, con
   u.K = D;
   u.C = h_q;
   u.Cs = h_s;
+  u.cs_rows = b;
   u.ldc = I;
   u.c_sub = p_begin;
   u.tiles = tiles;
@@ -476,6 +477,15 @@ moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t*
   if (!src || !q || !scale) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_quantize_mxfp8(static_cast<const uint16_t*>(src), rows, K, q, scale,
                                                static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_mxfp8_pack_scales(const uint8_t* scale, int64_t groups, int64_t rows, int64_t K, uint8_t* packed,
+                                 void* stream) {
+  if (groups < 0 || rows < 0 || K <= 0 || K % 128 != 0) return MOE_ERR_INVALID_ARG;
+  if (groups == 0 || rows == 0) return MOE_OK;
+  if (!scale || !packed || scale == packed) return MOE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(scale) % 4 || reinterpret_cast<uintptr_t>(packed) % 4) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_pack_mx_scales(scale, groups, rows, K, packed, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_probe_begin(int32_t kernel_id, int32_t max_launches) {

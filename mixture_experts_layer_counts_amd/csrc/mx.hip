@@ -75,10 +75,37 @@ hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t K, u
   return hipGetLastError();
 }
 
+// Scale words into the layout the MX GEMM reads: row-major [groups][rows][K/32]
+// -> stage-major [groups][K/128][rows][4] (one 4-byte word per row and 128-wide
+// K stage; one thread moves one word).
+__global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint32_t* __restrict__ src, int64_t words,
+                                                             int64_t rows, int64_t stages,
+                                                             uint32_t* __restrict__ dst) {
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (w >= words) return;
+  const int64_t per_group = stages * rows;
+  const int64_t g = w / per_group, rem = w - g * per_group;
+  const int64_t st = rem / rows, r = rem - st * rows;
+  dst[w] = src[(g * rows + r) * stages + st];
+}
+
+hipError_t launch_pack_mx_scales(const uint8_t* scale, int64_t groups, int64_t rows, int64_t K, uint8_t* packed,
+                                 hipStream_t stream) {
+  if (K % 128 != 0 || reinterpret_cast<uintptr_t>(scale) % 4 || reinterpret_cast<uintptr_t>(packed) % 4)
+    return hipErrorInvalidValue;
+  const int64_t stages = K / 128, words = groups * rows * stages;
+  if (words <= 0) return hipSuccess;
+  if ((words + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
+  pack_mx_scales_kernel<<<static_cast<unsigned>((words + 255) / 256), 256, 0, stream>>>(
+      reinterpret_cast<const uint32_t*>(scale), words, rows, stages, reinterpret_cast<uint32_t*>(packed));
+  return hipGetLastError();
+}
+
 // MX gather (§3.4: the activation quantisation rides on the dispatch).  As the
 // bf16 gather, schedule position p reads source row sched_src[p] / k and fills
-// ring slot p mod C, here as E4M3 bytes [C][D] and scale bytes [C][D/32]; one
-// thread quantises one 32-element block.
+// ring slot p mod C, here as E4M3 bytes [C][D] and stage-major scale bytes
+// [D/128][C][4] (the layout the MX GEMM reads); one thread quantises one
+// 32-element block.
 __global__ __launch_bounds__(256) void gather_mx_kernel(const uint16_t* __restrict__ x_src, int64_t src_rows, int D,
                                                         int k, const int32_t* __restrict__ sched_src,
                                                         const int32_t* __restrict__ offsets, int L, int64_t p_begin,
@@ -97,14 +124,15 @@ __global__ __launch_bounds__(256) void gather_mx_kernel(const uint16_t* __restri
     return;
   }
   const int64_t slot = p % ring_rows;
-  quantize_block32(x_src + src_row * D + blk * 32, ring_q + slot * D + blk * 32, ring_s + slot * nb + blk);
+  quantize_block32(x_src + src_row * D + blk * 32, ring_q + slot * D + blk * 32,
+                   ring_s + ((blk >> 2) * ring_rows + slot) * 4 + (blk & 3));
 }
 
 hipError_t launch_gather_mx(const uint16_t* x_src, int64_t src_rows, int D, int k, const int32_t* sched_src,
                             const int32_t* offsets, int L, int64_t p_begin, int64_t rows, int64_t ring_rows,
                             uint8_t* ring_q, uint8_t* ring_s, int* err, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  if (D % 32 != 0) return hipErrorInvalidValue;
+  if (D % 128 != 0) return hipErrorInvalidValue;
   const int64_t n = rows * (D / 32);
   if ((n + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
   gather_mx_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(
@@ -136,14 +164,14 @@ __global__ __launch_bounds__(256) void gather_src_mx_kernel(const uint16_t* __re
     u32x4_t* d = reinterpret_cast<u32x4_t*>(ring_q + slot * D + blk * 32);
     d[0] = lo;
     d[1] = hi;
-    ring_s[slot * nb + blk] = sc;
+    ring_s[((blk >> 2) * ring_rows + slot) * 4 + (blk & 3)] = sc;
   }
 }
 
 hipError_t launch_gather_src_mx(const uint16_t* x, int T, int D, int k, const int32_t* route_dst, int64_t P,
                                 int64_t ring_rows, uint8_t* ring_q, uint8_t* ring_s, int* err, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  if (D % 32 != 0) return hipErrorInvalidValue;
+  if (D % 128 != 0) return hipErrorInvalidValue;
   const int64_t n = static_cast<int64_t>(T) * (D / 32);
   if ((n + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
   gather_src_mx_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(x, T, D, k, route_dst, P,

@@ -41,12 +41,14 @@ def layer(w: synth.Workload, dev, b=None, C=None, R=1, precision="bf16"):
 
 
 def mx_weights_dev(inp_dev):
-    """Routed weights MX-quantised on the GPU by moe_quantize_mxfp8 (the
-    product's own preprocessing); the shared expert stays bf16."""
-    from mixture_experts_layer_counts_amd import quantize_mxfp8
+    """Routed weights MX-quantised on the GPU by moe_quantize_mxfp8, scales
+    packed by moe_mxfp8_pack_scales (the product's own preprocessing); the
+    shared expert stays bf16."""
+    from mixture_experts_layer_counts_amd import pack_mxfp8_scales, quantize_mxfp8
     out = {n: inp_dev[n] for n in ("ws_gate", "ws_up", "ws_down")}
     for n in ("gate", "up", "down"):
-        out["q_" + n], out["s_" + n] = quantize_mxfp8(inp_dev["w_" + n])
+        q, s = quantize_mxfp8(inp_dev["w_" + n])
+        out["q_" + n], out["s_" + n] = q, pack_mxfp8_scales(s)
     return out
 
 

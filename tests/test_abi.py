@@ -115,3 +115,13 @@ def test_calls_validate_before_launching(lib):
                            n, None) == -1
     # null shape
     assert lib.moe_workspace_bytes(None, ctypes.byref(ctypes.c_size_t())) == -1
+
+
+def test_pack_scales_validates_before_launching(lib):
+    a, b = ctypes.c_void_p(4096), ctypes.c_void_p(8192)  # never dereferenced
+    assert lib.moe_mxfp8_pack_scales(a, 2, 8, 96, b, None) == -1      # K not a multiple of 128
+    assert lib.moe_mxfp8_pack_scales(a, 2, 8, 128, a, None) == -1     # in place
+    assert lib.moe_mxfp8_pack_scales(ctypes.c_void_p(4097), 2, 8, 128, b, None) == -1  # misaligned
+    assert lib.moe_mxfp8_pack_scales(None, 2, 8, 128, b, None) == -1
+    assert lib.moe_mxfp8_pack_scales(a, -1, 8, 128, b, None) == -1
+    assert lib.moe_mxfp8_pack_scales(a, 0, 8, 128, b, None) == 0      # nothing to move: no launch

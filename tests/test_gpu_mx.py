@@ -48,6 +48,24 @@ def test_quantize_bit_exact(rows, K, seed):
     assert np.array_equal(q.cpu().numpy(), qo)
 
 
+@pytest.mark.parametrize("G,N,K", [(1, 1, 128), (3, 37, 384), (4, 2048, 7168)])
+def test_pack_scales_bit_exact(G, N, K):
+    """moe_mxfp8_pack_scales moves the scale byte of (group g, row r, K block
+    j) to ((g*(K/128) + j/4)*N + r)*4 + j%4, and nothing else."""
+    dev = need_gpu()
+    from mixture_experts_layer_counts_amd import pack_mxfp8_scales
+    s = torch.randint(0, 256, (G, N, K // 32), dtype=torch.uint8, generator=torch.Generator().manual_seed(G * N))
+    say("mx pack scales", (G, N, K))
+    got = pack_mxfp8_scales(s.to(dev)).cpu().numpy().reshape(-1)
+    torch.cuda.synchronize()
+    src = s.numpy()
+    g, r, j = np.meshgrid(np.arange(G), np.arange(N), np.arange(K // 32), indexing="ij")
+    dst = ((g * (K // 128) + j // 4) * N + r) * 4 + j % 4
+    want = np.empty(G * N * (K // 32), dtype=np.uint8)
+    want[dst.reshape(-1)] = src.reshape(-1)
+    assert np.array_equal(got, want)
+
+
 # ---------------------------------------------------------------------------
 # The layer in MXFP8 (routed experts MX, shared expert bf16) against the oracle
 # at 5e-2 * RMS; MX needs D and I to be multiples of 128.
