@@ -204,8 +204,10 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still target LDS when the workgroup ends
 }
 
+// One work item (row tile, N block, K range) of the GEMM: its K loop and its
+// epilogue.  The workgroup's LDS is free on entry and on return.
 template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args) {
+__device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blocks, int S, char* smem) {
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;  // B halves (gate, up)
   constexpr int BROWS = NB * BN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -216,21 +218,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args)
   constexpr int AI = BM / (NW * ROWS_PER_LD), BI = BROWS / (NW * ROWS_PER_LD);  // per wave per stage
   static_assert(FM >= 1 && FN >= 1 && AI * NW * ROWS_PER_LD == BM && BI * NW * ROWS_PER_LD == BROWS, "tile shape");
 
-  __shared__ __attribute__((aligned(1024))) char smem[kNSA * BM * RB + kNSB * BROWS * RB];
-
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
 
-  // ---- which (tile, N block) this workgroup computes ----
-  const int n_blocks = (args.N + BN - 1) / BN;
-  const int tcount = ROUTED ? *args.tile_count : (args.dense_rows + BM - 1) / BM;
-  const int S = ROUTED ? 1 : args.k_splits;  // K ranges (dense only), each with its own output plane
-  const int W = tcount * n_blocks * S;
-  const int chunk = (W + kXcds - 1) / kXcds;
-  const int local = static_cast<int>(blockIdx.x) / kXcds;
-  if (local >= chunk) return;
-  const int w = (static_cast<int>(blockIdx.x) % kXcds) * chunk + local;
-  if (w >= W) return;
   int e = 0, nrows, tile, nb, ks = 0;
   int64_t p0;
   if constexpr (ROUTED) {
@@ -358,7 +348,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args)
           float v = acc[0][fm][fn][r];
           if constexpr (EPI == kEpiSwiGLU) {
             const float u = acc[NB - 1][fm][fn][r];
-            v = v / (1.0f + __expf(-v)) * u;
+            v = silu_mul(v, u);
           }
           if constexpr (EPI == kEpiF32) {
             *reinterpret_cast<float*>(smem + row_b * CS + col_l * 4) = v;
@@ -394,15 +384,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args)
   }
 }
 
+// One work item per workgroup: workgroup b runs item (b mod 8) * ceil(W/8) +
+// b / 8, so each XCD walks a contiguous run of items.
+template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args) {
+  constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
+  constexpr int RB = BK * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[kNSA * BM * RB + kNSB * NB * BN * RB];
+  const int n_blocks = (args.N + BN - 1) / BN;
+  const int tcount = ROUTED ? *args.tile_count : (args.dense_rows + BM - 1) / BM;
+  const int S = ROUTED ? 1 : args.k_splits;  // K ranges (dense only), each with its own output plane
+  const int W = tcount * n_blocks * S;
+  const int chunk = (W + kXcds - 1) / kXcds;
+  const int local = static_cast<int>(blockIdx.x) / kXcds;
+  if (local >= chunk) return;
+  const int w = (static_cast<int>(blockIdx.x) % kXcds) * chunk + local;
+  if (w >= W) return;
+  gemm_item<BM, BN, WM, WN, EPI, ROUTED, BK>(args, w, n_blocks, S, smem);
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK = kStageK>
 hipError_t run(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles = ROUTED ? a.max_tiles : (a.dense_rows + BM - 1) / BM;
   const int64_t n_blocks = (a.N + BN - 1) / BN;
   const int64_t work = tiles * n_blocks * (ROUTED ? 1 : a.k_splits);
+  if (work <= 0) return hipSuccess;
+  if (work > 0x7ffffff0) return hipErrorInvalidValue;
+  auto kernel = gemm_kernel<BM, BN, WM, WN, EPI, ROUTED, BK>;
   const int64_t grid = (work + kXcds - 1) / kXcds * kXcds;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  gemm_kernel<BM, BN, WM, WN, EPI, ROUTED, BK><<<static_cast<unsigned>(grid), 64 * WM * WN, 0, stream>>>(a);
+  kernel<<<static_cast<unsigned>(grid), 64 * WM * WN, 0, stream>>>(a);
   return hipGetLastError();
 }
 

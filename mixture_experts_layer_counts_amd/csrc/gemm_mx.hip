@@ -14,7 +14,7 @@
 // supplies row l % 32; its 32 bytes are K[16h, 16h+16) and K[32+16h, 32+16h+16)
 // of the 64-wide step, and its scale byte is that row's scale of K block h.
 //
-// The pipeline is the bf16 kernel's: 256 x BN tiles, 4 waves, K stages of
+// The pipeline is the bf16 kernel's: 256 x BN tiles, 8 waves, K stages of
 // 128 bytes per row (two MFMA steps) in two LDS rings fed by direct
 // buffer->LDS loads (activation rows one stage ahead, weight rows two), the
 // same XOR swizzle, the same expert-major XCD-aware work order over the
@@ -28,10 +28,9 @@
 // depend on the tile or minibatch it falls in.
 //
 // Epilogues, staged through LDS so that rows leave in 16-byte stores: SwiGLU
-// with MX quantisation of h along I (a row's 32-column block lives in the 32
-// lanes of one half-wave, which reduce its largest magnitude by shuffles),
-// and bf16 for the down projection, scattered to the row of the route it
-// came from.
+// with MX quantisation of h along I (staged as fp32; one thread then
+// quantises one 32-column block of a row), and bf16 for the down projection,
+// scattered to the row of the route it came from.
 
 #include "common.h"
 #include "gemm_common.h"
@@ -46,9 +45,8 @@ constexpr int kMxBM = 256;      // tile rows (must match the tile lists, built w
 constexpr int kMxStageK = 128;  // K elements (bytes) per stage row
 constexpr int kRB = kMxStageK;  // bytes of one stage row
 constexpr int kNSA = 2, kNSB = 3;  // ring slots: activation rows, weight rows
-// 4 waves (2 x 2), one per SIMD: unlike the bf16 kernel, 8 waves measured
-// slower here (more scale-word loads and fragment reads per MFMA)
-constexpr int kWM = 2, kWN = 2;
+// 8 waves (4 x 2), two per SIMD: one wave's MFMAs issue while the other waits
+constexpr int kWM = 4, kWN = 2;
 constexpr int kNW = kWM * kWN;
 
 struct MxSrc {
@@ -130,23 +128,39 @@ __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const ui
     i32x8_t a[FML > 0 ? FML : 1];
     i32x8_t b[NB][FN];
   };
+  // LDS byte offsets of this lane's fragment halves within a slot, per MFMA
+  // step and half j.  The swizzle term depends on (row / 2) % 8 alone, which
+  // all fragment rows of a lane share (they differ by multiples of 32), so a
+  // fragment's halves sit at these offsets plus a constant: the reads need
+  // no address registers of their own.
+  static_assert((BN / 2) % 8 == 0, "fragment rows share the swizzle term");
+  uint32_t abase[2][2], bbase[2][2];
+#pragma unroll
+  for (int step = 0; step < 2; ++step)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = step * 4 + frag_h + 2 * j;
+      abase[step][j] = swz<kRB>(mx_tile_row(wm, 0) + frag_row, c);
+      bbase[step][j] = swz<kRB>(wn * WTN + frag_row, c);
+    }
   auto read_frags = [&](int kt, int step, Frags& f) __attribute__((always_inline)) {
     const char* sa = sa0 + (kt % kNSA) * ASLOT;
     const char* sb = sb0 + (kt % kNSB) * BSLOT;
-    const int c0 = step * 4 + frag_h, c1 = c0 + 2;
+    const char* a0 = sa + abase[step][0];
+    const char* a1 = sa + abase[step][1];
+    const char* b0 = sb + bbase[step][0];
+    const char* b1 = sb + bbase[step][1];
+    constexpr int kFragA = kWM * 32 * kRB;  // bytes between a lane's A fragment rows
 #pragma unroll
-    for (int fm = 0; fm < FML; ++fm) {
-      const int row = mx_tile_row(wm, fm) + frag_row;
-      f.a[fm] = cat8(*reinterpret_cast<const u32x4_t*>(sa + swz<kRB>(row, c0)),
-                     *reinterpret_cast<const u32x4_t*>(sa + swz<kRB>(row, c1)));
-    }
+    for (int fm = 0; fm < FML; ++fm)
+      f.a[fm] = cat8(*reinterpret_cast<const u32x4_t*>(a0 + fm * kFragA),
+                     *reinterpret_cast<const u32x4_t*>(a1 + fm * kFragA));
 #pragma unroll
     for (int h = 0; h < NB; ++h)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        const int row = h * BN + wn * WTN + fn * 32 + frag_row;
-        f.b[h][fn] = cat8(*reinterpret_cast<const u32x4_t*>(sb + swz<kRB>(row, c0)),
-                          *reinterpret_cast<const u32x4_t*>(sb + swz<kRB>(row, c1)));
+        const int off = (h * BN + fn * 32) * kRB;
+        f.b[h][fn] = cat8(*reinterpret_cast<const u32x4_t*>(b0 + off), *reinterpret_cast<const u32x4_t*>(b1 + off));
       }
   };
   // v_perm selector that replicates byte (2 step + h) of a scale word into all
@@ -217,8 +231,10 @@ __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const ui
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still target LDS when the workgroup ends
 }
 
+// One work item (row tile, N block): its K loop and its epilogue.  The
+// workgroup's LDS is free on entry and on return.
 template <int BN, int EPI>
-__global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args) {
+__device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int n_blocks, char* smem) {
   constexpr int BM = kMxBM;
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
   constexpr int BROWS = NB * BN;
@@ -228,18 +244,9 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args
   constexpr int AI = BM / (kNW * ROWS_PER_LD), BI = BROWS / (kNW * ROWS_PER_LD);
   constexpr int LDS_BYTES = kNSA * BM * kRB + kNSB * BROWS * kRB;
 
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
-
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / kWN, wn = wave % kWN;
 
-  const int n_blocks = (args.N + BN - 1) / BN;
-  const int W = *args.tile_count * n_blocks;
-  const int chunk = (W + kXcds - 1) / kXcds;
-  const int local = static_cast<int>(blockIdx.x) / kXcds;
-  if (local >= chunk) return;
-  const int w = (static_cast<int>(blockIdx.x) % kXcds) * chunk + local;
-  if (w >= W) return;
   const int4 g = args.tiles[w / n_blocks];
   const int nt = g.x >> 10, first = g.w;
   const int lw = w - first * n_blocks;
@@ -341,60 +348,111 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args
   }
 
   // ---- epilogue, staged through LDS so that rows leave in 16-byte pieces ----
-  constexpr int ESZ = (EPI == kEpiSwiGLU) ? 1 : 2;  // E4M3 h, or bf16 rows
-  constexpr int CS = BN * ESZ + 16;                 // LDS row stride of the staged tile
-  static_assert(BM * CS <= LDS_BYTES, "staged tile fits");
-  constexpr int CPR = BN * ESZ / 16;
-  constexpr int EPC = 16 / ESZ;
+  // The MFMA layout gives lane l column l % 32 of rows 8*(r/4) + 4*(l/32) +
+  // r%4 of each 32 x 32 block.
   __syncthreads();  // every wave is done with the K loop's LDS
+  if constexpr (EPI == kEpiSwiGLU) {
+    // SwiGLU, then MX quantisation of h along I, in two passes.  Pass 1: the
+    // lanes write SiLU(g) * u of their entries to LDS as fp32.  Pass 2: each
+    // thread takes one 32-column block of a row, finds its largest
+    // magnitude and writes the 32 E4M3 bytes and the scale byte.  Nothing
+    // crosses lanes and nothing branches per element.
+    constexpr int VS = BN * 4 + 16;  // fp32 row stride: an odd number of 16-byte units
+    static_assert(BM * VS <= LDS_BYTES, "staged tile fits");
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    if (fm >= fm_live) continue;  // wave-uniform
+    for (int fm = 0; fm < FM; ++fm) {
+      if (fm >= fm_live) continue;  // wave-uniform
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int col_l = wn * WTN + fn * 32 + (lane & 31);
-      const bool col_ok = n0 + wn * WTN + fn * 32 < args.N;  // N % 32 == 0: a 32-column block is all in or out
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col_l = wn * WTN + fn * 32 + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row_t = mx_tile_row(wm, fm) + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if constexpr (EPI == kEpiSwiGLU) {
-          const float gv = acc[0][fm][fn][r], uv = acc[1][fm][fn][r];
-          const float v = gv / (1.0f + __expf(-gv)) * uv;
-          // largest magnitude of the row's 32-column block: the 32 lanes of this half-wave
-          float amax = fabsf(v);
+        for (int r = 0; r < 16; ++r) {
+          const int row_t = mx_tile_row(wm, fm) + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          *reinterpret_cast<float*>(smem + row_t * VS + col_l * 4) = silu_mul(acc[0][fm][fn][r], acc[1][fm][fn][r]);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int BPR = BN / 32;  // 32-column blocks per row
+    // consecutive threads take consecutive rows of one block column: with the
+    // odd row stride their 16-byte reads fall on distinct banks
+    for (int it = tid; it < nrows * BPR; it += 64 * kNW) {
+      const int blk = it / nrows, row = it - blk * nrows;
+      const int col = n0 + blk * 32;
+      if (col >= args.N) continue;  // N % 32 == 0: a block is all in or out
+      float v[32];
 #pragma unroll
-          for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
-          const int X = mx_scale_exponent(amax);
-          *reinterpret_cast<uint8_t*>(smem + row_t * CS + col_l) = e4m3_from_f32(ldexpf(v, -X));
-          if (row_t < nrows && col_ok && (lane & 31) == 0)
-            args.Cs[(((n0 + col_l) / kMxStageK) * args.cs_rows + (p0 + row_t - args.c_sub)) * 4 +
-                    ((n0 + col_l) / 32) % 4] = static_cast<uint8_t>(X + 127);
-        } else {
+      for (int i = 0; i < 8; ++i) {
+        const f32x4_t q = *reinterpret_cast<const f32x4_t*>(smem + row * VS + blk * 128 + i * 16);
+        v[4 * i] = q[0];
+        v[4 * i + 1] = q[1];
+        v[4 * i + 2] = q[2];
+        v[4 * i + 3] = q[3];
+      }
+      u32x4_t lo, hi;
+      const uint8_t sc = quantize32_f32(v, lo, hi);
+      const int64_t p = p0 + row;
+      const int64_t crow = args.c_idx ? static_cast<int64_t>(args.c_idx[p]) : p - args.c_sub;
+      u32x4_t* d = reinterpret_cast<u32x4_t*>(static_cast<char*>(args.C) + crow * args.ldc + col);
+      d[0] = lo;
+      d[1] = hi;
+      args.Cs[((col / kMxStageK) * args.cs_rows + (p - args.c_sub)) * 4 + (col / 32) % 4] = sc;
+    }
+  } else {
+    constexpr int CS = BN * 2 + 16;  // bf16 row stride of the staged tile
+    static_assert(BM * CS <= LDS_BYTES, "staged tile fits");
+    constexpr int CPR = BN * 2 / 16;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (fm >= fm_live) continue;  // wave-uniform
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col_l = wn * WTN + fn * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row_t = mx_tile_row(wm, fm) + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
           *reinterpret_cast<uint16_t*>(smem + row_t * CS + col_l * 2) = f32_to_bf16(acc[0][fm][fn][r]);
         }
       }
     }
+    __syncthreads();
+    for (int idx = tid; idx < nrows * CPR; idx += 64 * kNW) {
+      const int row = idx / CPR, ch = idx - row * CPR;
+      const int col = n0 + ch * 8;
+      if (col >= args.N) continue;  // N % 32 == 0: a chunk is all in or out
+      const int64_t p = p0 + row;
+      const int64_t crow = args.c_idx ? static_cast<int64_t>(args.c_idx[p]) : p - args.c_sub;
+      *reinterpret_cast<u32x4_t*>(static_cast<char*>(args.C) + (crow * args.ldc + col) * 2) =
+          *reinterpret_cast<const u32x4_t*>(smem + row * CS + ch * 16);
+    }
   }
-  __syncthreads();
-  for (int idx = tid; idx < nrows * CPR; idx += 64 * kNW) {
-    const int row = idx / CPR, ch = idx - row * CPR;
-    const int col = n0 + ch * EPC;
-    if (col >= args.N) continue;  // N % 32 == 0: a chunk is all in or out
-    const int64_t p = p0 + row;
-    const int64_t crow = args.c_idx ? static_cast<int64_t>(args.c_idx[p]) : p - args.c_sub;
-    *reinterpret_cast<u32x4_t*>(static_cast<char*>(args.C) + (crow * args.ldc + col) * ESZ) =
-        *reinterpret_cast<const u32x4_t*>(smem + row * CS + ch * 16);
-  }
+}
+
+// One work item per workgroup: workgroup b runs item (b mod 8) * ceil(W/8) +
+// b / 8, so each XCD walks a contiguous run of items.
+template <int BN, int EPI>
+__global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args) {
+  constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) char smem[kNSA * kMxBM * kRB + kNSB * NB * BN * kRB];
+  const int n_blocks = (args.N + BN - 1) / BN;
+  const int W = *args.tile_count * n_blocks;
+  const int chunk = (W + kXcds - 1) / kXcds;
+  const int local = static_cast<int>(blockIdx.x) / kXcds;
+  if (local >= chunk) return;
+  const int w = (static_cast<int>(blockIdx.x) % kXcds) * chunk + local;
+  if (w >= W) return;
+  gemm_mx_item<BN, EPI>(args, w, n_blocks, smem);
 }
 
 template <int BN, int EPI>
 hipError_t run_mx(const MxGemmArgs& a, hipStream_t stream) {
   const int64_t n_blocks = (a.N + BN - 1) / BN;
   const int64_t work = static_cast<int64_t>(a.max_tiles) * n_blocks;
+  if (work <= 0) return hipSuccess;
+  if (work > 0x7ffffff0) return hipErrorInvalidValue;
+  auto kernel = gemm_mx_kernel<BN, EPI>;
   const int64_t grid = (work + kXcds - 1) / kXcds * kXcds;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  gemm_mx_kernel<BN, EPI><<<static_cast<unsigned>(grid), 64 * kNW, 0, stream>>>(a);
+  kernel<<<static_cast<unsigned>(grid), 64 * kNW, 0, stream>>>(a);
   return hipGetLastError();
 }
 

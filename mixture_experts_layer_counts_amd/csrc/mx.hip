@@ -33,21 +33,7 @@ __device__ __forceinline__ uint8_t quantize_block32_words(const uint16_t* __rest
       v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
     }
   }
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int X = mx_scale_exponent(amax);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) word |= static_cast<uint32_t>(e4m3_from_f32(ldexpf(v[4 * i + j], -X))) << (8 * j);
-    if (i < 4)
-      lo[i] = word;
-    else
-      hi[i - 4] = word;
-  }
-  return static_cast<uint8_t>(X + 127);
+  return quantize32_f32(v, lo, hi);
 }
 
 __device__ __forceinline__ void quantize_block32(const uint16_t* __restrict__ src, uint8_t* __restrict__ q,
