@@ -79,6 +79,16 @@ def src_digest(*names):
     return h.hexdigest()[:16]
 
 
+# sources an expert GEMM kernel is compiled from: stored counter readings
+# apply only while none of them has changed
+GEMM_SOURCES = {False: ("gemm.hip", "gemm_common.h", "common.h", "kernels.h"),
+                True: ("gemm_mx.hip", "gemm_common.h", "common.h", "kernels.h", "mx.h")}
+
+
+def gemm_digest(mx):
+    return src_digest(*GEMM_SOURCES[bool(mx)])
+
+
 class Job:
     """One benchmark configuration: its layer, inputs and step function."""
 
@@ -312,8 +322,7 @@ def main():
     tr_path = os.path.join(ROOT, "profiles", f"traffic_{dominant}_{job.name}.json")
     if os.path.exists(tr_path):
         tr = json.load(open(tr_path))
-        src = "gemm_mx.hip" if mx else "gemm.hip"
-        if tr.get("src_digest") == src_digest(src) and tr.get("minibatch_rows") == job.b and \
+        if tr.get("src_digest") == gemm_digest(mx) and tr.get("minibatch_rows") == job.b and \
                 tr.get("precision", "bf16") == job.precision:
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
