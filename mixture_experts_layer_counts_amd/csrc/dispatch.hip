@@ -47,40 +47,39 @@ hipError_t launch_gather(const uint16_t* x_src, int64_t src_rows, int D, int k, 
 }
 
 // The same placement walked from the source side, for one GPU (R = 1) when a
-// single minibatch holds every routed row: one wave per token reads the row
+// single minibatch holds every routed row: one block per token reads the row
 // once and writes it to the ring slots of the token's k routes (route_dst is
 // the inverse of the schedule table), instead of reading it k times.
 __global__ __launch_bounds__(256) void gather_src_kernel(const uint16_t* __restrict__ x, int T, int D, int k,
                                                          const int32_t* __restrict__ route_dst, int64_t P,
                                                          int64_t ring_rows, uint16_t* __restrict__ ring, int* err) {
-  const int t = static_cast<int>(blockIdx.x) * 4 + static_cast<int>(threadIdx.x) / kWave;
-  if (t >= T) return;
-  int64_t slot[16];
-  bool ok = true;
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    if (s < k) {
-      const int32_t p = route_dst[static_cast<int64_t>(t) * k + s];
-      ok = ok && p >= 0 && p < P;
-      slot[s] = (p >= 0 && p < P) ? p % ring_rows : -1;
-    }
+  __shared__ int32_t slot_s[16];  // ring slot of each route (< ring_rows), or -1
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < k) {
+    const int32_t p = route_dst[static_cast<int64_t>(t) * k + tid];
+    const bool ok = p >= 0 && p < P;
+    if (!ok) raise_error(err, kErrExpertRange);  // a table not built by the schedule kernels
+    slot_s[tid] = ok ? static_cast<int32_t>(p % ring_rows) : -1;
   }
-  if (!ok && lane_id() == 0) raise_error(err, kErrExpertRange);  // a table not built by the schedule kernels
+  __syncthreads();
+  int32_t slot[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) slot[s] = s < k ? slot_s[s] : -1;
   const uint4* __restrict__ src = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * D);
   const int n = D / 8;
-  for (int c = lane_id(); c < n; c += kWave) {
+  for (int c = tid; c < n; c += 256) {
     const uint4 v = src[c];
 #pragma unroll
     for (int s = 0; s < 16; ++s)
-      if (s < k && slot[s] >= 0) reinterpret_cast<uint4*>(ring + slot[s] * D)[c] = v;
+      if (slot[s] >= 0) reinterpret_cast<uint4*>(ring + static_cast<int64_t>(slot[s]) * D)[c] = v;
   }
 }
 
 hipError_t launch_gather_src(const uint16_t* x, int T, int D, int k, const int32_t* route_dst, int64_t P,
                              int64_t ring_rows, uint16_t* ring, int* err, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  gather_src_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, stream>>>(x, T, D, k, route_dst, P, ring_rows,
-                                                                           ring, err);
+  if (k > 16) return hipErrorInvalidValue;
+  gather_src_kernel<<<static_cast<unsigned>(T), 256, 0, stream>>>(x, T, D, k, route_dst, P, ring_rows, ring, err);
   return hipGetLastError();
 }
 
@@ -99,23 +98,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   }
   __syncthreads();
   for (int c = tid * 8; c < D; c += 256 * 8) {
+    // every load of this chunk is issued before the fixed-order sum uses them
+    uint4 y[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s < k && row_s[s] >= 0) y[s] = *reinterpret_cast<const uint4*>(Y + row_s[s] * D + c);
+    const float4* shp = reinterpret_cast<const float4*>(sh + static_cast<int64_t>(t) * D + c);
+    const float4 s0 = shp[0], s1 = shp[1];
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int s = 0; s < k; ++s) {
-      const int64_t row = row_s[s];
-      if (row < 0) continue;  // a route to a remote expert: its row is summed where it returns
-      const uint4 y = *reinterpret_cast<const uint4*>(Y + row * D + c);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      // a route to a remote expert (row < 0) is summed where its row returns
+      if (s >= k || row_s[s] < 0) continue;
       const float g = g_s[s];
-      const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+      const uint32_t w[4] = {y[s].x, y[s].y, y[s].z, y[s].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] = fmaf(g, __uint_as_float(w[i] << 16), acc[2 * i]);
         acc[2 * i + 1] = fmaf(g, __uint_as_float(w[i] & 0xffff0000u), acc[2 * i + 1]);
       }
     }
-    const float4* shp = reinterpret_cast<const float4*>(sh + static_cast<int64_t>(t) * D + c);
-    const float4 s0 = shp[0], s1 = shp[1];
     acc[0] += s0.x;
     acc[1] += s0.y;
     acc[2] += s0.z;
