@@ -26,6 +26,13 @@ CASES = [
     ("skewed", synth.Workload("skewed", T=257, D=192, I=128, E=24, k=6, I_shared=320, seed=8, routing="zipf"),
      [(None, None), (200, 400)]),
     ("mid", synth.workload("mid", routing="gaussian"), [(4096, 8192)]),
+    # limits: the most routes per token, the most experts, a single token
+    ("k16", synth.Workload("k16", T=33, D=128, I=64, E=64, k=16, I_shared=64, seed=14, routing="gaussian"),
+     [(None, None), (64, 128)]),
+    ("e1024", synth.Workload("e1024", T=40, D=128, I=64, E=1024, k=8, I_shared=64, seed=15, routing="gaussian"),
+     [(None, None), (100, 200)]),
+    ("t1", synth.Workload("t1", T=1, D=128, I=64, E=8, k=2, I_shared=64, seed=16, routing="gaussian"),
+     [(None, None), (1, 1)]),
 ]
 
 

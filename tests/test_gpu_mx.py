@@ -81,6 +81,8 @@ MX_CASES = [
      [(None, None), (200, 400)]),
     ("wide-mx", synth.Workload("wide-mx", T=1024, D=1024, I=512, E=48, k=8, I_shared=512, seed=33,
                                routing="gaussian"), [(8192, 8192), (1000, 3000)]),
+    ("k16-mx", synth.Workload("k16-mx", T=40, D=128, I=128, E=64, k=16, I_shared=64, seed=34, routing="gaussian"),
+     [(None, None), (128, 256)]),
 ]
 
 
