@@ -23,9 +23,9 @@
 // K blocks of a stage) straight into registers, one stage ahead; with the
 // stage-major scale layout the 32 rows of a fragment share one 128-byte line
 // (row-major scales would touch 32 lines per load and cost about a quarter of
-// the up/gate kernel's time).  The K loop
-// always runs from k = 0 in the same order, so a row's result does not
-// depend on the tile or minibatch it falls in.
+// the up/gate kernel's time).  The K loop always runs from k = 0 in the same
+// order, so a row's result does not depend on the tile or minibatch it falls
+// in.
 //
 // Epilogues, staged through LDS so that rows leave in 16-byte stores: SwiGLU
 // with MX quantisation of h along I (staged as fp32; one thread then
