@@ -13,8 +13,9 @@
 // the 32-row MFMA blocks of the tile are dealt to the four row groups in turn.  Both operands
 // are K-contiguous (activation rows and weight rows), so each lane feeds the
 // matrix core with one 16-byte LDS read per operand.  K tiles of 64 are staged
-// through LDS by direct loads: activation rows one stage ahead, weight rows
-// two stages ahead (they stream from HBM).  The K loop always runs from k = 0
+// through LDS by direct loads, each slot refilled as soon as its last reads
+// are done: activation rows one stage ahead, weight rows two (they stream from
+// HBM).  The K loop always runs from k = 0
 // in the same order and there is no split-K, so a row's result does not
 // depend on the tile or minibatch it falls in.
 //
@@ -54,8 +55,8 @@ constexpr int kWM = 4, kWN = 2;
 #define MOE_GEMM_NSB 3
 #endif
 constexpr int kStageK = MOE_GEMM_BK;  // K elements per pipeline stage
-constexpr int kNSA = 2;               // LDS ring slots: activation rows (one stage ahead)
-constexpr int kNSB = MOE_GEMM_NSB;    // weight rows (kNSB - 1 stages ahead)
+constexpr int kNSA = 2;               // LDS ring slots: activation rows (issued one stage ahead)
+constexpr int kNSB = MOE_GEMM_NSB;    // weight rows (issued kNSB - 1 stages ahead)
 
 // Largest divisor of fm that is at most fit (the 32-row blocks per row group
 // of one epilogue band).
@@ -76,15 +77,14 @@ __device__ __forceinline__ int tile_row(int wm, int fm) {
 // The K loop of one workgroup.  BK-wide K tiles are staged through two LDS
 // rings fed by direct buffer->LDS loads (lane l's 16 bytes land at base + 16 l,
 // so one wave instruction fills 1 KB; each lane fetches the global chunk the
-// swizzle maps to its slot): activation rows in 2 slots, one stage ahead, and
-// weight rows in 3 slots, two stages ahead, since weights stream from HBM and
-// need the longer lead.  At the top of step kt the wave requests A(kt+1) and
-// B(kt+2), spread under the first two K sub-steps' MFMAs.  The 16-wide K
-// sub-steps run back to back with the next sub-step's fragments read under
-// the current MFMAs; before the last sub-step's MFMAs the wave waits for
-// A(kt+1) and B(kt+1) (B(kt+2) may stay in flight) and passes the one barrier
-// of the step, so stage kt+1's first fragments are read under them.  FML =
-// 32-row MFMA blocks of this wave that hold tile rows.
+// swizzle maps to its slot): activation rows in 2 slots and weight rows in
+// kNSB slots, since weights stream from HBM and need the longer lead.  The
+// 16-wide K sub-steps run back to back with the next sub-step's fragments read
+// under the current MFMAs.  Before the last sub-step's MFMAs of stage kt the
+// wave waits for A(kt+1) and B(kt+1) and passes the one barrier of the step;
+// right after it, the slots stage kt used are refilled with A(kt+2) and
+// B(kt+kNSB), issued under those MFMAs while stage kt+1's first fragments are
+// read.  FML = 32-row MFMA blocks of this wave that hold tile rows.
 template <int BM, int BN, int WM, int WN, int NB, int FML, int FM, int FN, int BK, int AI, int BI>
 __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uint32_t (&a_off)[AI],
                                        const uint32_t (&b_off)[BI], int nk, int a_rows, int tid, int wm, int wn,
@@ -94,11 +94,10 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
   constexpr int BROWS = NB * BN;
   constexpr int WTN = BN / WN;
   constexpr int KS = BK / 16;  // 16-wide K sub-steps per stage
-  static_assert(KS >= 2, "loads are spread under the sub-steps before the barrier");
+  static_assert(KS >= 2, "fragment reads alternate between two register sets");
   constexpr int ROWS_PER_LD = 1024 / RB;
   static_assert(AI * ROWS_PER_LD * WM * WN == BM && BI * ROWS_PER_LD * WM * WN == BROWS,
                 "DMA instructions per wave per stage");
-  static_assert(BI * (NSB - 2) < 64, "vmcnt range");
   constexpr int ASLOT = BM * RB, BSLOT = BROWS * RB;
   char* const sa0 = smem;
   char* const sb0 = smem + NSA * ASLOT;
@@ -152,34 +151,35 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
   };
   constexpr int NMF = FML * NB * FN;  // MFMAs per 16-wide sub-step
   constexpr int NRD = FML + NB * FN;  // fragment reads per 16-wide sub-step
-  // one fragment read under each MFMA; in sub-steps 0 and 1 also one load
-  // (A loads, then B loads) under each MFMA
+  // one fragment read under each MFMA; in the sub-step after the barrier
+  // also the stage's loads (A, then B), one under each MFMA
   auto interleave = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NMF; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (KS > 2) {
-        if (ks == 0 && i < AI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        if (ks == 1 && i < BI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      } else if (ks == 0 && i < AI + BI) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
+      if (ks == KS && i < AI + BI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   };
 
+  // Ring protocol: a slot is refilled as soon as the barrier after its last
+  // reads has passed.  At the barrier that ends stage kt's reads, A(kt+2)
+  // goes to A slot kt % 2 and B(kt+NSB) to B slot kt % NSB: activation rows
+  // get a whole stage to arrive and weight rows NSB - 1 stages.
+  static_assert(NSB >= 3 && (NSB - 1) * BI + AI < 64, "B ring depth and vmcnt range");
   issue_a(0);
 #pragma unroll
   for (int j = 0; j < NSB - 1; ++j) issue_b(j);
-  asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI * (NSB - 2), 15)) : "memory");  // A(0), B(0) landed
+  issue_a(1);
+  issue_b(NSB - 1);
+  // A(0) and B(0) have landed; B(1 .. NSB-1) and A(1) may be in flight
+  asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm((NSB - 1) * BI + AI, 15)) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   frag_a_t af[2];
   frag_b_t bf[2];
   if constexpr (FML > 0) read_frags(0, 0, af[0], bf[0]);
   for (int kt = 0; kt < nk; ++kt) {
-    issue_a(kt + 1);
-    issue_b(kt + NSB - 1);
     if constexpr (FML > 0) {
 #pragma unroll
       for (int ks = 0; ks + 1 < KS; ++ks) {
@@ -188,12 +188,14 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
         interleave(ks);
       }
     }
-    // A(kt+1) and B(kt+1) have landed (this wave's loads; B(kt+2) may still
-    // be in flight) and this wave's reads of stage kt are done, before any
-    // wave refills a slot
-    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI * (NSB - 2), 0)) : "memory");
+    // A(kt+1) and B(kt+1) have landed (B(kt+NSB-1), issued after A(kt+1),
+    // may still be in flight) and this wave's reads of stage kt are done,
+    // before any wave refills a slot
+    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI, 0)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    issue_a(kt + 2);
+    issue_b(kt + NSB);
     if constexpr (FML > 0) {
       // past the last stage this reads the repeated stage, and is not used
       read_frags(kt + 1, 0, af[KS & 1], bf[KS & 1]);
