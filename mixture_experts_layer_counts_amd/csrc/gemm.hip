@@ -56,7 +56,13 @@ constexpr int kWM = 4, kWN = 2;
 #endif
 constexpr int kStageK = MOE_GEMM_BK;  // K elements per pipeline stage
 constexpr int kNSA = 2;               // LDS ring slots: activation rows (issued one stage ahead)
-constexpr int kNSB = MOE_GEMM_NSB;    // weight rows (issued kNSB - 1 stages ahead)
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU (gfx950)
+
+// LDS ring slots for weight rows (issued NSB - 1 stages ahead): MOE_GEMM_NSB
+// where the rings fit in LDS, else 2.
+constexpr int ring_b_slots(int a_stage_bytes, int b_stage_bytes) {
+  return kNSA * a_stage_bytes + MOE_GEMM_NSB * b_stage_bytes <= kLdsBytes ? MOE_GEMM_NSB : 2;
+}
 
 // Largest divisor of fm that is at most fit (the 32-row blocks per row group
 // of one epilogue band).
@@ -78,20 +84,20 @@ __device__ __forceinline__ int tile_row(int wm, int fm) {
 // rings fed by direct buffer->LDS loads (lane l's 16 bytes land at base + 16 l,
 // so one wave instruction fills 1 KB; each lane fetches the global chunk the
 // swizzle maps to its slot): activation rows in 2 slots and weight rows in
-// kNSB slots, since weights stream from HBM and need the longer lead.  The
+// NSB slots, since weights stream from HBM and need the longer lead.  The
 // 16-wide K sub-steps run back to back with the next sub-step's fragments read
 // under the current MFMAs.  Before the last sub-step's MFMAs of stage kt the
 // wave waits for A(kt+1) and B(kt+1) and passes the one barrier of the step;
 // right after it, the slots stage kt used are refilled with A(kt+2) and
-// B(kt+kNSB), issued under those MFMAs while stage kt+1's first fragments are
+// B(kt+NSB), issued under those MFMAs while stage kt+1's first fragments are
 // read.  FML = 32-row MFMA blocks of this wave that hold tile rows.
 template <int BM, int BN, int WM, int WN, int NB, int FML, int FM, int FN, int BK, int AI, int BI>
 __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uint32_t (&a_off)[AI],
                                        const uint32_t (&b_off)[BI], int nk, int a_rows, int tid, int wm, int wn,
                                        f32x16_t (&acc)[NB][FM][FN]) {
-  constexpr int NSA = kNSA, NSB = kNSB;  // ring slots
-  constexpr int RB = BK * 2;              // bytes of one row of a stage
+  constexpr int RB = BK * 2;  // bytes of one row of a stage
   constexpr int BROWS = NB * BN;
+  constexpr int NSA = kNSA, NSB = ring_b_slots(BM * RB, BROWS * RB);  // ring slots
   constexpr int WTN = BN / WN;
   constexpr int KS = BK / 16;  // 16-wide K sub-steps per stage
   static_assert(KS >= 2, "fragment reads alternate between two register sets");
@@ -166,7 +172,10 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
   // reads has passed.  At the barrier that ends stage kt's reads, A(kt+2)
   // goes to A slot kt % 2 and B(kt+NSB) to B slot kt % NSB: activation rows
   // get a whole stage to arrive and weight rows NSB - 1 stages.
-  static_assert(NSB >= 3 && (NSB - 1) * BI + AI < 64, "B ring depth and vmcnt range");
+  static_assert(NSB >= 2 && (NSB - 1) * BI + AI < 64, "B ring depth and vmcnt range");
+  // loads that may still be in flight once A(kt+1) and B(kt+1) have landed:
+  // B(kt+NSB-1), issued after A(kt+1), unless that is B(kt+1) itself
+  constexpr int VM_STAGE = NSB >= 3 ? BI : 0;
   issue_a(0);
 #pragma unroll
   for (int j = 0; j < NSB - 1; ++j) issue_b(j);
@@ -191,7 +200,7 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
     // A(kt+1) and B(kt+1) have landed (B(kt+NSB-1), issued after A(kt+1),
     // may still be in flight) and this wave's reads of stage kt are done,
     // before any wave refills a slot
-    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI, 0)) : "memory");
+    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_STAGE, 0)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue_a(kt + 2);
@@ -327,7 +336,7 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
   // row, then copied out by all threads in 16-byte chunks of whole rows.
   constexpr int ESZ = (EPI == kEpiF32) ? 4 : 2;  // bytes per output element
   constexpr int CS = BN * ESZ + 16;              // LDS row stride of the staged tile (padded against bank conflicts)
-  constexpr int LDS_BYTES = kNSA * BM * RB + kNSB * BROWS * RB;
+  constexpr int LDS_BYTES = kNSA * BM * RB + ring_b_slots(BM * RB, BROWS * RB) * BROWS * RB;
   constexpr int FMP_FIT = LDS_BYTES / CS / (WM * 32);  // 32-row blocks per row group that fit at once
   constexpr int FMP = band_blocks(FM, FMP_FIT);
   static_assert(FMP >= 1 && FM % FMP == 0, "epilogue bands");
@@ -392,7 +401,9 @@ template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args) {
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
   constexpr int RB = BK * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[kNSA * BM * RB + kNSB * NB * BN * RB];
+  constexpr int LDS_BYTES = kNSA * BM * RB + ring_b_slots(BM * RB, NB * BN * RB) * NB * BN * RB;
+  static_assert(LDS_BYTES <= kLdsBytes, "LDS rings");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const int n_blocks = (args.N + BN - 1) / BN;
   const int tcount = ROUTED ? *args.tile_count : (args.dense_rows + BM - 1) / BM;
   const int S = ROUTED ? 1 : args.k_splits;  // K ranges (dense only), each with its own output plane
@@ -420,7 +431,10 @@ hipError_t run(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-constexpr int kRoutedBM = 256;
+// Routed tiles: 320 rows on a 2 x 4 wave grid (five 32-row blocks per row
+// group), so that an expert segment of up to 320 rows (DeepSeek-V3 routing
+// gives 200-320 per expert) is one tile and its weights pass through LDS once.
+constexpr int kRoutedBM = 320, kRoutedWM = 2, kRoutedWN = 4;
 
 int gemm_routed_bm() { return kRoutedBM; }
 
@@ -439,13 +453,13 @@ hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t stream) {
   if (static_cast<int64_t>(a.N) * a.K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   switch (epilogue) {
     case kEpiSwiGLU:
-      return routed ? run<kRoutedBM, 128, kWM, kWN, kEpiSwiGLU, true>(a, stream)
+      return routed ? run<kRoutedBM, 128, kRoutedWM, kRoutedWN, kEpiSwiGLU, true>(a, stream)
                     : run<256, 128, kWM, kWN, kEpiSwiGLU, false>(a, stream);
     case kEpiBF16:
-      return routed ? run<kRoutedBM, 256, kWM, kWN, kEpiBF16, true>(a, stream)
+      return routed ? run<kRoutedBM, 256, kRoutedWM, kRoutedWN, kEpiBF16, true>(a, stream)
                     : run<256, 256, kWM, kWN, kEpiBF16, false>(a, stream);
     case kEpiF32:
-      return routed ? run<kRoutedBM, 256, kWM, kWN, kEpiF32, true>(a, stream)
+      return routed ? run<kRoutedBM, 256, kRoutedWM, kRoutedWN, kEpiF32, true>(a, stream)
                     : ((a.N <= 256 || a.k_splits > 1) ? run<128, 128, kWM, kWN, kEpiF32, false>(a, stream)
                                   : run<256, 256, kWM, kWN, kEpiF32, false>(a, stream));
     default:

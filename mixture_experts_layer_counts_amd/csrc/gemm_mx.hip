@@ -41,7 +41,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kMxBM = 256;      // tile rows (must match the tile lists, built with gemm_routed_bm())
+constexpr int kMxBM = 256;      // tile rows (the tile lists are built with gemm_mx_routed_bm())
 constexpr int kMxStageK = 128;  // K elements (bytes) per stage row
 constexpr int kRB = kMxStageK;  // bytes of one stage row
 constexpr int kNSA = 2, kNSB = 3;  // ring slots: activation rows, weight rows
@@ -458,8 +458,9 @@ hipError_t run_mx(const MxGemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+int gemm_mx_routed_bm() { return kMxBM; }
+
 hipError_t launch_gemm_mx(const MxGemmArgs& a, int epilogue, hipStream_t stream) {
-  if (gemm_routed_bm() != kMxBM) return hipErrorInvalidValue;
   if (a.K % kMxStageK != 0 || a.N <= 0 || a.N % 32 != 0 || a.a_rows <= 0 || !a.tiles || !a.tile_count)
     return hipErrorInvalidValue;
   // buffer resources address at most 2^31 bytes per operand here

@@ -87,8 +87,10 @@ struct MxGemmArgs {
   int max_tiles;
 };
 hipError_t launch_gemm_mx(const MxGemmArgs& args, int epilogue, hipStream_t stream);
+// Tile rows of the routed MXFP8 GEMM kernels (their tile lists are built with it).
+int gemm_mx_routed_bm();
 
-// Tile rows of the routed GEMM kernels (tile lists are built with it).
+// Tile rows of the routed bf16 GEMM kernels (their tile lists are built with it).
 int gemm_routed_bm();
 hipError_t launch_gemm(const GemmArgs& args, int epilogue, hipStream_t stream);
 int gemm_tiles_bound(int64_t rows, int groups, int bm);

@@ -66,7 +66,7 @@ Layout layout_of(const moe_shape* s) {
   Layout L{};
   L.router_splits = router_splits(s);
   const int64_t R = s->num_src_ranks, NK = s->T * s->k, Lx = s->experts_per_rank;
-  const int bm = moe::gemm_routed_bm();
+  const int bm = s->precision == MOE_MXFP8 ? moe::gemm_mx_routed_bm() : moe::gemm_routed_bm();
   L.n_minibatches = s->max_rows > 0 ? (s->max_rows + s->minibatch_rows - 1) / s->minibatch_rows : 0;
   L.max_tiles = moe::gemm_tiles_bound(std::min<int64_t>(s->minibatch_rows, std::max<int64_t>(s->max_rows, 1)),
                                       static_cast<int>(Lx), bm);
@@ -341,7 +341,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
   float* sh_out = at<float>(ws, L.shared_out);
   int4* tiles = at<int4>(ws, L.tiles);
   int32_t* tile_count = at<int32_t>(ws, L.tile_count);
-  const int bm = moe::gemm_routed_bm();
+  const int bm = mx ? moe::gemm_mx_routed_bm() : moe::gemm_routed_bm();
 
   // 1. tile lists of every minibatch, from the device-side expert offsets
   {
