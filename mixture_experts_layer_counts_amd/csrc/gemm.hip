@@ -9,15 +9,17 @@
 //
 // Tiling.  A workgroup of 8 waves (two per SIMD, so that one wave's MFMAs
 // issue while the other waits on a load or the barrier) computes a BM x BN
-// output tile with v_mfma_f32_32x32x16_bf16; the waves form a 4 x 2 grid, and
-// the 32-row MFMA blocks of the tile are dealt to the four row groups in turn.  Both operands
-// are K-contiguous (activation rows and weight rows), so each lane feeds the
-// matrix core with one 16-byte LDS read per operand.  K tiles of 64 are staged
-// through LDS by direct loads, each slot refilled as soon as its last reads
-// are done: activation rows one stage ahead, weight rows two (they stream from
-// HBM).  The K loop always runs from k = 0
-// in the same order and there is no split-K, so a row's result does not
-// depend on the tile or minibatch it falls in.
+// output tile with v_mfma_f32_32x32x16_bf16; the waves form a WM x WN grid
+// (4 x 2 for 256-row dense tiles, 2 x 4 for 320-row routed tiles), and the
+// 32-row MFMA blocks of the tile are dealt to the row groups in turn.  Both
+// operands are K-contiguous (activation rows and weight rows), so each lane
+// feeds the matrix core with one 16-byte LDS read per operand.  K tiles of 64
+// are staged through LDS rings by direct loads, each slot refilled as soon as
+// its last reads are done: activation rows one stage ahead, weight rows two
+// (they stream from HBM), or one where LDS cannot hold a third weight slot.
+// The K loop always runs from k = 0 in the same order and there is no
+// split-K, so a row's result does not depend on the tile or minibatch it
+// falls in.
 //
 // Work order (routed).  The 256 MI355X CUs sit in 8 XCDs, each with its own
 // L2, and workgroups are dealt to XCDs round-robin.  Work items are ordered
@@ -47,30 +49,36 @@ namespace {
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
 #endif
-// Workgroups of 8 waves (4 row groups x 2 column groups, two waves per SIMD):
-// while one wave of a SIMD waits on a load or a barrier the other issues its
-// MFMAs.  Each wave owns a 64 x 128 quadrant (128 accumulator registers).
+// Dense tiles: workgroups of 8 waves (4 row groups x 2 column groups, two
+// waves per SIMD): while one wave of a SIMD waits on a load or a barrier the
+// other issues its MFMAs.  Each wave owns a 64 x 128 block of a 256 x 256
+// tile (128 accumulator registers).
 constexpr int kWM = 4, kWN = 2;
-#ifndef MOE_GEMM_NSB
-#define MOE_GEMM_NSB 3
-#endif
-constexpr int kStageK = MOE_GEMM_BK;  // K elements per pipeline stage
-constexpr int kNSA = 2;               // LDS ring slots: activation rows (issued one stage ahead)
+constexpr int kStageK = MOE_GEMM_BK;    // K elements per pipeline stage (dense tiles)
 constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU (gfx950)
 
-// LDS ring slots for weight rows (issued NSB - 1 stages ahead): MOE_GEMM_NSB
-// where the rings fit in LDS, else 2.
-constexpr int ring_b_slots(int a_stage_bytes, int b_stage_bytes) {
-  return kNSA * a_stage_bytes + MOE_GEMM_NSB * b_stage_bytes <= kLdsBytes ? MOE_GEMM_NSB : 2;
+// LDS ring slots.  A slot is refilled at the barrier that ends the reads of
+// the stage it held, so a ring of n slots issues its rows n - 1 stages ahead.
+// The leads are set in K elements: weight rows stream from HBM and get twice
+// the activation rows' lead; the weight ring gives up slots (down to the
+// activation ring's count) where LDS would not hold it.
+#ifndef MOE_GEMM_LEAD_A
+#define MOE_GEMM_LEAD_A 64
+#endif
+#ifndef MOE_GEMM_LEAD_B
+#define MOE_GEMM_LEAD_B 128
+#endif
+constexpr int ring_a_slots(int bk) { return 1 + MOE_GEMM_LEAD_A / bk; }
+constexpr int ring_b_slots(int bk, int a_stage_bytes, int b_stage_bytes) {
+  int n = 1 + MOE_GEMM_LEAD_B / bk;
+  while (n > ring_a_slots(bk) && ring_a_slots(bk) * a_stage_bytes + n * b_stage_bytes > kLdsBytes) --n;
+  return n;
+}
+// LDS bytes of both rings for a BM-row tile with brows weight rows per stage.
+constexpr int ring_bytes(int bm, int brows, int bk) {
+  return ring_a_slots(bk) * bm * bk * 2 + ring_b_slots(bk, bm * bk * 2, brows * bk * 2) * brows * bk * 2;
 }
 
-// Largest divisor of fm that is at most fit (the 32-row blocks per row group
-// of one epilogue band).
-constexpr int band_blocks(int fm, int fit) {
-  int b = fit < fm ? fit : fm;
-  while (b > 1 && fm % b != 0) --b;
-  return b;
-}
 
 // Row of the tile held by 32-row MFMA block fm of a wave in row group wm:
 // blocks are dealt to the WM row groups in turn, so that a partly filled
@@ -97,7 +105,8 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
                                        f32x16_t (&acc)[NB][FM][FN]) {
   constexpr int RB = BK * 2;  // bytes of one row of a stage
   constexpr int BROWS = NB * BN;
-  constexpr int NSA = kNSA, NSB = ring_b_slots(BM * RB, BROWS * RB);  // ring slots
+  constexpr int NSA = ring_a_slots(BK), NSB = ring_b_slots(BK, BM * RB, BROWS * RB);  // ring slots
+  static_assert(NSA >= 2 && NSB >= NSA, "ring depths");
   constexpr int WTN = BN / WN;
   constexpr int KS = BK / 16;  // 16-wide K sub-steps per stage
   static_assert(KS >= 2, "fragment reads alternate between two register sets");
@@ -169,20 +178,24 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
   };
 
   // Ring protocol: a slot is refilled as soon as the barrier after its last
-  // reads has passed.  At the barrier that ends stage kt's reads, A(kt+2)
-  // goes to A slot kt % 2 and B(kt+NSB) to B slot kt % NSB: activation rows
-  // get a whole stage to arrive and weight rows NSB - 1 stages.
-  static_assert(NSB >= 2 && (NSB - 1) * BI + AI < 64, "B ring depth and vmcnt range");
-  // loads that may still be in flight once A(kt+1) and B(kt+1) have landed:
-  // B(kt+NSB-1), issued after A(kt+1), unless that is B(kt+1) itself
-  constexpr int VM_STAGE = NSB >= 3 ? BI : 0;
-  issue_a(0);
+  // reads has passed.  At the barrier that ends stage kt's reads, A(kt+NSA)
+  // goes to A slot kt % NSA and B(kt+NSB) to B slot kt % NSB.  The prologue
+  // issues in the same order, as if the barriers of stages -NSB .. -1 had run.
+  // Loads that may still be in flight once A(s) and B(s) have landed are the
+  // ones issued after A(s): B(s-NSA+NSB) at the same barrier (unless NSB ==
+  // NSA, when that is B(s) itself) and the NSA - 1 (prologue) or NSA - 2
+  // (loop) later barriers' loads.
+  constexpr int VM_AFTER = NSB > NSA ? BI : 0;
+  constexpr int VM_FIRST = VM_AFTER + (NSA - 1) * (AI + BI);
+  constexpr int VM_STAGE = VM_AFTER + (NSA - 2) * (AI + BI);
+  static_assert(VM_FIRST < 64, "vmcnt range");
 #pragma unroll
-  for (int j = 0; j < NSB - 1; ++j) issue_b(j);
-  issue_a(1);
-  issue_b(NSB - 1);
-  // A(0) and B(0) have landed; B(1 .. NSB-1) and A(1) may be in flight
-  asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm((NSB - 1) * BI + AI, 15)) : "memory");
+  for (int v = -NSB; v < 0; ++v) {
+    if (v + NSA >= 0) issue_a(v + NSA);
+    issue_b(v + NSB);
+  }
+  // A(0) and B(0) have landed
+  asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_FIRST, 15)) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   frag_a_t af[2];
@@ -197,13 +210,12 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
         interleave(ks);
       }
     }
-    // A(kt+1) and B(kt+1) have landed (B(kt+NSB-1), issued after A(kt+1),
-    // may still be in flight) and this wave's reads of stage kt are done,
-    // before any wave refills a slot
+    // A(kt+1) and B(kt+1) have landed and this wave's reads of stage kt are
+    // done, before any wave refills a slot
     asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_STAGE, 0)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue_a(kt + 2);
+    issue_a(kt + NSA);
     issue_b(kt + NSB);
     if constexpr (FML > 0) {
       // past the last stage this reads the repeated stage, and is not used
@@ -336,19 +348,20 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
   // row, then copied out by all threads in 16-byte chunks of whole rows.
   constexpr int ESZ = (EPI == kEpiF32) ? 4 : 2;  // bytes per output element
   constexpr int CS = BN * ESZ + 16;              // LDS row stride of the staged tile (padded against bank conflicts)
-  constexpr int LDS_BYTES = kNSA * BM * RB + ring_b_slots(BM * RB, BROWS * RB) * BROWS * RB;
+  constexpr int LDS_BYTES = ring_bytes(BM, BROWS, BK);
   constexpr int FMP_FIT = LDS_BYTES / CS / (WM * 32);  // 32-row blocks per row group that fit at once
-  constexpr int FMP = band_blocks(FM, FMP_FIT);
-  static_assert(FMP >= 1 && FM % FMP == 0, "epilogue bands");
+  constexpr int FMP = FMP_FIT < FM ? FMP_FIT : FM;  // (the last band may hold fewer)
+  constexpr int NBANDS = (FM + FMP - 1) / FMP;
+  static_assert(FMP >= 1, "epilogue bands");
   constexpr int BAND = FMP * WM * 32;         // tile rows per band
   constexpr int CPR = BN * ESZ / 16;          // 16-byte chunks per staged row
   constexpr int EPC = 16 / ESZ;               // elements per chunk
   const bool vec_ok = ((args.ldc * ESZ) % 16 == 0) && (reinterpret_cast<uintptr_t>(cbase) % 16 == 0);
   __syncthreads();  // every wave is done with the K loop's LDS
 #pragma unroll
-  for (int band = 0; band < FM / FMP; ++band) {
+  for (int band = 0; band < NBANDS; ++band) {
 #pragma unroll
-    for (int fm = band * FMP; fm < (band + 1) * FMP; ++fm) {
+    for (int fm = band * FMP; fm < (band + 1) * FMP && fm < FM; ++fm) {
       if (fm >= fm_live) continue;  // wave-uniform
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -391,7 +404,7 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
         }
       }
     }
-    if (band + 1 < FM / FMP) __syncthreads();  // the next band reuses the LDS
+    if (band + 1 < NBANDS) __syncthreads();  // the next band reuses the LDS
   }
 }
 
@@ -400,8 +413,7 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
 template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args) {
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
-  constexpr int RB = BK * 2;
-  constexpr int LDS_BYTES = kNSA * BM * RB + ring_b_slots(BM * RB, NB * BN * RB) * NB * BN * RB;
+  constexpr int LDS_BYTES = ring_bytes(BM, NB * BN, BK);
   static_assert(LDS_BYTES <= kLdsBytes, "LDS rings");
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const int n_blocks = (args.N + BN - 1) / BN;
@@ -434,7 +446,7 @@ hipError_t run(const GemmArgs& a, hipStream_t stream) {
 // Routed tiles: 320 rows on a 2 x 4 wave grid (five 32-row blocks per row
 // group), so that an expert segment of up to 320 rows (DeepSeek-V3 routing
 // gives 200-320 per expert) is one tile and its weights pass through LDS once.
-constexpr int kRoutedBM = 320, kRoutedWM = 2, kRoutedWN = 4;
+constexpr int kRoutedBM = 320, kRoutedWM = 2, kRoutedWN = 4, kRoutedBK = kStageK;
 
 int gemm_routed_bm() { return kRoutedBM; }
 
@@ -453,13 +465,13 @@ hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t stream) {
   if (static_cast<int64_t>(a.N) * a.K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   switch (epilogue) {
     case kEpiSwiGLU:
-      return routed ? run<kRoutedBM, 128, kRoutedWM, kRoutedWN, kEpiSwiGLU, true>(a, stream)
+      return routed ? run<kRoutedBM, 128, kRoutedWM, kRoutedWN, kEpiSwiGLU, true, kRoutedBK>(a, stream)
                     : run<256, 128, kWM, kWN, kEpiSwiGLU, false>(a, stream);
     case kEpiBF16:
-      return routed ? run<kRoutedBM, 256, kRoutedWM, kRoutedWN, kEpiBF16, true>(a, stream)
+      return routed ? run<kRoutedBM, 256, kRoutedWM, kRoutedWN, kEpiBF16, true, kRoutedBK>(a, stream)
                     : run<256, 256, kWM, kWN, kEpiBF16, false>(a, stream);
     case kEpiF32:
-      return routed ? run<kRoutedBM, 256, kRoutedWM, kRoutedWN, kEpiF32, true>(a, stream)
+      return routed ? run<kRoutedBM, 256, kRoutedWM, kRoutedWN, kEpiF32, true, kRoutedBK>(a, stream)
                     : ((a.N <= 256 || a.k_splits > 1) ? run<128, 128, kWM, kWN, kEpiF32, false>(a, stream)
                                   : run<256, 256, kWM, kWN, kEpiF32, false>(a, stream));
     default:
