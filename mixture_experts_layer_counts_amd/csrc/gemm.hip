@@ -446,9 +446,19 @@ hipError_t run(const GemmArgs& a, hipStream_t stream) {
 // Routed tiles: 320 rows on a 2 x 4 wave grid (five 32-row blocks per row
 // group), so that an expert segment of up to 320 rows (DeepSeek-V3 routing
 // gives 200-320 per expert) is one tile and its weights pass through LDS once.
-constexpr int kRoutedBM = 320, kRoutedWM = 2, kRoutedWN = 4, kRoutedBK = kStageK;
+// They pay off when segments commonly exceed 256 rows (192 or more per expert
+// on average) and a minibatch gives at least half as many up/gate work items
+// as there are CUs.  Otherwise 256-row tiles are faster: their weight ring is
+// a stage deeper, each loads fewer activation rows, and a small minibatch
+// splits into more of them.
+constexpr int kRoutedBM = 320, kRoutedWM = 2, kRoutedWN = 4;
+constexpr int kSmallBM = 256;
 
-int gemm_routed_bm() { return kRoutedBM; }
+int gemm_routed_bm(int64_t mb_rows, int64_t max_rows, int64_t experts, int64_t n_up) {
+  const bool big_segments = max_rows >= 192 * (experts > 0 ? experts : 1);
+  const int64_t items = mb_rows / kRoutedBM * ((n_up + 127) / 128);  // up/gate tiles are 128 columns wide
+  return big_segments && items >= 128 ? kRoutedBM : kSmallBM;
+}
 
 int gemm_tiles_bound(int64_t rows, int groups, int bm) {
   // every group (expert segment) adds at most one partial tile
@@ -463,17 +473,22 @@ hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t stream) {
   // buffer resources address at most 2^31 bytes per operand here
   if (a.a_bytes <= 0 || a.a_bytes >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   if (static_cast<int64_t>(a.N) * a.K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (routed && a.tile_rows != kRoutedBM && a.tile_rows != kSmallBM) return hipErrorInvalidValue;
+  const bool big = routed && a.tile_rows == kRoutedBM;
   switch (epilogue) {
     case kEpiSwiGLU:
-      return routed ? run<kRoutedBM, 128, kRoutedWM, kRoutedWN, kEpiSwiGLU, true, kRoutedBK>(a, stream)
-                    : run<256, 128, kWM, kWN, kEpiSwiGLU, false>(a, stream);
+      return big      ? run<kRoutedBM, 128, kRoutedWM, kRoutedWN, kEpiSwiGLU, true>(a, stream)
+             : routed ? run<kSmallBM, 128, kWM, kWN, kEpiSwiGLU, true>(a, stream)
+                      : run<256, 128, kWM, kWN, kEpiSwiGLU, false>(a, stream);
     case kEpiBF16:
-      return routed ? run<kRoutedBM, 256, kRoutedWM, kRoutedWN, kEpiBF16, true, kRoutedBK>(a, stream)
-                    : run<256, 256, kWM, kWN, kEpiBF16, false>(a, stream);
+      return big      ? run<kRoutedBM, 256, kRoutedWM, kRoutedWN, kEpiBF16, true>(a, stream)
+             : routed ? run<kSmallBM, 256, kWM, kWN, kEpiBF16, true>(a, stream)
+                      : run<256, 256, kWM, kWN, kEpiBF16, false>(a, stream);
     case kEpiF32:
-      return routed ? run<kRoutedBM, 256, kRoutedWM, kRoutedWN, kEpiF32, true, kRoutedBK>(a, stream)
-                    : ((a.N <= 256 || a.k_splits > 1) ? run<128, 128, kWM, kWN, kEpiF32, false>(a, stream)
-                                  : run<256, 256, kWM, kWN, kEpiF32, false>(a, stream));
+      return big      ? run<kRoutedBM, 256, kRoutedWM, kRoutedWN, kEpiF32, true>(a, stream)
+             : routed ? run<kSmallBM, 256, kWM, kWN, kEpiF32, true>(a, stream)
+             : (a.N <= 256 || a.k_splits > 1) ? run<128, 128, kWM, kWN, kEpiF32, false>(a, stream)
+                                              : run<256, 256, kWM, kWN, kEpiF32, false>(a, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -54,6 +54,7 @@ struct GemmArgs {
   int64_t c_sub;
   const int4* tiles;         // routed: {expert, p0, rows, 0}; NULL: dense rows 0..dense_rows-1
   const int32_t* tile_count;  // routed: number of valid tiles
+  int tile_rows;              // routed: the height the tile lists were built with (gemm_routed_bm)
   int dense_rows;
   int max_tiles;
   int k_splits;            // dense only: K is cut into this many equal ranges, one output plane each
@@ -90,8 +91,10 @@ hipError_t launch_gemm_mx(const MxGemmArgs& args, int epilogue, hipStream_t stre
 // Tile rows of the routed MXFP8 GEMM kernels (their tile lists are built with it).
 int gemm_mx_routed_bm();
 
-// Tile rows of the routed bf16 GEMM kernels (their tile lists are built with it).
-int gemm_routed_bm();
+// Tile rows of the routed bf16 GEMM kernels for minibatches of mb_rows rows,
+// max_rows routed rows in all over `experts` local experts, and up/gate
+// outputs n_up wide (the tile lists are built with it).
+int gemm_routed_bm(int64_t mb_rows, int64_t max_rows, int64_t experts, int64_t n_up);
 hipError_t launch_gemm(const GemmArgs& args, int epilogue, hipStream_t stream);
 int gemm_tiles_bound(int64_t rows, int groups, int bm);
 

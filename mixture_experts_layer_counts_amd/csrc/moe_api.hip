@@ -21,6 +21,7 @@ struct Layout {
   int router_splits;
   int64_t n_minibatches;
   int max_tiles;
+  int routed_bm;  // tile height of the routed GEMMs' tile lists
   int64_t y_rows;
 };
 
@@ -66,10 +67,11 @@ Layout layout_of(const moe_shape* s) {
   Layout L{};
   L.router_splits = router_splits(s);
   const int64_t R = s->num_src_ranks, NK = s->T * s->k, Lx = s->experts_per_rank;
-  const int bm = s->precision == MOE_MXFP8 ? moe::gemm_mx_routed_bm() : moe::gemm_routed_bm();
+  const int64_t mb_rows = std::min<int64_t>(s->minibatch_rows, std::max<int64_t>(s->max_rows, 1));
+  const int bm = s->precision == MOE_MXFP8 ? moe::gemm_mx_routed_bm() : moe::gemm_routed_bm(mb_rows, s->max_rows, Lx, s->I);
+  L.routed_bm = bm;
   L.n_minibatches = s->max_rows > 0 ? (s->max_rows + s->minibatch_rows - 1) / s->minibatch_rows : 0;
-  L.max_tiles = moe::gemm_tiles_bound(std::min<int64_t>(s->minibatch_rows, std::max<int64_t>(s->max_rows, 1)),
-                                      static_cast<int>(Lx), bm);
+  L.max_tiles = moe::gemm_tiles_bound(mb_rows, static_cast<int>(Lx), bm);
   L.y_rows = (R == 1) ? NK : s->max_rows;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -341,7 +343,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
   float* sh_out = at<float>(ws, L.shared_out);
   int4* tiles = at<int4>(ws, L.tiles);
   int32_t* tile_count = at<int32_t>(ws, L.tile_count);
-  const int bm = mx ? moe::gemm_mx_routed_bm() : moe::gemm_routed_bm();
+  const int bm = L.routed_bm;
 
   // 1. tile lists of every minibatch, from the device-side expert offsets
   {
@@ -428,6 +430,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     u.tiles = tiles + m * L.max_tiles;
     u.tile_count = tile_count + m;
     u.max_tiles = L.max_tiles;
+    u.tile_rows = L.routed_bm;
     {
       ProbeScope probe(MOE_K_UP_GATE, s);
       MOE_TRY_HIP(moe::launch_gemm(u, moe::kEpiSwiGLU, s));
@@ -450,6 +453,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     d.tiles = tiles + m * L.max_tiles;
     d.tile_count = tile_count + m;
     d.max_tiles = L.max_tiles;
+    d.tile_rows = L.routed_bm;
     ProbeScope probe(MOE_K_DOWN, s);
     MOE_TRY_HIP(moe::launch_gemm(d, moe::kEpiBF16, s));
   }

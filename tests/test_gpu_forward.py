@@ -25,7 +25,13 @@ CASES = [
      [(None, None), (100, 300), (256, 512)]),
     ("skewed", synth.Workload("skewed", T=257, D=192, I=128, E=24, k=6, I_shared=320, seed=8, routing="zipf"),
      [(None, None), (200, 400)]),
-    ("mid", synth.workload("mid", routing="gaussian"), [(4096, 8192)]),
+    # 4096-row minibatches take 256-row routed tiles, all rows at once 320-row
+    # tiles (>= 192 rows per expert and >= 128 up/gate work items)
+    ("mid", synth.workload("mid", routing="gaussian"), [(4096, 8192), (None, None)]),
+    # 320-row tiles with Zipf routing: experts of one to four such tiles and
+    # of a few rows, in one minibatch and in two
+    ("skewed320", synth.Workload("skewed320", T=1024, D=256, I=1024, E=24, k=6, I_shared=128, seed=9,
+                                 routing="zipf"), [(None, None), (5120, 5120)]),
     # limits: the most routes per token, the most experts, a single token
     ("k16", synth.Workload("k16", T=33, D=128, I=64, E=64, k=16, I_shared=64, seed=14, routing="gaussian"),
      [(None, None), (64, 128)]),
