@@ -23,8 +23,8 @@
 //
 // Work order (routed).  The 256 MI355X CUs sit in 8 XCDs, each with its own
 // L2, and workgroups are dealt to XCDs round-robin.  Work items are ordered
-// expert-major, then by N block, then by row tile, and workgroup b runs item
-// (b mod 8) * ceil(W/8) + b / 8: each XCD walks a contiguous run of items, so
+// expert-major, then by N block, then by row tile, and cut into 8 contiguous
+// runs, one per XCD, whose resident workgroups walk it side by side: so
 // the N-block tiles of one expert (which share the same activation rows) and
 // the row tiles of one (expert, N block) (which share the same weight rows)
 // run side by side on one XCD and meet in its L2, while every weight byte is
@@ -37,6 +37,9 @@
 // optionally scattered to the row of the route it came from, reusing the
 // schedule table as in §3.1) and fp32 store (shared expert output, router
 // logits).
+
+#include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "gemm_common.h"
@@ -230,7 +233,7 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
 // One work item (row tile, N block, K range) of the GEMM: its K loop and its
 // epilogue.  The workgroup's LDS is free on entry and on return.
 template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK>
-__device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blocks, int S, char* smem) {
+__device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blocks, int S, char* smem, int wave0) {
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;  // B halves (gate, up)
   constexpr int BROWS = NB * BN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -241,18 +244,21 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
   constexpr int AI = BM / (NW * ROWS_PER_LD), BI = BROWS / (NW * ROWS_PER_LD);  // per wave per stage
   static_assert(FM >= 1 && FN >= 1 && AI * NW * ROWS_PER_LD == BM && BI * NW * ROWS_PER_LD == BROWS, "tile shape");
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  constexpr bool kItemLoop = EPI == kEpiBF16 && ROUTED;  // resident workgroups walk several items
+  const int tid = kItemLoop ? item_thread_index(wave0) : static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1), wave = kItemLoop ? wave0 : __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
 
   int e = 0, nrows, tile, nb, ks = 0;
   int64_t p0;
   if constexpr (ROUTED) {
-    const int4 g = args.tiles[w / n_blocks];  // a tile of the expert group that owns item w
+    // a tile of the expert group that owns item w
+    const int4 g = kItemLoop ? load_uniform(args.tiles + w / n_blocks) : args.tiles[w / n_blocks];
     const int nt = g.x >> 10, first = g.w;
     const int lw = w - first * n_blocks;
     nb = lw / nt;
     tile = first + lw % nt;
-    const int4 t = args.tiles[tile];
+    const int4 t = kItemLoop ? load_uniform(args.tiles + tile) : args.tiles[tile];
     e = t.x & 1023;
     p0 = t.y;
     nrows = t.z;
@@ -357,6 +363,20 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
   constexpr int CPR = BN * ESZ / 16;          // 16-byte chunks per staged row
   constexpr int EPC = 16 / ESZ;               // elements per chunk
   const bool vec_ok = ((args.ldc * ESZ) % 16 == 0) && (reinterpret_cast<uintptr_t>(cbase) % 16 == 0);
+  // Copy-out mapping: in pass `it` of a band, wave w stores tile rows
+  // it * RSTEP + w * RPI + lane / CPR, 16 bytes per lane.  Where output rows
+  // come from a row table (the scatter of the routed down projection), each
+  // row's entry is read once, before the first store: lane q * RPI + j of
+  // wave w holds the entry of tile row q * RSTEP + w * RPI + j and passes it
+  // on by a cross-lane read.  A table load inside the store loop would make
+  // every pass wait for all earlier stores, since one counter tracks both.
+  constexpr int RPI = 64 / CPR, RSTEP = RPI * NW;
+  static_assert(64 % CPR == 0 && BM <= 64 * NW && BAND % RSTEP == 0, "copy-out mapping");
+  int row_entry = 0;
+  if (args.c_idx) {
+    const int r = (lane / RPI) * RSTEP + wave * RPI + lane % RPI;
+    if (r < nrows) row_entry = args.c_idx[p0 + r];
+  }
   __syncthreads();  // every wave is done with the K loop's LDS
 #pragma unroll
   for (int band = 0; band < NBANDS; ++band) {
@@ -384,12 +404,13 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
     }
     __syncthreads();
     const int band_rows = min(BAND, nrows - band * BAND);
-    for (int idx = tid; idx < band_rows * CPR; idx += 64 * NW) {
-      const int row_b = idx / CPR, ch = idx - row_b * CPR;
+    for (int it = 0; it * RSTEP < band_rows; ++it) {
+      const int row_b = it * RSTEP + wave * RPI + lane / CPR, ch = lane % CPR;
+      const int entry = args.c_idx ? __shfl(row_entry, (band * BAND / RSTEP + it) * RPI + lane / CPR) : 0;
       const int col = n0 + ch * EPC;
-      if (col >= args.N) continue;
+      if (row_b >= band_rows || col >= args.N) continue;
       const int64_t p = p0 + band * BAND + row_b;
-      const int64_t crow = args.c_idx ? static_cast<int64_t>(args.c_idx[p]) : p - args.c_sub;
+      const int64_t crow = args.c_idx ? static_cast<int64_t>(entry) : p - args.c_sub;
       const char* src_l = smem + row_b * CS + ch * 16;
       char* dst = cbase + (crow * args.ldc + col) * ESZ;
       if (vec_ok && col + EPC <= args.N) {
@@ -408,8 +429,15 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
   }
 }
 
-// One work item per workgroup: workgroup b runs item (b mod 8) * ceil(W/8) +
-// b / 8, so each XCD walks a contiguous run of items.
+// Work items are split into 8 contiguous runs, one per XCD (workgroups are
+// dealt to XCDs round-robin, so workgroup b sits on XCD b mod 8), and
+// workgroup b takes item b / 8 of its XCD's run.  The routed down projection
+// launches only as many workgroups as fit on the chip at once, and workgroup
+// b walks items b / 8, b / 8 + G, b / 8 + 2G, ... of its run (G = workgroups
+// per XCD), so the XCD's workgroups still move through the run side by side:
+// a workgroup that stays resident overlaps one item's output stores with the
+// next item's first loads, where a fresh workgroup would first wait for the
+// stores to drain and then for its loads.
 template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args) {
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
@@ -421,11 +449,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args)
   const int S = ROUTED ? 1 : args.k_splits;  // K ranges (dense only), each with its own output plane
   const int W = tcount * n_blocks * S;
   const int chunk = (W + kXcds - 1) / kXcds;
-  const int local = static_cast<int>(blockIdx.x) / kXcds;
-  if (local >= chunk) return;
-  const int w = (static_cast<int>(blockIdx.x) % kXcds) * chunk + local;
-  if (w >= W) return;
-  gemm_item<BM, BN, WM, WN, EPI, ROUTED, BK>(args, w, n_blocks, S, smem);
+  const int run0 = (static_cast<int>(blockIdx.x) % kXcds) * chunk;
+  const int first = static_cast<int>(blockIdx.x) / kXcds;
+  const int wave0 = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  if constexpr (!(EPI == kEpiBF16 && ROUTED)) {
+    if (first < chunk && run0 + first < W)
+      gemm_item<BM, BN, WM, WN, EPI, ROUTED, BK>(args, run0 + first, n_blocks, S, smem, wave0);
+  } else {
+    const int per_xcd = static_cast<int>(gridDim.x) / kXcds;  // the grid is a multiple of kXcds
+    for (int local = first; local < chunk && run0 + local < W; local += per_xcd) {
+      // the previous item's copy-out has read the LDS before this item's loads refill it
+      if (local > first) __syncthreads();
+      gemm_item<BM, BN, WM, WN, EPI, ROUTED, BK>(args, __builtin_amdgcn_readfirstlane(run0 + local), n_blocks, S,
+                                                 smem, wave0);
+    }
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK = kStageK>
@@ -436,7 +474,22 @@ hipError_t run(const GemmArgs& a, hipStream_t stream) {
   if (work <= 0) return hipSuccess;
   if (work > 0x7ffffff0) return hipErrorInvalidValue;
   auto kernel = gemm_kernel<BM, BN, WM, WN, EPI, ROUTED, BK>;
-  const int64_t grid = (work + kXcds - 1) / kXcds * kXcds;
+  // Resident workgroups walk several items only for the routed down
+  // projection, whose items end in large output stores (a 320 x 256 bf16
+  // tile after 32 K stages); elsewhere one item per workgroup measured as
+  // fast or faster.
+  int64_t cap = work;
+  if (EPI == kEpiBF16 && ROUTED) {
+    static std::atomic<int64_t> resident_cache{0};
+    int64_t resident = resident_cache.load(std::memory_order_relaxed);
+    if (resident <= 0) {
+      resident = resident_workgroups(reinterpret_cast<const void*>(kernel), 64 * WM * WN);
+      if (resident <= 0) return hipErrorInvalidValue;
+      resident_cache.store(resident, std::memory_order_relaxed);
+    }
+    cap = std::min(work, resident);
+  }
+  const int64_t grid = (cap + kXcds - 1) / kXcds * kXcds;
   kernel<<<static_cast<unsigned>(grid), 64 * WM * WN, 0, stream>>>(a);
   return hipGetLastError();
 }

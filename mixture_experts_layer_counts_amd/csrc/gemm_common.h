@@ -32,6 +32,38 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, ui
                                            0);
 }
 
+// A work-item descriptor, read through the scalar cache (the wait is in the
+// same statement): its address is the same for every lane, and a scalar read
+// does not wait behind the previous item's output stores, which the vector
+// memory counter still holds.
+__device__ __forceinline__ int4 load_uniform(const int4* p) {
+  int4 v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+// Thread index within the workgroup, rebuilt per work item from the wave
+// index (uniform, held in a scalar register) and the lane's position in the
+// wave: a workgroup that runs several items would otherwise keep lane-derived
+// offsets of the item body live across the item loop, and the accumulator
+// tiles leave no vector registers for that.
+__device__ __forceinline__ int item_thread_index(int wave) {
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  return wave * 64 + lane;
+}
+
+// Workgroups of `kernel` (launched with `block` threads) that fit on the
+// current device at once: compute units times the occupancy per unit.  The
+// result is kept per call site by the caller; 0 when the runtime cannot say.
+inline int64_t resident_workgroups(const void* kernel, int block) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
+  return static_cast<int64_t>(cus) * per_cu;
+}
+
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= lgkm, expcnt untouched.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8); }
 

@@ -32,6 +32,9 @@
 // quantises one 32-column block of a row), and bf16 for the down projection,
 // scattered to the row of the route it came from.
 
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
@@ -234,7 +237,7 @@ __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const ui
 // One work item (row tile, N block): its K loop and its epilogue.  The
 // workgroup's LDS is free on entry and on return.
 template <int BN, int EPI>
-__device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int n_blocks, char* smem) {
+__device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int n_blocks, char* smem, int wave0) {
   constexpr int BM = kMxBM;
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
   constexpr int BROWS = NB * BN;
@@ -244,14 +247,16 @@ __device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int 
   constexpr int AI = BM / (kNW * ROWS_PER_LD), BI = BROWS / (kNW * ROWS_PER_LD);
   constexpr int LDS_BYTES = kNSA * BM * kRB + kNSB * BROWS * kRB;
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  constexpr bool kItemLoop = EPI == kEpiBF16;  // resident workgroups walk several items
+  const int tid = kItemLoop ? item_thread_index(wave0) : static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1), wave = kItemLoop ? wave0 : __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / kWN, wn = wave % kWN;
 
-  const int4 g = args.tiles[w / n_blocks];
+  const int4 g = kItemLoop ? load_uniform(args.tiles + w / n_blocks) : args.tiles[w / n_blocks];
   const int nt = g.x >> 10, first = g.w;
   const int lw = w - first * n_blocks;
   const int nb = lw / nt;
-  const int4 t = args.tiles[first + lw % nt];
+  const int4 t = kItemLoop ? load_uniform(args.tiles + first + lw % nt) : args.tiles[first + lw % nt];
   const int e = t.x & 1023;
   const int64_t p0 = t.y;
   const int nrows = t.z;
@@ -402,6 +407,18 @@ __device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int 
     constexpr int CS = BN * 2 + 16;  // bf16 row stride of the staged tile
     static_assert(BM * CS <= LDS_BYTES, "staged tile fits");
     constexpr int CPR = BN * 2 / 16;
+    // Copy-out mapping: in pass `it`, wave w stores tile rows it * RSTEP +
+    // w * RPI + lane / CPR.  A row table's entries are read once, before
+    // any store (lane q * RPI + j of wave w holds tile row q * RSTEP + w *
+    // RPI + j) and passed on by a cross-lane read: a table load inside the
+    // store loop would wait for all earlier stores (one counter tracks both).
+    constexpr int RPI = 64 / CPR, RSTEP = RPI * kNW;
+    static_assert(64 % CPR == 0 && BM <= 64 * kNW, "copy-out mapping");
+    int row_entry = 0;
+    if (args.c_idx) {
+      const int r = (lane / RPI) * RSTEP + wave * RPI + lane % RPI;
+      if (r < nrows) row_entry = args.c_idx[p0 + r];
+    }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       if (fm >= fm_live) continue;  // wave-uniform
@@ -416,20 +433,25 @@ __device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int 
       }
     }
     __syncthreads();
-    for (int idx = tid; idx < nrows * CPR; idx += 64 * kNW) {
-      const int row = idx / CPR, ch = idx - row * CPR;
+    for (int it = 0; it * RSTEP < nrows; ++it) {
+      const int row = it * RSTEP + wave * RPI + lane / CPR, ch = lane % CPR;
+      const int entry = args.c_idx ? __shfl(row_entry, it * RPI + lane / CPR) : 0;
       const int col = n0 + ch * 8;
-      if (col >= args.N) continue;  // N % 32 == 0: a chunk is all in or out
+      if (row >= nrows || col >= args.N) continue;  // N % 32 == 0: a chunk is all in or out
       const int64_t p = p0 + row;
-      const int64_t crow = args.c_idx ? static_cast<int64_t>(args.c_idx[p]) : p - args.c_sub;
+      const int64_t crow = args.c_idx ? static_cast<int64_t>(entry) : p - args.c_sub;
       *reinterpret_cast<u32x4_t*>(static_cast<char*>(args.C) + (crow * args.ldc + col) * 2) =
           *reinterpret_cast<const u32x4_t*>(smem + row * CS + ch * 16);
     }
   }
 }
 
-// One work item per workgroup: workgroup b runs item (b mod 8) * ceil(W/8) +
-// b / 8, so each XCD walks a contiguous run of items.
+// Work items are cut into 8 contiguous runs, one per XCD, and workgroup b
+// takes item b / 8 of the run of XCD b mod 8.  The down projection launches
+// only as many workgroups as fit on the chip at once, and they walk their
+// XCD's run side by side (workgroup b takes items b / 8, b / 8 + G, ... with G
+// workgroups per XCD), so that one item's output stores drain under the next
+// item's first loads.
 template <int BN, int EPI>
 __global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args) {
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
@@ -437,11 +459,19 @@ __global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args
   const int n_blocks = (args.N + BN - 1) / BN;
   const int W = *args.tile_count * n_blocks;
   const int chunk = (W + kXcds - 1) / kXcds;
-  const int local = static_cast<int>(blockIdx.x) / kXcds;
-  if (local >= chunk) return;
-  const int w = (static_cast<int>(blockIdx.x) % kXcds) * chunk + local;
-  if (w >= W) return;
-  gemm_mx_item<BN, EPI>(args, w, n_blocks, smem);
+  const int run0 = (static_cast<int>(blockIdx.x) % kXcds) * chunk;
+  const int first = static_cast<int>(blockIdx.x) / kXcds;
+  const int wave0 = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  if constexpr (EPI != kEpiBF16) {
+    if (first < chunk && run0 + first < W) gemm_mx_item<BN, EPI>(args, run0 + first, n_blocks, smem, wave0);
+  } else {
+    const int per_xcd = static_cast<int>(gridDim.x) / kXcds;  // the grid is a multiple of kXcds
+    for (int local = first; local < chunk && run0 + local < W; local += per_xcd) {
+      // the previous item's copy-out has read the LDS before this item's loads refill it
+      if (local > first) __syncthreads();
+      gemm_mx_item<BN, EPI>(args, __builtin_amdgcn_readfirstlane(run0 + local), n_blocks, smem, wave0);
+    }
+  }
 }
 
 template <int BN, int EPI>
@@ -451,7 +481,21 @@ hipError_t run_mx(const MxGemmArgs& a, hipStream_t stream) {
   if (work <= 0) return hipSuccess;
   if (work > 0x7ffffff0) return hipErrorInvalidValue;
   auto kernel = gemm_mx_kernel<BN, EPI>;
-  const int64_t grid = (work + kXcds - 1) / kXcds * kXcds;
+  // resident workgroups walk several items only for the down projection,
+  // whose items end in large output stores; the up/gate items measured faster
+  // one per workgroup
+  int64_t cap = work;
+  if (EPI == kEpiBF16) {
+    static std::atomic<int64_t> resident_cache{0};
+    int64_t resident = resident_cache.load(std::memory_order_relaxed);
+    if (resident <= 0) {
+      resident = resident_workgroups(reinterpret_cast<const void*>(kernel), 64 * kNW);
+      if (resident <= 0) return hipErrorInvalidValue;
+      resident_cache.store(resident, std::memory_order_relaxed);
+    }
+    cap = std::min(work, resident);
+  }
+  const int64_t grid = (cap + kXcds - 1) / kXcds * kXcds;
   kernel<<<static_cast<unsigned>(grid), 64 * kNW, 0, stream>>>(a);
   return hipGetLastError();
 }

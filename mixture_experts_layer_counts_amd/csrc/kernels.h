@@ -15,9 +15,10 @@ struct SchedScratch {
 
 int sched_chunks(int NK);
 
-// Top-k and gates from `parts` fp32 planes [T, E] (stride part_stride
-// elements), summed in plane order; with parts > 1 the sums are written to
-// `logits`.
+// Top-k and gates from `parts` (1 .. kMaxRouterParts) fp32 planes [T, E]
+// (stride part_stride elements), summed in plane order; with parts > 1 the
+// sums are written to `logits`.
+constexpr int kMaxRouterParts = 4;
 hipError_t launch_topk_gate(const float* planes, int parts, int64_t part_stride, float* logits, int T, int E, int k,
                             int32_t* idx, float* gate, int* err, hipStream_t stream);
 

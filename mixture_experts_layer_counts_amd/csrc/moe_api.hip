@@ -59,7 +59,7 @@ int router_splits(const moe_shape* s) {
   const int64_t tiles = ((s->T + 127) / 128) * ((s->E_total + 127) / 128);
   const int64_t stages = s->D / 64;
   int S = 1;
-  while (S < 4 && tiles * S < 512 && stages % (2 * S) == 0) S *= 2;
+  while (2 * S <= moe::kMaxRouterParts && tiles * S < 512 && stages % (2 * S) == 0) S *= 2;
   return S;
 }
 

@@ -16,6 +16,38 @@
 
 namespace moe {
 
+constexpr int kNoExpert = 0x7fffffff;  // id of an empty candidate
+
+// (bv, bi) meets another lane's pair and keeps the larger under the order
+// (value desc, id asc).
+__device__ __forceinline__ void argmax_meet(float& bv, int& bi, float ov, int oi) {
+  const bool take = ov > bv || (ov == bv && oi < bi);
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
+}
+
+// One step against the lane that the DPP control CTRL maps to this lane.
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& bv, int& bi) {
+  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xF, 0xF, false);
+  argmax_meet(bv, bi, ov, oi);
+}
+
+// Wave-wide arg-max; every lane ends with the result.  Within a 16-lane row
+// the partners come by DPP: lane ^ 1 and lane ^ 2 (quad permutations), then
+// the mirror within 8 lanes and within 16 lanes, each of which pairs lanes
+// from the two halves that already agree; across rows by lane ^ 16 and
+// lane ^ 32 through the LDS crossbar.
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  argmax_dpp<0xB1>(bv, bi);   // quad_perm [1, 0, 3, 2]
+  argmax_dpp<0x4E>(bv, bi);   // quad_perm [2, 3, 0, 1]
+  argmax_dpp<0x141>(bv, bi);  // row_half_mirror
+  argmax_dpp<0x140>(bv, bi);  // row_mirror
+  argmax_meet(bv, bi, __shfl_xor(bv, 16), __shfl_xor(bi, 16));
+  argmax_meet(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
+}
+
 // EPL = logits per lane (ceil(E / 64)), so the row lives in registers.
 // The router GEMM may leave the logits as `parts` partial sums over K ranges
 // (planes part_stride apart); they are added here in plane order, a fixed
@@ -30,6 +62,16 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
   const int lane = lane_id();
   const float* row = planes + static_cast<int64_t>(token) * E;
 
+  // every plane's values are loaded before the first is used, so that the
+  // loads are in flight together
+  float pv[kMaxRouterParts][EPL];
+#pragma unroll
+  for (int pp = 0; pp < kMaxRouterParts; ++pp)
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      const int e = lane + kWave * q;
+      pv[pp][q] = (pp < parts && e < E) ? row[pp * part_stride + e] : 0.f;
+    }
   float v[EPL];
   bool bad = false;
 #pragma unroll
@@ -37,8 +79,10 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
     const int e = lane + kWave * q;
     float x = -INFINITY;
     if (e < E) {
-      x = row[e];
-      for (int pp = 1; pp < parts; ++pp) x += row[pp * part_stride + e];
+      x = pv[0][q];
+#pragma unroll
+      for (int pp = 1; pp < kMaxRouterParts; ++pp)
+        if (pp < parts) x += pv[pp][q];
       if (parts > 1) logits[static_cast<int64_t>(token) * E + e] = x;
       if (!__builtin_isfinite(x)) {
         bad = true;
@@ -49,68 +93,43 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
   }
   if (__any(bad) && lane == 0) raise_error(err, kErrNonFinite);
 
+  // k rounds of a wave-wide arg-max; lane s keeps the id and the unnormalised
+  // gate of slot s, and the gate sum runs in slot order
   uint32_t taken = 0;
-  float sel_v[16];
-  int sel_i[16];
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    sel_v[s] = -INFINITY;
-    sel_i[s] = 0;
-  }
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    if (s >= k) continue;
+  float v0 = 0.f, sum = 0.f, my_z = 0.f;
+  int my_i = 0;
+  for (int s = 0; s < k; ++s) {
     float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    int bi = kNoExpert;
 #pragma unroll
     for (int q = 0; q < EPL; ++q) {
+      // ids rise with q, so an equal value never replaces an earlier candidate
       const int e = lane + kWave * q;
-      if (e < E && !((taken >> q) & 1u)) {
-        if (v[q] > bv || (v[q] == bv && e < bi)) {
-          bv = v[q];
-          bi = e;
-        }
-      }
+      const bool take = e < E && !((taken >> q) & 1u) && (v[q] > bv || bi == kNoExpert);
+      bv = take ? v[q] : bv;
+      bi = take ? e : bi;
     }
-    // wave-wide arg-max under the total order (value desc, id asc)
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_argmax(bv, bi);
     if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-    sel_v[s] = bv;
-    sel_i[s] = bi;
-  }
-
-  // gates: exp(l_s - l_0) / sum_s' exp(l_s' - l_0), summed in slot order
-  float z[16];
-  float sum = 0.f;
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    z[s] = 0.f;
-    if (s < k) {
-      z[s] = expf(sel_v[s] - sel_v[0]);
-      sum += z[s];
+    if (s == 0) v0 = bv;
+    // gates: exp(l_s - l_0) / sum_s' exp(l_s' - l_0)
+    const float z = expf(bv - v0);
+    sum += z;
+    if (lane == s) {
+      my_z = z;
+      my_i = bi;
     }
   }
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    if (s < k && lane == s) {
-      idx[static_cast<int64_t>(token) * k + s] = sel_i[s];
-      gate[static_cast<int64_t>(token) * k + s] = z[s] / sum;
-    }
+  if (lane < k) {
+    idx[static_cast<int64_t>(token) * k + lane] = my_i;
+    gate[static_cast<int64_t>(token) * k + lane] = my_z / sum;
   }
 }
 
 hipError_t launch_topk_gate(const float* planes, int parts, int64_t part_stride, float* logits, int T, int E, int k,
                             int32_t* idx, float* gate, int* err, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  if (parts < 1) return hipErrorInvalidValue;
+  if (parts < 1 || parts > kMaxRouterParts) return hipErrorInvalidValue;
   const dim3 grid((T + 3) / 4), block(256);
   const int epl = (E + kWave - 1) / kWave;
   if (epl <= 1)

@@ -10,10 +10,11 @@
 //   count : per chunk of a source rank's routes, the chunk-local ordinal of
 //           every local route (wave ballots + per-wave counts in LDS, taken in
 //           wave order) and the chunk's per-expert histogram;
-//   scan  : per (r, l) exclusive prefix over chunks -> chunk bases and M[r][l];
-//           counts and expert offsets S_l (block-wide scan);
-//   place : o = chunk base + local ordinal, then the closed form above; writes
-//           the table row and its inverse.
+//   scan  : per (r, l) exclusive prefix over chunks -> chunk bases and M[r][l]
+//           (a few threads per pair, each over a run of chunks); counts and
+//           expert offsets S_l (block-wide scan);
+//   place : o = chunk base + local ordinal, then the closed form above (M
+//           staged in LDS); writes the table row and its inverse.
 
 #include "common.h"
 #include "kernels.h"
@@ -103,22 +104,56 @@ __global__ __launch_bounds__(256) void sched_count_kernel(const int32_t* __restr
 __global__ __launch_bounds__(1024) void sched_scan_kernel(int R, int L, int nch, int NK, int32_t* __restrict__ chunk_cnt,
                                                           int32_t* __restrict__ Mmat, int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets, int64_t max_rows, int* err) {
+  __shared__ int Ms[kMaxExperts];  // M[r][l] (R * L = E_total <= kMaxExperts)
   const int tid = threadIdx.x;
-  for (int pair = tid; pair < R * L; pair += 1024) {
-    const int r = pair / L, l = pair % L;
-    int base = 0;
-    for (int ch = 0; ch < (NK > 0 ? nch : 0); ++ch) {  // no count pass ran when there are no routes
-      const int64_t ix = (static_cast<int64_t>(r) * nch + ch) * L + l;
-      const int cnt = chunk_cnt[ix];
-      chunk_cnt[ix] = base;
-      base += cnt;
+  // G threads (adjacent lanes) share one (r, l) pair, each taking a run of
+  // chunks; the chunk counts of a run are loaded in batches of 8 so that the
+  // loads are in flight together
+  const int pairs = R * L;
+  int G = 1;
+  while (G < 16 && pairs * G * 2 <= 1024) G *= 2;
+  const int pair = tid / G, g = tid % G;
+  const bool active = pair < pairs && NK > 0;  // no count pass ran when there are no routes
+  const int per = (nch + G - 1) / G;
+  const int ch0 = g * per, ch1 = min(nch, ch0 + per);
+  const int64_t row = static_cast<int64_t>(pair / (L > 0 ? L : 1)) * nch;  // first chunk entry of rank r
+  const int l = pair % (L > 0 ? L : 1);
+  auto at = [&](int ch) { return (row + ch) * L + l; };
+  int part = 0;
+  for (int ch = ch0; active && ch < ch1; ch += 8) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ch + i < ch1 ? chunk_cnt[at(ch + i)] : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part += v[i];
+  }
+  // exclusive prefix of the runs' sums over the pair's G threads
+  int incl = part;
+  for (int off = 1; off < G; off <<= 1) {
+    const int y = __shfl_up(incl, off, G);
+    if (g >= off) incl += y;
+  }
+  int base = incl - part;
+  const int pair_total = __shfl(incl, G - 1, G);
+  // chunk counts -> exclusive chunk bases, in chunk order
+  for (int ch = ch0; active && ch < ch1; ch += 8) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ch + i < ch1 ? chunk_cnt[at(ch + i)] : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (ch + i < ch1) chunk_cnt[at(ch + i)] = base;
+      base += v[i];
     }
-    Mmat[pair] = base;
+  }
+  if (pair < pairs && g == 0) {
+    Mmat[pair] = pair_total;
+    Ms[pair] = pair_total;
   }
   __syncthreads();
   int cnt = 0;
   if (tid < L) {
-    for (int r = 0; r < R; ++r) cnt += Mmat[r * L + tid];
+    for (int r = 0; r < R; ++r) cnt += Ms[r * L + tid];
     counts[tid] = cnt;
   }
   int total = 0;
@@ -137,6 +172,9 @@ __global__ __launch_bounds__(256) void sched_place_kernel(const int32_t* __restr
                                                           const int32_t* __restrict__ offsets, int64_t max_rows,
                                                           int32_t* __restrict__ sched_src,
                                                           int32_t* __restrict__ route_dst, int* err) {
+  __shared__ int Ms[kMaxExperts];  // M[r][l] (R * L = E_total <= kMaxExperts)
+  for (int i = threadIdx.x; i < R * L; i += 256) Ms[i] = Mmat[i];
+  __syncthreads();
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (gid >= static_cast<int64_t>(R) * NK) return;
   const int r = static_cast<int>(gid / NK), j = static_cast<int>(gid % NK);
@@ -149,7 +187,7 @@ __global__ __launch_bounds__(256) void sched_place_kernel(const int32_t* __restr
   const int o = chunk_base[(static_cast<int64_t>(r) * nch + j / kSchedChunk) * L + l] + ord_local[gid];
   int p = 0;
   for (int r2 = 0; r2 < R; ++r2) {
-    const int m = Mmat[r2 * L + l];
+    const int m = Ms[r2 * L + l];
     p += m < o ? m : o;
     if (r2 < r && m > o) ++p;
   }
