@@ -414,7 +414,14 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
       const char* src_l = smem + row_b * CS + ch * 16;
       char* dst = cbase + (crow * args.ldc + col) * ESZ;
       if (vec_ok && col + EPC <= args.N) {
-        *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src_l);
+        // the routed down projection's rows are next read by the combine,
+        // long after they leave the caches: non-temporal stores (measured
+        // 3% faster for that kernel)
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src_l);
+        if constexpr (EPI == kEpiBF16 && ROUTED)
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
+        else
+          *reinterpret_cast<u32x4_t*>(dst) = v;
       } else {
         const int n_el = min(EPC, args.N - col);
         for (int e = 0; e < n_el; ++e) {

@@ -440,8 +440,10 @@ __device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int 
       if (row >= nrows || col >= args.N) continue;  // N % 32 == 0: a chunk is all in or out
       const int64_t p = p0 + row;
       const int64_t crow = args.c_idx ? static_cast<int64_t>(entry) : p - args.c_sub;
-      *reinterpret_cast<u32x4_t*>(static_cast<char*>(args.C) + (crow * args.ldc + col) * 2) =
-          *reinterpret_cast<const u32x4_t*>(smem + row * CS + ch * 16);
+      // the rows are next read by the combine, long after they leave the
+      // caches: non-temporal stores
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(smem + row * CS + ch * 16),
+                                  reinterpret_cast<u32x4_t*>(static_cast<char*>(args.C) + (crow * args.ldc + col) * 2));
     }
   }
 }
