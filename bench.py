@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--sweep", default="", metavar="B[:C],...",
                     help="after the main run, time the step at these minibatch sizes b (ring C, default b) and "
                          "report them under 'granularity_sweep'")
+    ap.add_argument("--graph", action="store_true",
+                    help="in the sweep, also time the step captured once in a HIP graph and replayed "
+                         "(launch overhead removed)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy a MIB-MiB buffer 3 times with a plain device copy (a known-size "
                          "reference for hardware byte counters)")
@@ -395,9 +398,32 @@ def sweep(job, args, torch):
         ms = (time.perf_counter() - t0) * 1e3 / n
         if layer.device_error():
             raise RuntimeError(f"device error word {layer.device_error():#x} at b={b} C={C}")
-        out.append({"minibatch_rows": b, "ring_rows": C, "minibatches": (job.P + b - 1) // b,
-                    "ms_per_step": round(ms, 4), "tokens_per_s": round(job.T / (ms * 1e-3), 1)})
-        log(f"sweep b={b} C={C}: {ms:.3f} ms/step")
+        e = {"minibatch_rows": b, "ring_rows": C, "minibatches": (job.P + b - 1) // b,
+             "ms_per_step": round(ms, 4), "tokens_per_s": round(job.T / (ms * 1e-3), 1)}
+        if args.graph:
+            # the same step captured once (the library allocates nothing and
+            # never synchronises, so it can be captured) and replayed
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                g.replay()
+            torch.cuda.synchronize()
+            e["graph_ms_per_step"] = round((time.perf_counter() - t0) * 1e3 / n, 4)
+            if layer.device_error():
+                raise RuntimeError(f"device error word {layer.device_error():#x} at b={b} C={C} (graph)")
+            del g
+        out.append(e)
+        log(f"sweep b={b} C={C}: {ms:.3f} ms/step" + (f", graph {e['graph_ms_per_step']:.3f}" if args.graph else ""))
         del layer, step
         torch.cuda.empty_cache()
     return out
