@@ -171,6 +171,10 @@ moe_status moe_schedule(const moe_shape* shape, const int32_t* routes, int32_t* 
  *   acc = 0; for s in 0..k-1: acc = fma(g[t,s], y[t,s], acc); out32[t] = acc + shared[t]
  * where y[t,s] is the row of route t*k+s, or 0 for a route to a remote expert
  * (R > 1: its row comes back from another rank, outside this library).
+ * The first call in a process asks the runtime for the current device's
+ * compute-unit count and the down kernels' occupancy (host queries only: no
+ * allocation, no synchronisation) and keeps them; the call can be captured in
+ * a HIP graph.
  */
 moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const void* x_src,
                        const void* x_local, const float* topk_gate, const int32_t* expert_offsets,
