@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -89,8 +89,11 @@ typedef struct {
   int64_t max_rows;            /* bound on routed rows P received; T*k when R == 1 */
   int64_t minibatch_rows;      /* b: rows per gather/GEMM step (granularity), >= 1 */
   int64_t ring_rows;           /* C: ring buffer capacity, a positive multiple of b */
-  int32_t precision;           /* moe_precision */
-  int32_t reserved;            /* must be 0 */
+  int32_t precision;           /* moe_precision of the routed experts */
+  int32_t shared_precision;    /* moe_precision of the shared expert: MOE_BF16, as
+                                  the MoK paper keeps it (§3.4, "MXFP8 Support"),
+                                  or MOE_MXFP8 as an option (D and I_shared then
+                                  multiples of 128) */
 } moe_shape;
 
 /* Expert weights, all K-contiguous (each output row is a contiguous K vector):
@@ -98,11 +101,18 @@ typedef struct {
  *           s_gate, s_up [L, D/128, I, 4]; s_down [L, I/128, D, 4]   (E8M0,
  *           MXFP8 only): stage-major scales, as moe_mxfp8_pack_scales writes
  *           them from the row-major [L, N, K/32] of moe_quantize_mxfp8
- *   shared  ws_gate, ws_up [I_shared, D]; ws_down [D, I_shared]   (bf16) */
+ *   shared  ws_gate, ws_up [I_shared, D]; ws_down [D, I_shared]   (bf16, or
+ *           e4m3 when shared_precision is MOE_MXFP8)
+ *           ss_gate, ss_up [D/128, I_shared, 4]; ss_down [I_shared/128, D, 4]
+ *           (E8M0, shared_precision MOE_MXFP8 only, else NULL): stage-major
+ *           scales, as moe_mxfp8_pack_scales writes them with groups = 1
+ * In MXFP8 the activations follow the weights: x (routed: in the gather;
+ * shared: in its own pass) and h are quantised along their K axis. */
 typedef struct {
   const void *w_gate, *w_up, *w_down;
   const uint8_t *s_gate, *s_up, *s_down;
   const void *ws_gate, *ws_up, *ws_down;
+  const uint8_t *ss_gate, *ss_up, *ss_down;
 } moe_weights;
 
 /* Bytes of device workspace the three calls below need for `shape` (one

@@ -27,12 +27,13 @@ class MoeShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "T", "D", "I", "I_shared", "E_total", "k", "num_src_ranks", "rank", "experts_per_rank",
         "tokens_per_src_rank", "max_rows", "minibatch_rows", "ring_rows")] + [
-        ("precision", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+        ("precision", ctypes.c_int32), ("shared_precision", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "ws_gate", "ws_up", "ws_down")]
+        "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "ws_gate", "ws_up", "ws_down", "ss_gate", "ss_up",
+        "ss_down")]
 
 
 class MoeError(RuntimeError):

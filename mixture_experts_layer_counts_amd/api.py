@@ -38,8 +38,11 @@ def _need(t: torch.Tensor, name: str, dtype, shape, device: torch.device) -> Non
 
 def shape_for(T: int, D: int, I: int, E: int, k: int, I_shared: Optional[int] = None,
               minibatch_rows: Optional[int] = None, ring_rows: Optional[int] = None,
-              precision: str = "bf16", R: int = 1, rank: int = 0, max_rows: Optional[int] = None) -> _lib.MoeShape:
-    """A moe_shape for one GPU (R = 1) or for rank ``rank`` of R source ranks."""
+              precision: str = "bf16", R: int = 1, rank: int = 0, max_rows: Optional[int] = None,
+              shared_precision: str = "bf16") -> _lib.MoeShape:
+    """A moe_shape for one GPU (R = 1) or for rank ``rank`` of R source ranks.
+    ``precision`` is that of the routed experts, ``shared_precision`` that of
+    the shared expert (bf16 unless MXFP8 is asked for)."""
     L = E // R
     max_rows = T * k if max_rows is None else max_rows
     b = minibatch_rows or max(max_rows, 1)
@@ -49,7 +52,7 @@ def shape_for(T: int, D: int, I: int, E: int, k: int, I_shared: Optional[int] = 
     s.num_src_ranks, s.rank, s.experts_per_rank, s.tokens_per_src_rank = R, rank, L, T
     s.max_rows, s.minibatch_rows, s.ring_rows = max_rows, b, C
     s.precision = {"bf16": _lib.MOE_BF16, "mxfp8": _lib.MOE_MXFP8}[precision]
-    s.reserved = 0
+    s.shared_precision = {"bf16": _lib.MOE_BF16, "mxfp8": _lib.MOE_MXFP8}[shared_precision]
     return s
 
 
@@ -136,9 +139,17 @@ class MoELayer:
                 _need(weights[sn], sn, torch.uint8, (L, shp[2] // 128, shp[1], 4), dev)
                 setattr(w, n, _ptr(weights[qn]))
                 setattr(w, sn, _ptr(weights[sn]))
-        for n, shp in (("ws_gate", (Is, D)), ("ws_up", (Is, D)), ("ws_down", (D, Is))):
-            _need(weights[n], n, torch.bfloat16, shp, dev)
-            setattr(w, n, _ptr(weights[n]))
+        if s.shared_precision == _lib.MOE_BF16:
+            for n, shp in (("ws_gate", (Is, D)), ("ws_up", (Is, D)), ("ws_down", (D, Is))):
+                _need(weights[n], n, torch.bfloat16, shp, dev)
+                setattr(w, n, _ptr(weights[n]))
+        else:  # E4M3 bytes "qs_*" and packed scales "ss_*" (quantize_mxfp8, pack_mxfp8_scales)
+            for n, qn, sn, shp in (("ws_gate", "qs_gate", "ss_gate", (Is, D)), ("ws_up", "qs_up", "ss_up", (Is, D)),
+                                   ("ws_down", "qs_down", "ss_down", (D, Is))):
+                _need(weights[qn], qn, torch.uint8, shp, dev)
+                _need(weights[sn], sn, torch.uint8, (shp[1] // 128, shp[0], 4), dev)
+                setattr(w, n, _ptr(weights[qn]))
+                setattr(w, sn, _ptr(weights[sn]))
         if out is None:
             out = torch.empty((s.T, D), dtype=torch.bfloat16, device=dev)
         _need(out, "out", torch.bfloat16, (s.T, D), dev)

@@ -403,6 +403,40 @@ __device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int 
       d[1] = hi;
       args.Cs[((col / kMxStageK) * args.cs_rows + (p - args.c_sub)) * 4 + (col / 32) % 4] = sc;
     }
+  } else if constexpr (EPI == kEpiF32) {
+    // fp32 rows (the shared expert's output): one 128-row band per 32-row
+    // block index fm (block fm of the four row groups covers tile rows fm*128
+    // .. fm*128+127), staged through LDS and copied out in 16-byte stores
+    constexpr int CS = BN * 4 + 16;  // fp32 row stride of a staged band
+    constexpr int BAND = kWM * 32;
+    static_assert(BAND * CS <= LDS_BYTES, "staged band fits");
+    constexpr int CPR = BN * 4 / 16;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (fm * BAND >= nrows) break;  // workgroup-uniform
+      if (fm > 0) __syncthreads();    // the previous band's copy-out is done with the LDS
+      if (fm < fm_live) {             // wave-uniform
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col_l = wn * WTN + fn * 32 + (lane & 31);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row_b = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            *reinterpret_cast<float*>(smem + row_b * CS + col_l * 4) = acc[0][fm][fn][r];
+          }
+        }
+      }
+      __syncthreads();
+      const int band_rows = min(BAND, nrows - fm * BAND);
+      for (int idx = tid; idx < band_rows * CPR; idx += 64 * kNW) {
+        const int row = idx / CPR, ch = idx - row * CPR;
+        const int col = n0 + ch * 4;
+        if (col >= args.N) continue;  // N % 32 == 0: a chunk is all in or out
+        const int64_t p = p0 + fm * BAND + row;
+        *reinterpret_cast<f32x4_t*>(static_cast<char*>(args.C) + ((p - args.c_sub) * args.ldc + col) * 4) =
+            *reinterpret_cast<const f32x4_t*>(smem + row * CS + ch * 16);
+      }
+    }
   } else {
     constexpr int CS = BN * 2 + 16;  // bf16 row stride of the staged tile
     static_assert(BM * CS <= LDS_BYTES, "staged tile fits");
@@ -523,6 +557,9 @@ hipError_t launch_gemm_mx(const MxGemmArgs& a, int epilogue, hipStream_t stream)
     case kEpiBF16:
       if (a.ldc % 8 != 0) return hipErrorInvalidValue;
       return run_mx<256, kEpiBF16>(a, stream);
+    case kEpiF32:  // rows in tile order only (no row table)
+      if (a.ldc % 4 != 0 || a.c_idx) return hipErrorInvalidValue;
+      return run_mx<256, kEpiF32>(a, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -29,6 +29,12 @@ hipError_t launch_schedule(const int32_t* routes, int R, int NK, int c, int L, i
 hipError_t launch_build_tiles(const int32_t* offsets, int L, int64_t b, int64_t max_rows, int BM, int n_minibatches,
                               int max_tiles, int4* tiles, int32_t* tile_count, hipStream_t stream);
 
+// Tile list of a dense GEMM run through the routed kernels: rows 0 .. rows-1 as
+// one segment of expert 0, cut into ceil(rows / BM) tiles of equal height
+// (rounded up to 32), in the same format as the routed lists.
+int dense_tiles_bound(int64_t rows, int BM);
+hipError_t launch_dense_tiles(int64_t rows, int BM, int4* tiles, int32_t* tile_count, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // Grouped GEMM  C[rows, N] = A[rows, K] * B[e][N, K]^T  (bf16 in, fp32 accumulate)
 // ---------------------------------------------------------------------------
@@ -62,8 +68,9 @@ struct GemmArgs {
   int64_t c_split_stride;  // elements between the output planes of the K ranges
 };
 
-// Grouped MXFP8 GEMM (routed only): E4M3 operands with one E8M0 scale per 32
-// elements along K, fp32 accumulate.  Data row-major, scales stage-major (the
+// Grouped MXFP8 GEMM over a tile list (routed experts, or a dense GEMM through
+// a one-expert list): E4M3 operands with one E8M0 scale per 32 elements along
+// K, fp32 accumulate.  Data row-major, scales stage-major (the
 // byte of row r, K block j at ((j / 4) * rows + r) * 4 + j % 4): A [a_rows][K]
 // + [K/128][a_rows][4]; B per expert [N][K] + [K/128][N][4].
 struct MxGemmArgs {
@@ -78,7 +85,7 @@ struct MxGemmArgs {
   const uint8_t* Bs1;
   int N;
   int K;
-  void* C;      // SwiGLU: E4M3 [.][ldc], scales to Cs [ldc/128][cs_rows][4]; BF16: bf16 [.][ldc]
+  void* C;      // SwiGLU: E4M3 [.][ldc], scales to Cs [ldc/128][cs_rows][4]; BF16: bf16 [.][ldc]; F32: fp32 [.][ldc]
   uint8_t* Cs;  // output row = c_idx ? c_idx[p] : p - c_sub
   int64_t cs_rows;
   int64_t ldc;
@@ -128,6 +135,10 @@ hipError_t launch_clear_int(int* p, int n, hipStream_t stream);
 // MXFP8: rows x K bf16 -> E4M3 codes + one E8M0 scale per 32 elements along K.
 hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale,
                                  hipStream_t stream);
+// rows x K bf16 -> E4M3 codes [rows][K] + E8M0 scales stage-major [K/128][rows][4]
+// (the layout the MX GEMMs read activation scales in); K a multiple of 128.
+hipError_t launch_quantize_rows_mx_staged(const uint16_t* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale,
+                                          hipStream_t stream);
 // Row-major scales [groups][rows][K/32] -> stage-major [groups][K/128][rows][4].
 hipError_t launch_pack_mx_scales(const uint8_t* scale, int64_t groups, int64_t rows, int64_t K, uint8_t* packed,
                                  hipStream_t stream);

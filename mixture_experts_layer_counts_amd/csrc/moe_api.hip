@@ -17,7 +17,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   size_t err, ord_local, chunk_cnt, M, tiles, tile_count, ring, ring_s, h, h_s, Y, h_shared, shared_out, router_parts,
-      total;
+      xs_q, xs_s, hs_s, shared_tiles, shared_tile_count, total;
   int router_splits;
   int64_t n_minibatches;
   int max_tiles;
@@ -28,7 +28,7 @@ struct Layout {
 bool valid_shape(const moe_shape* s, moe_status* why) {
   *why = MOE_ERR_INVALID_ARG;
   if (!s) return false;
-  if (s->reserved != 0) return false;
+  if (s->shared_precision != MOE_BF16 && s->shared_precision != MOE_MXFP8) return false;
   if (s->T < 0 || s->D <= 0 || s->I <= 0 || s->I_shared <= 0 || s->E_total <= 0 || s->k <= 0) return false;
   if (s->k > s->E_total) return false;
   if (s->num_src_ranks < 1 || s->rank < 0 || s->rank >= s->num_src_ranks) return false;
@@ -48,6 +48,7 @@ bool valid_shape(const moe_shape* s, moe_status* why) {
   if (s->D > 65536 || s->I > 65536 || s->I_shared > 65536) return false;
   // MXFP8 GEMM stages are 128 elements of K wide (D for up/gate, I for down)
   if (s->precision == MOE_MXFP8 && (s->D % 128 || s->I % 128)) return false;
+  if (s->shared_precision == MOE_MXFP8 && (s->D % 128 || s->I_shared % 128)) return false;
   *why = MOE_OK;
   return true;
 }
@@ -98,8 +99,17 @@ Layout layout_of(const moe_shape* s) {
     L.h = take(sizeof(uint16_t) * s->minibatch_rows * s->I);
   }
   L.Y = take(sizeof(uint16_t) * L.y_rows * s->D);
-  L.h_shared = take(sizeof(uint16_t) * s->T * s->I_shared);
   L.shared_out = take(sizeof(float) * s->T * s->D);
+  if (s->shared_precision == MOE_MXFP8) {  // x and h of the shared expert in E4M3 + stage-major E8M0
+    L.xs_q = take(s->T * s->D);
+    L.xs_s = take(s->T * (s->D / 32));
+    L.h_shared = take(s->T * s->I_shared);
+    L.hs_s = take(s->T * (s->I_shared / 32));
+    L.shared_tiles = take(sizeof(int4) * moe::dense_tiles_bound(s->T, moe::gemm_mx_routed_bm()));
+    L.shared_tile_count = take(sizeof(int32_t));
+  } else {
+    L.h_shared = take(sizeof(uint16_t) * s->T * s->I_shared);
+  }
   L.router_parts = take(L.router_splits > 1 ? sizeof(float) * L.router_splits * s->T * s->E_total : 0);
   L.total = off;
   return L;
@@ -149,6 +159,75 @@ moe_status check_ws(const moe_shape* s, const void* ws, size_t ws_bytes, Layout*
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < L->total) return MOE_ERR_WORKSPACE;
   return MOE_OK;
+}
+
+// The shared expert in MXFP8, an option beside the MoK paper's bf16 shared
+// expert (§3.4, "MXFP8 Support"): x is MX-quantised along D, the up/gate GEMM
+// quantises h along I_shared in its epilogue, and the down GEMM writes fp32
+// rows for the combine.  Both GEMMs are the routed MX kernels over a tile list
+// holding the T rows as one segment of "expert" 0.
+hipError_t shared_expert_mx(const moe_shape* shape, const moe_weights* w, const void* x_local, const Layout& L,
+                            void* ws, hipStream_t s) {
+  const int64_t T = shape->T, D = shape->D, Is = shape->I_shared;
+  uint8_t* xq = at<uint8_t>(ws, L.xs_q);
+  uint8_t* xs = at<uint8_t>(ws, L.xs_s);
+  uint8_t* hq = at<uint8_t>(ws, L.h_shared);
+  uint8_t* hs = at<uint8_t>(ws, L.hs_s);
+  int4* tiles = at<int4>(ws, L.shared_tiles);
+  int32_t* count = at<int32_t>(ws, L.shared_tile_count);
+  const int bm = moe::gemm_mx_routed_bm();
+  {
+    ProbeScope probe(MOE_K_SHARED_UP, s);
+    hipError_t e = moe::launch_quantize_rows_mx_staged(static_cast<const uint16_t*>(x_local), T, D, xq, xs, s);
+    if (e == hipSuccess) e = moe::launch_dense_tiles(T, bm, tiles, count, s);
+    if (e != hipSuccess) return e;
+    moe::MxGemmArgs u{};
+    u.A = xq;
+    u.As = xs;
+    u.a_rows = T;
+    u.a_sub = 0;
+    u.a_mod = INT64_MAX;
+    u.B0 = static_cast<const uint8_t*>(w->ws_gate);
+    u.B1 = static_cast<const uint8_t*>(w->ws_up);
+    u.Bs0 = w->ss_gate;
+    u.Bs1 = w->ss_up;
+    u.N = static_cast<int>(Is);
+    u.K = static_cast<int>(D);
+    u.C = hq;
+    u.Cs = hs;
+    u.cs_rows = T;
+    u.ldc = Is;
+    u.c_idx = nullptr;
+    u.c_sub = 0;
+    u.tiles = tiles;
+    u.tile_count = count;
+    u.max_tiles = moe::dense_tiles_bound(T, bm);
+    e = moe::launch_gemm_mx(u, moe::kEpiSwiGLU, s);
+    if (e != hipSuccess) return e;
+  }
+  moe::MxGemmArgs d{};
+  d.A = hq;
+  d.As = hs;
+  d.a_rows = T;
+  d.a_sub = 0;
+  d.a_mod = INT64_MAX;
+  d.B0 = static_cast<const uint8_t*>(w->ws_down);
+  d.B1 = nullptr;
+  d.Bs0 = w->ss_down;
+  d.Bs1 = nullptr;
+  d.N = static_cast<int>(D);
+  d.K = static_cast<int>(Is);
+  d.C = at<float>(ws, L.shared_out);
+  d.Cs = nullptr;
+  d.cs_rows = 0;
+  d.ldc = D;
+  d.c_idx = nullptr;
+  d.c_sub = 0;
+  d.tiles = tiles;
+  d.tile_count = count;
+  d.max_tiles = moe::dense_tiles_bound(T, bm);
+  ProbeScope probe(MOE_K_SHARED_DOWN, s);
+  return moe::launch_gemm_mx(d, moe::kEpiF32, s);
 }
 
 // One minibatch of the routed experts in MXFP8 (MoK paper §3.4 "MXFP8
@@ -329,6 +408,8 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
   const bool mx = shape->precision == MOE_MXFP8;
   if (!w || !w->w_gate || !w->w_up || !w->w_down || !w->ws_gate || !w->ws_up || !w->ws_down) return MOE_ERR_INVALID_ARG;
   if (mx && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+  const bool shared_mx = shape->shared_precision == MOE_MXFP8;
+  if (shared_mx && (!w->ss_gate || !w->ss_up || !w->ss_down)) return MOE_ERR_INVALID_ARG;
   if (!expert_offsets || !route_dst || !topk_gate || !out) return MOE_ERR_INVALID_ARG;
   if (shape->T > 0 && !x_local) return MOE_ERR_INVALID_ARG;
   if (shape->max_rows > 0 && (!x_src || !sched_src)) return MOE_ERR_INVALID_ARG;
@@ -358,7 +439,9 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
 
   // 2. shared expert on this rank's tokens (MoK paper §3.4, "Shared Expert":
   //    it needs no dispatch, so it goes first)
-  if (T > 0) {
+  if (T > 0 && shared_mx) {
+    MOE_TRY_HIP(shared_expert_mx(shape, w, x_local, L, ws, s));
+  } else if (T > 0) {
     moe::GemmArgs g{};
     g.k_splits = 1;
     g.A = static_cast<const uint16_t*>(x_local);

@@ -61,6 +61,30 @@ hipError_t launch_quantize_mxfp8(const uint16_t* src, int64_t rows, int64_t K, u
   return hipGetLastError();
 }
 
+// Rows quantised with their scales written stage-major ([K/128][rows][4], the
+// layout the MX GEMMs read activation scales in): one thread per 32-element
+// block, the same encoder as above.
+__global__ __launch_bounds__(256) void quantize_rows_mx_staged_kernel(const uint16_t* __restrict__ src, int64_t rows,
+                                                                      int64_t K, uint8_t* __restrict__ q,
+                                                                      uint8_t* __restrict__ scale) {
+  const int64_t nb = K / 32;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= rows * nb) return;
+  const int64_t row = i / nb, blk = i % nb;
+  quantize_block32(src + i * 32, q + i * 32, scale + ((blk >> 2) * rows + row) * 4 + (blk & 3));
+}
+
+hipError_t launch_quantize_rows_mx_staged(const uint16_t* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale,
+                                          hipStream_t stream) {
+  if (K % 128 != 0) return hipErrorInvalidValue;
+  const int64_t blocks = rows * (K / 32);
+  if (blocks <= 0) return hipSuccess;
+  if ((blocks + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
+  quantize_rows_mx_staged_kernel<<<static_cast<unsigned>((blocks + 255) / 256), 256, 0, stream>>>(src, rows, K, q,
+                                                                                                  scale);
+  return hipGetLastError();
+}
+
 // Scale words into the layout the MX GEMM reads: row-major [groups][rows][K/32]
 // -> stage-major [groups][K/128][rows][4] (one 4-byte word per row and 128-wide
 // K stage; one thread moves one word).

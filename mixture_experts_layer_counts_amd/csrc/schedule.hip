@@ -262,6 +262,29 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   if (l == 0) tile_count[m] = total < max_tiles ? total : max_tiles;
 }
 
+// Dense tile list: one segment [0, rows) of expert 0, split as the routed
+// lists split an expert segment (equal heights rounded up to 32, at most BM).
+__global__ void dense_tiles_kernel(int64_t rows, int BM, int4* __restrict__ tiles, int32_t* __restrict__ tile_count) {
+  const int n = static_cast<int>((rows + BM - 1) / BM);
+  int64_t h = (rows + n - 1) / n;
+  h = (h + 31) / 32 * 32;  // <= BM since BM is a multiple of 32
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int64_t p0 = static_cast<int64_t>(i) * h;
+    const int64_t r = rows - p0 < h ? rows - p0 : h;  // > 0: (n - 1) * h < rows
+    tiles[i] = make_int4(n << 10, static_cast<int>(p0), static_cast<int>(r), 0);
+  }
+  if (threadIdx.x == 0) *tile_count = n;
+}
+
+int dense_tiles_bound(int64_t rows, int BM) { return rows > 0 ? static_cast<int>((rows + BM - 1) / BM) : 1; }
+
+hipError_t launch_dense_tiles(int64_t rows, int BM, int4* tiles, int32_t* tile_count, hipStream_t stream) {
+  if (rows <= 0 || BM <= 0 || BM % 32 || rows >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if ((rows + BM - 1) / BM >= (1 << 21)) return hipErrorInvalidValue;  // the tile count shares a word with the expert id
+  dense_tiles_kernel<<<1, 256, 0, stream>>>(rows, BM, tiles, tile_count);
+  return hipGetLastError();
+}
+
 hipError_t launch_build_tiles(const int32_t* offsets, int L, int64_t b, int64_t max_rows, int BM, int n_minibatches,
                               int max_tiles, int4* tiles, int32_t* tile_count, hipStream_t stream) {
   if (n_minibatches <= 0) return hipSuccess;

@@ -20,7 +20,10 @@ Readings where the pages are silent (listed in the design doc):
   routed expert's output row is stored in bf16; the shared expert's output and
   the gate-weighted sum stay at full precision;
 * in MXFP8 mode the routed experts see MX-quantised activations and weights
-  (§3.4 "MXFP8 Support"); the shared expert and the router stay bf16.
+  (§3.4 "MXFP8 Support"); the shared expert and the router stay bf16.  The
+  shared expert may be taken to MXFP8 too, as an option beside the pages'
+  choice: then it sees MX-quantised x and weights and stores h in MX along
+  I_shared, like a routed expert, and its output stays at full precision.
 """
 
 from __future__ import annotations
@@ -216,11 +219,21 @@ def routed_outputs(x_bits: np.ndarray, weights: Dict[str, np.ndarray], idx: np.n
 
 
 def shared_output(x_bits: np.ndarray, weights: Dict[str, np.ndarray],
-                  tokens: Optional[np.ndarray] = None, exact: bool = False) -> np.ndarray:
-    """f_shared(x) in fp64 (bf16 weights, h stored in bf16, output unrounded)."""
+                  tokens: Optional[np.ndarray] = None, exact: bool = False,
+                  precision: str = "bf16") -> np.ndarray:
+    """f_shared(x) in fp64, output unrounded.  bf16: bf16 weights, h stored in
+    bf16.  mxfp8: x MX-quantised along D, the MX weights "qs_*"/"ss_*"
+    (row-major scales [N, K/32]) dequantised, h stored in MX along I_shared."""
     x = _bf16.to_f64(x_bits if tokens is None else x_bits[tokens])
-    return ffn(x, _bf16.to_f64(weights["ws_gate"]), _bf16.to_f64(weights["ws_up"]),
-               _bf16.to_f64(weights["ws_down"]), h_store=None if exact else "bf16", y_store=None)
+    if precision == "bf16":
+        return ffn(x, _bf16.to_f64(weights["ws_gate"]), _bf16.to_f64(weights["ws_up"]),
+                   _bf16.to_f64(weights["ws_down"]), h_store=None if exact else "bf16", y_store=None)
+    if precision == "mxfp8":
+        return ffn(_mx.round_f64(x), _mx.dequantize(weights["qs_gate"], weights["ss_gate"]),
+                   _mx.dequantize(weights["qs_up"], weights["ss_up"]),
+                   _mx.dequantize(weights["qs_down"], weights["ss_down"]),
+                   h_store=None if exact else "mx", y_store=None)
+    raise ValueError(precision)
 
 
 def combine(shared: np.ndarray, g: np.ndarray, Y: np.ndarray) -> np.ndarray:
@@ -230,7 +243,7 @@ def combine(shared: np.ndarray, g: np.ndarray, Y: np.ndarray) -> np.ndarray:
 
 def forward(x_bits: np.ndarray, weights: Dict[str, np.ndarray], logits_f32: np.ndarray, k: int,
             precision: str = "bf16", tokens: Optional[np.ndarray] = None,
-            exact: bool = False) -> Dict[str, np.ndarray]:
+            exact: bool = False, shared_precision: str = "bf16") -> Dict[str, np.ndarray]:
     """The whole layer for the given (or all) tokens from fp32 router logits.
 
     The selection and the gates are taken on the given fp32 logits (the same
@@ -241,7 +254,7 @@ def forward(x_bits: np.ndarray, weights: Dict[str, np.ndarray], logits_f32: np.n
     g = gates(logits_f32, idx)
     tok = np.arange(idx.shape[0]) if tokens is None else np.asarray(tokens)
     Y = routed_outputs(x_bits, weights, idx, precision, tok, exact=exact)
-    sh = shared_output(x_bits, weights, tok, exact=exact)
+    sh = shared_output(x_bits, weights, tok, exact=exact, precision=shared_precision)
     return {"idx": idx, "gates": g, "Y": Y, "shared": sh, "out": combine(sh, g[tok], Y)}
 
 
@@ -323,6 +336,17 @@ def quantize_weights_mx(weights: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]
     out = dict(weights)
     for name, q, s in (("w_gate", "q_gate", "s_gate"), ("w_up", "q_up", "s_up"),
                        ("w_down", "q_down", "s_down")):
+        out[q], out[s] = _mx.quantize(_bf16.to_f64(weights[name]))
+    return out
+
+
+def quantize_shared_mx(weights: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    """MX-quantise the shared expert's weights along their K axis (D for gate
+    and up, I_shared for down) from their bf16 values: "qs_*" codes and "ss_*"
+    row-major scales [N, K/32]."""
+    out = dict(weights)
+    for name, q, s in (("ws_gate", "qs_gate", "ss_gate"), ("ws_up", "qs_up", "ss_up"),
+                       ("ws_down", "qs_down", "ss_down")):
         out[q], out[s] = _mx.quantize(_bf16.to_f64(weights[name]))
     return out
 

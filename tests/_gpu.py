@@ -34,10 +34,21 @@ def to_dev(inp, dev):
     return {n: t.to(dev) for n, t in inp.items()}
 
 
-def layer(w: synth.Workload, dev, b=None, C=None, R=1, precision="bf16"):
+def layer(w: synth.Workload, dev, b=None, C=None, R=1, precision="bf16", shared_precision="bf16"):
     from mixture_experts_layer_counts_amd import MoELayer, shape_for
     return MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
-                              precision=precision), device=dev)
+                              precision=precision, shared_precision=shared_precision), device=dev)
+
+
+def mx_shared_weights_dev(inp_dev):
+    """The shared expert's weights MX-quantised on the GPU (moe_quantize_mxfp8)
+    with their scales packed stage-major (moe_mxfp8_pack_scales, one group)."""
+    from mixture_experts_layer_counts_amd import pack_mxfp8_scales, quantize_mxfp8
+    out = {}
+    for n in ("gate", "up", "down"):
+        q, s = quantize_mxfp8(inp_dev["ws_" + n])
+        out["qs_" + n], out["ss_" + n] = q, pack_mxfp8_scales(s.unsqueeze(0))[0]
+    return out
 
 
 def mx_weights_dev(inp_dev):

@@ -66,7 +66,7 @@ def test_workspace_sizes(lib):
     ("ring_rows", 1000, -1),    # not a multiple of b
     ("max_rows", 5, -1),        # R == 1 needs T*k
     ("precision", 7, -1),
-    ("reserved", 1, -1),
+    ("shared_precision", 7, -1),
     ("tokens_per_src_rank", 3, -1),
 ])
 def test_invalid_shapes_are_rejected(lib, field, value, code):
@@ -87,6 +87,28 @@ def test_mxfp8_shapes(lib):
     sm = shape_for(T=8192, D=7168, I=2048, E=384, k=8, minibatch_rows=65536, ring_rows=65536, precision="mxfp8")
     saved = 65536 * 7168 * 2 - 65536 * (7168 + 224) + 65536 * 2048 * 2 - 65536 * (2048 + 64)
     assert abs((ws_bytes(lib, sb)[1] - ws_bytes(lib, sm)[1]) - saved) < 4096
+
+
+def test_mxfp8_shared_shapes(lib):
+    # the MX shared expert's GEMMs take 128-wide K stages over D and I_shared
+    for D, Is, code in ((128, 128, 0), (7168, 2048, 0), (128, 64, -2), (192, 128, -2)):
+        s = shape_for(T=64, D=D, I=64, E=8, k=2, I_shared=Is, shared_precision="mxfp8")
+        assert ws_bytes(lib, s)[0] == code
+    # its activations take E4M3 bytes plus stage-major scales in the workspace
+    sb = shape_for(T=8192, D=7168, I=2048, E=384, k=8)
+    sm = shape_for(T=8192, D=7168, I=2048, E=384, k=8, shared_precision="mxfp8")
+    assert ws_bytes(lib, sm)[1] > ws_bytes(lib, sb)[1]
+
+
+def test_mxfp8_shared_forward_needs_scales(lib):
+    s = shape_for(T=64, D=128, I=128, E=8, k=2, I_shared=128, shared_precision="mxfp8")
+    st, n = ws_bytes(lib, s)
+    fake = ctypes.c_void_p(4096)  # never dereferenced: the call returns first
+    w = _lib.MoeWeights()
+    for f in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+        setattr(w, f, 4096)
+    assert lib.moe_forward(ctypes.byref(s), ctypes.byref(w), fake, fake, fake, fake, fake, fake, fake, None, fake,
+                           n, None) == -1
 
 
 def test_mxfp8_forward_needs_scales(lib):

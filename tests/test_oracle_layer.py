@@ -150,6 +150,39 @@ def test_mx_mode_is_lossless_on_grid_inputs():
     assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
 
 
+def test_mx_shared_expert_is_lossless_on_grid_inputs():
+    # the MXFP8 shared expert on x and weights chosen on the MX grid equals the
+    # bf16 shared expert when h is left unrounded (a swapped gate/up, a wrong
+    # operand or a missed dequantisation would break the equality)
+    w, inp, host, logits = small(D=64, I=32, Is=64)
+    rng = np.random.default_rng(3)
+
+    def grid(shape):
+        codes = rng.integers(0x30, 0x50, shape).astype(np.uint8)  # |v| in [2^-1, 2^3]
+        codes[..., ::32] = 0x7E
+        codes |= (rng.integers(0, 2, shape) * 0x80).astype(np.uint8)
+        return mx.dequantize(codes, np.full(shape[:-1] + (shape[-1] // 32,), 127 - 9, dtype=np.uint8))
+
+    h2 = dict(host)
+    for n in ("ws_gate", "ws_up", "ws_down", "x"):
+        h2[n] = bf16.from_f64(grid(host[n].shape))
+    q = moe.quantize_shared_mx(h2)
+    for n in ("gate", "up", "down"):
+        assert np.array_equal(mx.dequantize(q["qs_" + n], q["ss_" + n]), bf16.to_f64(h2["ws_" + n]))
+    a = moe.shared_output(h2["x"], q, exact=True, precision="mxfp8")
+    b = moe.shared_output(h2["x"], h2, exact=True, precision="bf16")
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+    # stored: h in MX along I_shared moves the output by a bounded amount
+    s = moe.shared_output(h2["x"], q, precision="mxfp8")
+    rms = np.sqrt(np.mean(b ** 2))
+    assert 1e-4 < np.max(np.abs(s - b)) / rms < 0.3
+    # the whole layer with the MX shared expert changes only the shared term
+    f1 = moe.forward(h2["x"], q, logits, w.k, shared_precision="mxfp8")
+    f0 = moe.forward(h2["x"], h2, logits, w.k)
+    assert np.array_equal(f1["Y"], f0["Y"])
+    assert np.allclose(f1["out"] - f1["shared"], f0["out"] - f0["shared"], rtol=0, atol=1e-12)
+
+
 def test_storage_rounding_is_present_and_bounded():
     # Rounding h and each routed output row to bf16 moves the layer output by
     # about 1e-2 RMS: the same size as the bf16 parity tolerance.  This is why
