@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--workload", default="dsv3", choices=["tiny", "mid", "dsv3", "mx", "ep64"])
     ap.add_argument("--precision", default=None, choices=["bf16", "mxfp8"],
                     help="routed-expert precision (default: mxfp8 for the mx workload, else bf16)")
+    ap.add_argument("--shared-precision", default="bf16", choices=["bf16", "mxfp8"],
+                    help="shared-expert precision (bf16 as the pages keep it; mxfp8 is an option)")
     ap.add_argument("--minibatch", type=int, default=0, help="rows per minibatch b (0: all routed rows)")
     ap.add_argument("--ring", type=int, default=0, help="ring rows C (0: b)")
     ap.add_argument("--routing", default="x", choices=["x", "gaussian", "zipf"],
@@ -144,6 +146,12 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
             q, sc = quantize_mxfp8(inp["w_" + n])
             weights["q_" + n], weights["s_" + n] = q, pack_mxfp8_scales(sc)
         wq = time_weight_quantize(torch, inp, quantize_mxfp8, pack_mxfp8_scales)
+    if args.shared_precision == "mxfp8":  # the shared weights too, ahead of time
+        from mixture_experts_layer_counts_amd import pack_mxfp8_scales
+        weights = dict(weights)
+        for n in ("gate", "up", "down"):
+            q, sc = quantize_mxfp8(inp["ws_" + n])
+            weights["qs_" + n], weights["ss_" + n] = q, pack_mxfp8_scales(sc.unsqueeze(0))[0]
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
     dev = torch.device("cuda", 0)
@@ -152,7 +160,7 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
 
     def make(b, C):
         layer = MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
-                                   precision=precision), device=dev)
+                                   precision=precision, shared_precision=args.shared_precision), device=dev)
 
         def step():
             if logits_in is not None:
@@ -167,14 +175,18 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
     layer, step = make(b, C)
     return Job(name=w.name, w=w, R=1, c=0, T=w.T, E_route=w.E, P=P, b=b, C=C, precision=precision, layer=layer,
                inp=inp, step=step, make=make, routed_from_x=logits_in is None, weight_quantize=wq,
+               shared_precision=args.shared_precision,
                config={"workload": f"{w.name}: T={w.T} D={w.D} I={w.I} E={w.E} top-{w.k} + 1 shared "
                                    f"(I={w.I_shared})", "minibatch_rows": b, "ring_rows": C,
+                       "shared_precision": args.shared_precision,
                        "routing": "router projection from x" if logits_in is None else f"given {args.routing} logits"})
 
 
 def setup_ep64(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
     """One rank's share at EP = 64 (DeepSeek-V3 expert shape)."""
     import numpy as np
+    if args.shared_precision != "bf16":
+        raise SystemExit("--shared-precision mxfp8 is for the single-GPU workloads")
     R, N, k, L, c, E_total = 64, 4096, 8, 4, 0, 256
     counts = synth.zipf_counts(32768, L, 1.2)
     P = int(sum(counts))
@@ -235,6 +247,8 @@ def kernel_model(job, offsets, sched_src):
     D, I, Is, k = w.D, w.I, w.I_shared, w.k
     mx = job.precision == "mxfp8"
     wb = 1.0 + 1.0 / 32 if mx else 2.0  # bytes per routed weight / activation element
+    smx = getattr(job, "shared_precision", "bf16") == "mxfp8"
+    sb = 1.0 + 1.0 / 32 if smx else 2.0  # the same for the shared expert
     counts = np.diff(offsets)
     touched = int(np.count_nonzero(counts))
     unique_src = len(np.unique(sched_src[:P] // k)) if P else 0
@@ -244,8 +258,9 @@ def kernel_model(job, offsets, sched_src):
         "topk": (T * E * 4 + T * k * 8, 0.0),
         "schedule": (job.R * T * k * 8 + P * 4 + len(offsets) * 8, 0.0),
         "tiles": (len(offsets) * 4, 0.0),
-        "shared_up": (T * D * 2 + 2 * Is * D * 2 + T * Is * 2, 4.0 * T * Is * D),
-        "shared_down": (T * Is * 2 + D * Is * 2 + T * D * 4, 2.0 * T * D * Is),
+        # MX shared expert: x read once in bf16, written and read again in MX
+        "shared_up": (T * D * 2 + (2 * T * D * sb if smx else 0) + 2 * Is * D * sb + T * Is * sb, 4.0 * T * Is * D),
+        "shared_down": (T * Is * sb + D * Is * sb + T * D * 4, 2.0 * T * D * Is),
         "gather": (unique_src * D * 2 + P * D * wb, 0.0),
         "up_gate": (touched * 2 * I * D * wb + P * D * wb + P * I * wb, 4.0 * P * I * D),
         "down": (touched * D * I * wb + P * I * wb + P * D * 2, 2.0 * P * D * I),
@@ -316,7 +331,8 @@ def main():
                 continue
             t = tot.value / reps * 1e-3
             nbytes, flops = model[name]
-            peak_k = peak_mma if name in ("up_gate", "down") else PEAK_BF16
+            shared_mx = name.startswith("shared") and getattr(job, "shared_precision", "bf16") == "mxfp8"
+            peak_k = peak_mma if name in ("up_gate", "down") else (PEAK_FP8 if shared_mx else PEAK_BF16)
             e = {"ms_per_step": round(t * 1e3, 4), "launches_per_step": n.value // reps,
                  "alg_bytes": int(nbytes), "GB_per_s": round(nbytes / t / 1e9, 1),
                  "hbm_frac": round(nbytes / t / PEAK_HBM, 4)}
@@ -512,8 +528,11 @@ def cpu_baseline(job, n_tok):
         host[n] = _ExpertTable({int(e): sub[i] for i, e in enumerate(experts)})
     if job.precision == "mxfp8":
         _oracle_mx(host, experts)
+    sp = getattr(job, "shared_precision", "bf16")
+    if sp == "mxfp8":  # the oracle's own MX quantisation of the shared weights (ahead of time, not timed)
+        host = ref.quantize_shared_mx(host)
     t0 = time.perf_counter()
-    ref.forward(xb, host, lg, w.k, precision=job.precision, tokens=tok)
+    ref.forward(xb, host, lg, w.k, precision=job.precision, tokens=tok, shared_precision=sp)
     secs = t_route + time.perf_counter() - t0
     return {"value": round(n_tok / secs, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n_tok} tokens of the {w.name} workload ({len(experts)} distinct routed experts + "
