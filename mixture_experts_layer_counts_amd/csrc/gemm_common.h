@@ -1,6 +1,8 @@
 // Pieces shared by the bf16 and MXFP8 grouped GEMMs (gfx950 device code).
 #pragma once
 
+#include <atomic>
+
 #include "common.h"
 
 namespace moe {
@@ -51,6 +53,19 @@ __device__ __forceinline__ int item_thread_index(int wave) {
   int lane;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   return wave * 64 + lane;
+}
+
+// Compute units of the current device, asked once per process (0 when the
+// runtime cannot say).
+inline int64_t device_compute_units() {
+  static std::atomic<int64_t> cached{0};
+  int64_t v = cached.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  cached.store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 // Workgroups of `kernel` (launched with `block` threads) that fit on the
