@@ -84,3 +84,29 @@ def test_mx_shared_expert_alone_matches_oracle_shared_term():
     err = rel_err(r["out32"].cpu().numpy(), want)
     say("  max|err|/RMS =", err)
     assert err <= TOL_MX
+
+
+def test_mx_shared_expert_full_size_sampled():
+    # the shared expert at the DeepSeek-V3 layer shape (8192 tokens, D = 7168,
+    # I_shared = 2048): 32 dense tiles, the fp32 epilogue over N = 7168.  Two
+    # routed experts with zero weights and top-1 keep the routed term at zero,
+    # so the output is the shared term; sampled tokens against the oracle.
+    dev = need_gpu()
+    w = synth.Workload("dsv3-shared", T=8192, D=7168, I=2048, E=2, k=1, I_shared=2048, seed=45, routing="gaussian")
+    say("mx_shared_full: drawing inputs on the GPU")
+    inp = synth.make_inputs(w, device="cuda")
+    for n in ("w_gate", "w_up", "w_down"):
+        inp[n].zero_()
+    weights = dict(inp)
+    weights.update(mx_shared_weights_dev(inp))
+    m = layer(w, dev, shared_precision="mxfp8")
+    r = m(inp["x"], inp["w_router"], weights, logits=inp["logits"])
+    torch.cuda.synchronize()
+    assert m.device_error() == 0
+    tok = np.array([0, 1, 255, 256, 4095, 7679, 7680, 8000, 8191])  # tile edges of 256-row tiles
+    host = ref.quantize_shared_mx({n: synth.bits(inp[n].cpu()) for n in ("ws_gate", "ws_up", "ws_down")})
+    want = ref.shared_output(synth.bits(inp["x"][torch.as_tensor(tok, device=dev)].cpu()), host, precision="mxfp8")
+    got = r["out32"][torch.as_tensor(tok, device=dev)].cpu().numpy()
+    err = rel_err(got, want)
+    say("  max|err|/RMS =", err)
+    assert err <= TOL_MX
