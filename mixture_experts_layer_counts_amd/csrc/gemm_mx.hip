@@ -1,4 +1,4 @@
-// Grouped MXFP8 GEMMs of the routed expert FFNs on gfx950 scaled MFMA.
+// Grouped MXFP8 GEMMs of the expert FFNs on gfx950 scaled MFMA.
 //
 // MoK paper "Mixture-of-Kittens: MoE Megakernel for NVL72s", §3.4 "MXFP8
 // Support": the routed experts run on MXFP8 operands; weights are quantised
@@ -29,8 +29,10 @@
 //
 // Epilogues, staged through LDS so that rows leave in 16-byte stores: SwiGLU
 // with MX quantisation of h along I (staged as fp32; one thread then
-// quantises one 32-column block of a row), and bf16 for the down projection,
-// scattered to the row of the route it came from.
+// quantises one 32-column block of a row), bf16 for the down projection,
+// scattered to the row of the route it came from, and fp32 in 128-row bands
+// (the shared expert's down projection when it runs in MXFP8: a dense GEMM
+// through a tile list holding its T rows as one segment).
 
 #include <algorithm>
 #include <atomic>
