@@ -26,6 +26,9 @@ CASES = [
                               routing="gaussian"), "mxfp8", [(None, None), (256, 512)]),
     ("wide", synth.Workload("wide-mxs", T=1024, D=1024, I=512, E=48, k=8, I_shared=512, seed=42, routing="zipf"),
      "mxfp8", [(None, None)]),
+    # one token: a single shared tile of one row
+    ("t1", synth.Workload("t1-mxs", T=1, D=128, I=128, E=8, k=2, I_shared=128, seed=46, routing="gaussian"),
+     "mxfp8", [(None, None), (1, 2)]),
     # routed experts in bf16, shared expert in MXFP8
     ("bf16-routed", synth.Workload("bf16r-mxs", T=257, D=256, I=192, E=24, k=6, I_shared=384, seed=43,
                                    routing="gaussian"), "bf16", [(None, None), (200, 400)]),
