@@ -23,12 +23,13 @@
 //
 // Work order (routed).  The 256 MI355X CUs sit in 8 XCDs, each with its own
 // L2, and workgroups are dealt to XCDs round-robin.  Work items are ordered
-// expert-major, then by N block, then by row tile, and cut into 8 contiguous
-// runs, one per XCD, whose resident workgroups walk it side by side: so
-// the N-block tiles of one expert (which share the same activation rows) and
-// the row tiles of one (expert, N block) (which share the same weight rows)
-// run side by side on one XCD and meet in its L2, while every weight byte is
-// fetched from HBM about once.  With BM = 256 an expert's rows at the
+// expert-major, then by group of row tiles, then by N block, then by row tile
+// in the group (grouped_item), and cut into 8 contiguous runs, one per XCD,
+// whose workgroups walk it side by side: so the row tiles of one (expert, N
+// block) (which share the same weight rows) and the N-block tiles of one
+// group (which share the same activation rows) run close together on one XCD
+// and meet in its L2, while every weight byte is fetched from HBM about once
+// for each group of row tiles.  With BM = 256 an expert's rows at the
 // DeepSeek-V3 shape (about 256 per expert) mostly fit in one tile; 32-row
 // blocks past the end of a tile are not multiplied.
 //
@@ -255,9 +256,9 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
     // a tile of the expert group that owns item w
     const int4 g = kItemLoop ? load_uniform(args.tiles + w / n_blocks) : args.tiles[w / n_blocks];
     const int nt = g.x >> 10, first = g.w;
-    const int lw = w - first * n_blocks;
-    nb = lw / nt;
-    tile = first + lw % nt;
+    int lt;
+    grouped_item(w - first * n_blocks, nt, n_blocks, nb, lt);
+    tile = first + lt;
     const int4 t = kItemLoop ? load_uniform(args.tiles + tile) : args.tiles[tile];
     e = t.x & 1023;
     p0 = t.y;

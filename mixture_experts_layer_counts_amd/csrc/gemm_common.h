@@ -55,6 +55,24 @@ __device__ __forceinline__ int item_thread_index(int wave) {
   return wave * 64 + lane;
 }
 
+// Work order inside one expert's items (row tiles x N blocks): the row tiles
+// go in groups of kTileGroup, and each group sweeps the N blocks with its
+// tiles innermost.  A weight slab is then read by the group's tiles back to
+// back, and the group's activation rows stay in the caches over the sweep;
+// without groups every N block re-read all of a large expert's rows (the ep64
+// share's up/gate fetched 6.8 GB from HBM for 0.5 GB of algorithmic bytes).
+// Measured on that share: groups of 2, 4 and 8 took the step from 3.18 ms to
+// 3.10, 3.07-3.10 and 3.11 ms.  Item lw of an expert with nt tiles ->
+// (N block, tile index) below.
+constexpr int kTileGroup = 4;
+__device__ __forceinline__ void grouped_item(int lw, int nt, int n_blocks, int& nb, int& tile) {
+  const int q = lw / (kTileGroup * n_blocks);
+  const int tg = nt - q * kTileGroup < kTileGroup ? nt - q * kTileGroup : kTileGroup;  // tiles in group q
+  const int lq = lw - q * kTileGroup * n_blocks;
+  nb = lq / tg;
+  tile = q * kTileGroup + lq % tg;
+}
+
 // Compute units of the current device, asked once per process (0 when the
 // runtime cannot say).
 inline int64_t device_compute_units() {

@@ -256,9 +256,9 @@ __device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int 
 
   const int4 g = kItemLoop ? load_uniform(args.tiles + w / n_blocks) : args.tiles[w / n_blocks];
   const int nt = g.x >> 10, first = g.w;
-  const int lw = w - first * n_blocks;
-  const int nb = lw / nt;
-  const int4 t = kItemLoop ? load_uniform(args.tiles + first + lw % nt) : args.tiles[first + lw % nt];
+  int nb, lt;
+  grouped_item(w - first * n_blocks, nt, n_blocks, nb, lt);
+  const int4 t = kItemLoop ? load_uniform(args.tiles + first + lt) : args.tiles[first + lt];
   const int e = t.x & 1023;
   const int64_t p0 = t.y;
   const int nrows = t.z;
