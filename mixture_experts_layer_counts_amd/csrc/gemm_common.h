@@ -60,10 +60,10 @@ __device__ __forceinline__ int item_thread_index(int wave) {
 // tiles innermost.  A weight slab is then read by the group's tiles back to
 // back, and the group's activation rows stay in the caches over the sweep;
 // without groups every N block re-read all of a large expert's rows (the ep64
-// share's up/gate fetched 6.8 GB from HBM for 0.5 GB of algorithmic bytes).
-// Measured on that share: groups of 2, 4 and 8 took the step from 3.18 ms to
-// 3.10, 3.07-3.10 and 3.11 ms.  Item lw of an expert with nt tiles ->
-// (N block, tile index) below.
+// share's up/gate moved 7.0 GB through HBM for 0.84 GB of algorithmic bytes;
+// 3.5 GB with groups of 4).  Measured on that share: groups of 2, 4 and 8
+// took the step from 3.18 ms to 3.10, 3.07-3.10 and 3.11 ms.  Item lw of an
+// expert with nt tiles -> (N block, tile index) below.
 constexpr int kTileGroup = 4;
 __device__ __forceinline__ void grouped_item(int lw, int nt, int n_blocks, int& nb, int& tile) {
   const int q = lw / (kTileGroup * n_blocks);
