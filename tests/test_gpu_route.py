@@ -15,6 +15,10 @@ ROUTE_CASES = [
     synth.Workload("ragged", T=333, D=320, I=64, E=24, k=5, I_shared=64, seed=11),
     synth.Workload("wide", T=130, D=256, I=64, E=384, k=8, I_shared=64, seed=12),
     synth.Workload("e1k", T=70, D=128, I=64, E=1000, k=16, I_shared=64, seed=13),
+    # the router GEMM's K ranges: 132 output tiles take 2 ranges, 258 take one
+    # (the small cases above take 4); the top-k adds the planes in order
+    synth.Workload("k2ranges", T=5632, D=128, I=64, E=384, k=8, I_shared=64, seed=17),
+    synth.Workload("k1range", T=11008, D=128, I=64, E=384, k=8, I_shared=64, seed=18),
 ]
 
 
