@@ -29,6 +29,10 @@
  *     the caller (stream order does that).
  *   - Shapes are validated on the host from `moe_shape` alone, before any
  *     launch; violations return MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED.
+ *     Every GEMM operand must stay below 2^31 bytes (x: T*D*2; the ring:
+ *     C*D*e; h: b*I*e; the shared h: T*I_shared*e; one routed or the shared
+ *     weight matrix: I*D*e, I_shared*D*e; e = 2 in bf16, 1 in MXFP8);
+ *     larger shapes return MOE_ERR_UNSUPPORTED.
  *   - Data errors found on the device (an expert id out of range, more routed
  *     rows than `max_rows`, a non-finite router logit) set bits of a sticky
  *     word in the workspace and never cause an out-of-bounds access; read it

@@ -25,6 +25,28 @@ struct Layout {
   int64_t y_rows;
 };
 
+// The GEMMs read every operand through a buffer resource, which addresses
+// fewer than 2^31 bytes.  Each operand a launch would read that way must fit,
+// so that an oversized shape is refused here, before any launch:
+//   x (router, shared expert)  T*D*2     ring      C*D*e      routed h  b*I*e
+//   shared h                   T*I_s*e_s one routed weight matrix I*D*e
+//   shared weight matrix       I_s*D*e_s
+// with e (e_s) = 2 bytes per element in bf16 and 1 in MXFP8.  T, D, I and
+// I_s are already bounded when this runs; the router weights, E_total*D*2,
+// stay below 2^28 under the bounds E_total <= 1024 and D <= 65536.
+bool operands_addressable(const moe_shape* s) {
+  constexpr int64_t kLimit = int64_t(1) << 31;
+  if (s->ring_rows >= kLimit || s->minibatch_rows >= kLimit) return false;
+  const int64_t e = s->precision == MOE_MXFP8 ? 1 : 2;
+  const int64_t es = s->shared_precision == MOE_MXFP8 ? 1 : 2;
+  // every factor is now below 2^31 and every multiplier below 2^17: no int64 overflow
+  const int64_t bytes[] = {s->T * s->D * 2,         s->ring_rows * s->D * e, s->minibatch_rows * s->I * e,
+                           s->T * s->I_shared * es, s->I * s->D * e,         s->I_shared * s->D * es};
+  for (const int64_t v : bytes)
+    if (v >= kLimit) return false;
+  return true;
+}
+
 bool valid_shape(const moe_shape* s, moe_status* why) {
   *why = MOE_ERR_INVALID_ARG;
   if (!s) return false;
@@ -49,6 +71,7 @@ bool valid_shape(const moe_shape* s, moe_status* why) {
   // MXFP8 GEMM stages are 128 elements of K wide (D for up/gate, I for down)
   if (s->precision == MOE_MXFP8 && (s->D % 128 || s->I % 128)) return false;
   if (s->shared_precision == MOE_MXFP8 && (s->D % 128 || s->I_shared % 128)) return false;
+  if (!operands_addressable(s)) return false;
   *why = MOE_OK;
   return true;
 }

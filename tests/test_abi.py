@@ -147,3 +147,40 @@ def test_pack_scales_validates_before_launching(lib):
     assert lib.moe_mxfp8_pack_scales(None, 2, 8, 128, b, None) == -1
     assert lib.moe_mxfp8_pack_scales(a, -1, 8, 128, b, None) == -1
     assert lib.moe_mxfp8_pack_scales(a, 0, 8, 128, b, None) == 0      # nothing to move: no launch
+
+
+# Each case breaks exactly one buffer-resource limit of the GEMM operands
+# (fewer than 2^31 bytes each) while every other operand stays small; the
+# second set of sizes is the same shape brought just under that limit.
+@pytest.mark.parametrize("name,kw,ok", [
+    ("x T*D*2", dict(T=16384, D=65536, I=64, E=8, k=1, minibatch_rows=64, ring_rows=64), dict(T=16383)),
+    ("ring C*D*2", dict(T=64, D=7168, I=64, E=8, k=2, minibatch_rows=150016, ring_rows=150016),
+     dict(minibatch_rows=149760, ring_rows=149760)),
+    ("h b*I*2", dict(T=64, D=64, I=65536, E=8, k=2, I_shared=64, minibatch_rows=16384, ring_rows=16384),
+     dict(minibatch_rows=16320, ring_rows=16320)),
+    ("shared h T*Is*2", dict(T=16384, D=64, I=64, E=8, k=1, I_shared=65536, minibatch_rows=64, ring_rows=64),
+     dict(T=16383)),
+    ("routed weights I*D*2", dict(T=64, D=32768, I=32768, E=8, k=2, I_shared=64, minibatch_rows=64, ring_rows=64),
+     dict(I=32704)),
+    ("shared weights Is*D*2", dict(T=64, D=32768, I=64, E=8, k=2, I_shared=32768, minibatch_rows=64,
+                                   ring_rows=64), dict(I_shared=32704)),
+])
+def test_operand_byte_limits_are_refused_before_any_launch(lib, name, kw, ok):
+    s = shape_for(**kw)
+    assert ws_bytes(lib, s)[0] == -2, name
+    fake = ctypes.c_void_p(4096)  # never dereferenced: every call below returns first
+    w = _lib.MoeWeights()
+    for f in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+        setattr(w, f, 4096)
+    assert lib.moe_forward(ctypes.byref(s), ctypes.byref(w), fake, fake, fake, fake, fake, fake, fake, None, fake,
+                           1 << 40, None) == -2, name
+    assert lib.moe_route(ctypes.byref(s), fake, fake, fake, fake, fake, fake, 1 << 40, None) == -2, name
+    assert lib.moe_schedule(ctypes.byref(s), fake, fake, fake, fake, fake, fake, 1 << 40, None) == -2, name
+    assert ws_bytes(lib, shape_for(**{**kw, **ok}))[0] == 0, name
+
+
+def test_mxfp8_operands_are_one_byte_per_element(lib):
+    # the MX ring holds E4M3 bytes: a ring that is too large in bf16 fits in MXFP8
+    kw = dict(T=64, D=7168, I=128, E=8, k=2, I_shared=128, minibatch_rows=150016, ring_rows=150016)
+    assert ws_bytes(lib, shape_for(**kw))[0] == -2
+    assert ws_bytes(lib, shape_for(**kw, precision="mxfp8"))[0] == 0
