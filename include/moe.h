@@ -147,18 +147,22 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router
                      int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Dispatch schedule of Algorithm 1 (MoK paper §3.1): for routes A [R, N*k]
- * (global expert ids; topk_idx is A when R == 1), with local expert l = global
- * expert c*L + l:
- *   M[r][l]  routes from source rank r to local expert l;
- *   S_l      = sum_{l' < l} sum_r M[r][l']   (expert_offsets[l]; [L] = P);
- *   o        = earlier routes j' < j of the same rank to the same expert;
- *   p        = sum_{r'} min(M[r'][l], o) + #{r' < r : M[r'][l] > o};
- *   sched_src[S_l + p] = r*N*k + j  (the table row is the buffer position);
- *   route_dst[r*N*k + j] = S_l + p, or -1 for a route to a non-local expert.
- * Outputs: expert_counts [L], expert_offsets [L+1], sched_src [max_rows]
- * (entries >= P untouched), route_dst [R*N*k].  Integer only; deterministic
- * (no order-dependent atomics).  Bit-exact with the definition above.
+ * Dispatch schedule (MoK paper §3.1, "Scheduling", and its Algorithm 1).
+ * routes A [R, N*k] holds global expert ids (topk_idx is A when R == 1);
+ * route j of source rank r goes to local expert l = A[r][j] - c*L when that
+ * lies in [0, L).  The received routes are laid out expert by expert: local
+ * expert l owns positions offsets[l] .. offsets[l+1]-1.  Inside that region
+ * the routes are ordered by their ordinal o (the number of earlier routes of
+ * the same rank to the same expert) and then by source rank, so the ranks
+ * take turns.  Each route's position is computed on its own in closed form,
+ * from the per-(rank, expert) counts and o, with no sort.
+ * Outputs: expert_counts [L] routes per local expert; expert_offsets [L+1]
+ * (exclusive prefix sum, [L] = P); sched_src [max_rows]: sched_src[p] =
+ * r*N*k + j for the route at position p (the table row is the buffer
+ * position; entries >= P untouched); route_dst [R*N*k]: the inverse, the
+ * position of each route, or -1 for a route to a non-local expert.  Integer
+ * only; deterministic (no order-dependent atomics).  Bit-exact with the
+ * ordering above.
  */
 moe_status moe_schedule(const moe_shape* shape, const int32_t* routes, int32_t* expert_counts,
                         int32_t* expert_offsets, int32_t* sched_src, int32_t* route_dst, void* ws,

@@ -84,66 +84,47 @@ def gates(logits_f32: np.ndarray, idx: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def schedule(A: np.ndarray, c: int, L: int) -> Dict[str, np.ndarray]:
-    """Algorithm 1 of the MoK paper, step by step.
+    """The dispatch schedule of the MoK paper, §3.1 "Scheduling".
 
     A [R, N*K]: A[r, j] is the global expert of route j on source rank r.
-    c: current rank; local expert l is global expert c*L + l.
+    c: this rank; local expert l is global expert c*L + l.
+
+    The routes this rank receives are laid out expert by expert, each local
+    expert's routes in one contiguous region.  Inside a region a route is
+    keyed by its ordinal o (how many earlier routes of the same source rank
+    went to the same expert) and then by its source rank r, so the ranks take
+    turns.  The table is therefore the local routes sorted by the key
+    (l, o, r); no two routes share a key.  Algorithm 1 of §3.1 computes the
+    same positions in closed form; the tests check that form against this
+    table.
 
     Returns
       M        [R, L]  routes per (source rank, local expert)
       counts   [L]     rows received per local expert (sum over r of M)
-      offsets  [L+1]   S_l, the start of expert l's region; offsets[L] = P
-      sched    [P]     Phi: position p receives route (r, j), stored as r*N*K + j
+      offsets  [L+1]   start of each expert's region; offsets[L] = P
+      sched    [P]     position p receives route (r, j), stored as r*N*K + j
       route_dst [R*N*K] position of each route on this rank, -1 if not local
     """
     A = np.asarray(A, dtype=np.int64)
     R, NK = A.shape
     local = (A >= c * L) & (A < c * L + L)
+    r, j = np.nonzero(local)  # the local routes, by rank and then by route id
+    l = A[r, j] - c * L
     M = np.zeros((R, L), dtype=np.int64)
-    for r in range(R):
-        M[r] = np.bincount(A[r][local[r]] - c * L, minlength=L)
+    np.add.at(M, (r, l), 1)
     counts = M.sum(axis=0)
-    S = np.concatenate([[0], np.cumsum(counts)])
-    P = int(S[L])
-    sched = np.full(P, -1, dtype=np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    # ordinal: the routes of one (rank, expert) pair, in route order, are 0, 1, 2, ...
+    o = np.zeros(len(r), dtype=np.int64)
+    for pair in np.unique(r * L + l):
+        mine = np.nonzero(r * L + l == pair)[0]  # ascending route id j
+        o[mine] = np.arange(len(mine))
+    # the table: local routes sorted by (l, o, r)
+    order = np.lexsort((r, o, l))
+    sched = (r[order] * NK + j[order]).astype(np.int64)
     route_dst = np.full(R * NK, -1, dtype=np.int64)
-    for r in range(R):
-        seen = np.zeros(L, dtype=np.int64)  # earlier routes of rank r per local expert
-        for j in range(NK):
-            if not local[r, j]:
-                continue
-            l = int(A[r, j] - c * L)
-            o = int(seen[l])  # |{j' < j : A[r, j'] = A[r, j]}|
-            seen[l] += 1
-            Ml = M[:, l]
-            p = int(np.minimum(Ml, o).sum()) + int(np.count_nonzero(Ml[:r] > o))
-            pos = int(S[l]) + p
-            assert sched[pos] == -1
-            sched[pos] = r * NK + j
-            route_dst[r * NK + j] = pos
-    assert np.all(sched >= 0)
-    return {"M": M, "counts": counts, "offsets": S.astype(np.int64), "sched": sched,
-            "route_dst": route_dst}
-
-
-def schedule_by_sort(A: np.ndarray, c: int, L: int) -> np.ndarray:
-    """The same table as a sort of the local routes by the key (l, o, r) (§3.1).
-
-    Returns the sched column (r*N*K + j for each position).
-    """
-    A = np.asarray(A, dtype=np.int64)
-    R, NK = A.shape
-    keys = []
-    for r in range(R):
-        count = {}
-        for j in range(NK):
-            e = int(A[r, j])
-            if c * L <= e < c * L + L:
-                o = count.get(e, 0)
-                count[e] = o + 1
-                keys.append((e - c * L, o, r, r * NK + j))
-    keys.sort()
-    return np.array([key[3] for key in keys], dtype=np.int64)
+    route_dst[sched] = np.arange(len(sched))
+    return {"M": M, "counts": counts, "offsets": offsets, "sched": sched, "route_dst": route_dst}
 
 
 # ----------------------------------------------------------------------------

@@ -1,9 +1,10 @@
-"""Pins of the oracle's dispatch schedule (Algorithm 1 of the MoK paper).
+"""Pins of the oracle's dispatch schedule (MoK paper §3.1, "Scheduling").
 
-The paper gives two descriptions of the same table: Algorithm 1's closed form
-for the position p, and (§3.1 "Scheduling") an ordering of the routes by
-local expert, then per-rank ordinal, then source rank.  Each one checks the other.  On top of
-that: library routines (bincount, stable argsort) and the properties the
+The oracle builds the table as the definition of §3.1 states it: the local
+routes sorted by (local expert, per-rank ordinal, source rank).  Algorithm 1
+of the same section gives each position in closed form instead; the first
+test derives that form by counting and checks the table against it.  On top
+of that: library routines (bincount, stable argsort) and the properties the
 table must have (a bijection onto expert-contiguous regions, source ranks
 interleaved round-robin inside a region).
 """
@@ -28,11 +29,32 @@ CASES = [  # R, N, K, L, c, E_total, skew
 ]
 
 
+def closed_form_position(A, c, L, r, j):
+    """Where route j of source rank r lands, counted directly.
+
+    In the region of its local expert l the route follows every route with a
+    smaller ordinal (each rank r' contributes min(M[r', l], o) of those) and
+    the routes with the same ordinal from lower ranks (each rank r' < r that
+    sent more than o routes to l contributes one).  That count, plus the
+    region start, is the closed form of Algorithm 1 (MoK paper §3.1).
+    """
+    l = int(A[r, j]) - c * L
+    o = int(np.count_nonzero(A[r, :j] == A[r, j]))
+    M_l = np.array([np.count_nonzero(A[q] == c * L + l) for q in range(A.shape[0])])
+    start = sum(np.count_nonzero(A == c * L + e) for e in range(l))
+    return start + int(np.minimum(M_l, o).sum()) + int(np.count_nonzero(M_l[:r] > o))
+
+
 @pytest.mark.parametrize("R,N,K,L,c,E_total,skew", CASES)
-def test_closed_form_equals_sort_by_key(R, N, K, L, c, E_total, skew):
+def test_table_matches_closed_form(R, N, K, L, c, E_total, skew):
     A = random_routes(R, N, K, E_total, seed=R * 100 + N, skew=skew)
     s = moe.schedule(A, c, L)
-    assert np.array_equal(s["sched"], moe.schedule_by_sort(A, c, L))
+    for r in range(R):
+        for j in range(N * K):
+            if c * L <= A[r, j] < (c + 1) * L:
+                p = closed_form_position(A, c, L, r, j)
+                assert s["sched"][p] == r * N * K + j
+                assert s["route_dst"][r * N * K + j] == p
 
 
 @pytest.mark.parametrize("R,N,K,L,c,E_total,skew", CASES)
