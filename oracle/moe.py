@@ -174,13 +174,16 @@ def _expert_weights(weights: Dict[str, np.ndarray], e: int, precision: str):
 
 def routed_outputs(x_bits: np.ndarray, weights: Dict[str, np.ndarray], idx: np.ndarray,
                    precision: str = "bf16", tokens: Optional[np.ndarray] = None,
-                   exact: bool = False) -> np.ndarray:
+                   exact: bool = False, experts: Optional[np.ndarray] = None) -> np.ndarray:
     """Y[t, s] = f_{idx[t,s]}(x_t) for every route, fp64 [len(tokens), k, D].
 
     The routes of one expert are evaluated together (a matmul per expert); each
     route's row is independent of the others.  In MXFP8 mode x is MX-quantised
     along D before the projections (§3.4: activation quantisation in dispatch).
-    ``exact`` skips the storage rounding of h and of the output rows.
+    ``exact`` skips the storage rounding of h and of the output rows.  With
+    ``experts`` given, only the routes to those experts are evaluated and the
+    other rows of Y stay zero (so that disjoint expert sets can be evaluated
+    apart and their results added).
     """
     idx = np.asarray(idx, dtype=np.int64)
     tokens = np.arange(idx.shape[0]) if tokens is None else np.asarray(tokens)
@@ -192,7 +195,10 @@ def routed_outputs(x_bits: np.ndarray, weights: Dict[str, np.ndarray], idx: np.n
     Y = np.zeros((n, k, x.shape[1]), dtype=np.float64)
     h_store = None if exact else ("bf16" if precision == "bf16" else "mx")
     y_store = None if exact else "bf16"
+    keep = None if experts is None else {int(e) for e in experts}
     for e in np.unique(sel):
+        if keep is not None and int(e) not in keep:
+            continue
         ti, si = np.nonzero(sel == e)
         wg, wu, wd = _expert_weights(weights, int(e), precision)
         Y[ti, si] = ffn(x[ti], wg, wu, wd, h_store=h_store, y_store=y_store)
@@ -330,19 +336,6 @@ def quantize_shared_mx(weights: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
                        ("ws_down", "qs_down", "ss_down")):
         out[q], out[s] = _mx.quantize(_bf16.to_f64(weights[name]))
     return out
-
-
-def logit_bound_probabilistic(x_bits: np.ndarray, w_router_bits: np.ndarray, lam: float = 8.0) -> np.ndarray:
-    """High-probability bound on |fl32(logit) - logit|: lam * sqrt(D) * u *
-    sum_d |x_d w_{e,d}| (Higham and Mary, "A New Approach to Probabilistic
-    Rounding Error Analysis", SIAM J. Sci. Comput. 41(5), 2019: rounding
-    errors modelled as independent, mean-zero; lam = 8 makes a violation a
-    far-tail event).  Used only to decide which tokens have an unambiguous
-    top-k, never as a tolerance on a value."""
-    x = np.abs(_bf16.to_f64(x_bits))
-    w = np.abs(_bf16.to_f64(w_router_bits))
-    D = x.shape[1]
-    return lam * np.sqrt(D) * 2.0 ** -23 * (x @ w.T)
 
 
 def logit_bound(x_bits: np.ndarray, w_router_bits: np.ndarray) -> np.ndarray:

@@ -102,3 +102,94 @@ def gate_tolerance(logits_sel: np.ndarray, k: int) -> np.ndarray:
 
 def oracle_layer(w: synth.Workload, inp, logits_np, tokens=None):
     return ref.forward(synth.bits(inp["x"]), host_weights(inp), logits_np, w.k, tokens=tokens)
+
+
+def cover_tokens(idx: np.ndarray, n: int, seed: int, sched=None, offsets=None, k=None) -> np.ndarray:
+    """Token ids for a full-shape parity sample: a seeded draw of n tokens,
+    one more token for every expert the draw leaves without a route, and,
+    given the schedule (sched_src, offsets, k), the tokens whose routes sit
+    at the first and the last position of every expert's region (the tile
+    edges of that expert's rows)."""
+    idx = np.asarray(idx)
+    T = idx.shape[0]
+    rng = np.random.default_rng(seed)
+    tok = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    seen = set(idx[sorted(tok)].ravel().tolist())
+    for e in np.unique(idx):
+        if int(e) not in seen:
+            t = int(np.nonzero((idx == e).any(axis=1))[0][0])
+            tok.add(t)
+            seen.update(idx[t].tolist())
+    if sched is not None:
+        for e in range(len(offsets) - 1):
+            if offsets[e + 1] > offsets[e]:
+                tok.add(int(sched[offsets[e]]) // k)
+                tok.add(int(sched[offsets[e + 1] - 1]) // k)
+    return np.array(sorted(tok), dtype=np.int64)
+
+
+def _expert_groups(experts, per_job):
+    experts = np.asarray(sorted(set(int(e) for e in experts)), dtype=np.int64)
+    return [experts[i:i + per_job] for i in range(0, len(experts), per_job)]
+
+
+def oracle_routed_pooled(x_bits, fetch, cases, precision="bf16", per_job=2, workers=16):
+    """The oracle's routed outputs for several (idx, tokens) cases over the
+    same expert weights, evaluated expert group by expert group in a thread
+    pool (numpy releases the GIL in the arithmetic).
+
+    fetch(experts) returns the oracle's weights dict for those experts
+    (keyed by expert id: "w_*" bf16 bits, or "q_*"/"s_*" MX codes and
+    row-major scales).  Each job runs ref.routed_outputs on the tokens that
+    route to its experts, with ``experts`` set, so the jobs' results are
+    disjoint and are placed into Y [len(tokens), k, D] per case.  Returns one
+    Y per case."""
+    from concurrent.futures import ThreadPoolExecutor
+    ys = [np.zeros((len(tok), idx.shape[1], x_bits.shape[1]), dtype=np.float64) for idx, tok in cases]
+    used = set()
+    for idx, tok in cases:
+        used.update(np.unique(np.asarray(idx)[tok]).tolist())
+
+    def job(group):
+        wts = fetch(group)
+        res = []
+        for idx, tok in cases:
+            sel = np.asarray(idx)[tok]
+            rows = np.nonzero(np.isin(sel, group).any(axis=1))[0]
+            res.append((rows, ref.routed_outputs(x_bits, wts, idx, precision, tok[rows], experts=group)
+                        if len(rows) else None))
+        return res
+
+    groups = _expert_groups(used, per_job)
+    with ThreadPoolExecutor(max_workers=min(workers, os.cpu_count() or 1)) as ex:
+        for n, res in enumerate(ex.map(job, groups), 1):
+            for y, (rows, part) in zip(ys, res):
+                if part is not None:
+                    y[rows] += part
+            if n % max(1, len(groups) // 10) == 0:
+                say(f"  oracle: {n}/{len(groups)} expert groups done")
+    return ys
+
+
+def fetch_bf16(inp):
+    """fetch() for oracle_routed_pooled: the bf16 bits of some experts, copied
+    from the (device) weight tensors."""
+    def fetch(group):
+        return {n: {int(e): synth.bits(inp[n][int(e)]) for e in group} for n in ("w_gate", "w_up", "w_down")}
+    return fetch
+
+
+def fetch_mx(inp):
+    """fetch() for oracle_routed_pooled: the oracle's own MX quantisation of
+    some experts' bf16 weights (codes and row-major scales along K)."""
+    from oracle import bf16, mx
+
+    def fetch(group):
+        out = {}
+        for n in ("gate", "up", "down"):
+            q, s = {}, {}
+            for e in group:
+                q[int(e)], s[int(e)] = mx.quantize(bf16.to_f64(synth.bits(inp["w_" + n][int(e)])))
+            out["q_" + n], out["s_" + n] = q, s
+        return out
+    return fetch

@@ -1,12 +1,20 @@
 """Parity at the full DeepSeek-V3 layer shape (T=8192, D=7168, I=2048, 256
 experts, top-8, shared I=2048), in the launch configuration bench.py times
-(one minibatch of all 65,536 routed rows, ring of the same size).
+(one minibatch of all 65,536 routed rows, ring of the same size), and in ring
+mode (minibatches of 2,048 rows cycling a 4,096-row ring).
 
-The oracle cannot run the whole layer here in seconds, so:
 * routing and schedule from given fp32 logits: bit-exact over all tokens;
-* the full path from x: sampled tokens, evaluated one by one by the oracle
-  (router logits within the fp32 bound, selection, output within tolerance);
-* schedule tables: properties that hold at any size.
+* the full path from x, over all tokens:
+  - router logits within the fp32 summation bound of the fp64 logits;
+  - the selection equal to the oracle's top-k of the GPU's own fp32 logits
+    (the spec condition: identical fp32 logits give identical
+    indices), and the gates within the fp32 gate bound of the oracle's;
+  - the schedule tables equal to the oracle's for that selection;
+  - bf16 output = RNE(out32);
+* the layer output against the oracle, fed the same fp32 logits, on a sample
+  of over 512 tokens that together route to every one of the 256 experts and
+  include the first and last row of every expert's region;
+* ring mode: bitwise equal to the single-minibatch run.
 """
 
 import numpy as np
@@ -15,11 +23,10 @@ import torch
 
 import synth
 from oracle import moe as ref
-from tests._gpu import layer, need_gpu, rel_err, say
+from tests._gpu import (cover_tokens, fetch_bf16, gate_tolerance, layer, need_gpu, oracle_routed_pooled, rel_err,
+                        say)
 
 pytestmark = pytest.mark.gpu
-
-SAMPLE = [0, 1, 511, 1024, 2047, 3000, 4096, 5000, 6000, 7000, 8000, 8191]
 
 
 @pytest.fixture(scope="module")
@@ -34,10 +41,27 @@ def dsv3():
     torch.cuda.empty_cache()
 
 
+@pytest.fixture(scope="module")
+def dsv3_run(dsv3):
+    """The layer from x at b = C = P, the configuration the benchmark times."""
+    w, inp, dev = dsv3
+    P = w.T * w.k
+    m = layer(w, dev, P, P)
+    say("dsv3 full layer from x, b = C =", P)
+    r = m(inp["x"], inp["w_router"], inp)
+    torch.cuda.synchronize()
+    assert m.device_error() == 0
+    # bf16 tensors are kept as their int16 bit patterns (numpy has no bf16)
+    host = {n: (v.cpu().view(torch.int16) if v.dtype == torch.bfloat16 else v.cpu()).numpy() for n, v in r.items()}
+    del m, r
+    torch.cuda.empty_cache()
+    return host
+
+
 def check_schedule_properties(sched, idx, E, P):
-    counts, offsets = sched["counts"].cpu().numpy(), sched["offsets"].cpu().numpy()
-    src, dst = sched["sched"].cpu().numpy()[:P], sched["route_dst"].cpu().numpy()
-    flat = idx.cpu().numpy().reshape(-1)
+    counts, offsets = sched["counts"], sched["offsets"]
+    src, dst = sched["sched"][:P], sched["route_dst"]
+    flat = idx.reshape(-1)
     assert offsets[0] == 0 and offsets[-1] == P
     assert np.array_equal(np.diff(offsets), counts)
     assert np.array_equal(counts, np.bincount(flat, minlength=E))
@@ -60,6 +84,9 @@ def test_dsv3_given_logits_route_and_schedule_bit_exact(dsv3):
     l = logits.numpy()
     oi = ref.topk(l, w.k)
     assert np.array_equal(idx.cpu().numpy(), oi)
+    g = gate.cpu().numpy().astype(np.float64)
+    gref = ref.gates(l, oi)
+    assert np.all(np.abs(g - gref) <= gate_tolerance(np.take_along_axis(l, oi, 1).astype(np.float64), w.k) * gref)
     want = ref.schedule(oi.reshape(1, -1), 0, w.E)
     assert np.array_equal(sched["counts"].cpu().numpy(), want["counts"])
     assert np.array_equal(sched["offsets"].cpu().numpy(), want["offsets"])
@@ -67,49 +94,58 @@ def test_dsv3_given_logits_route_and_schedule_bit_exact(dsv3):
     assert np.array_equal(sched["route_dst"].cpu().numpy(), want["route_dst"])
 
 
-def test_dsv3_full_path_sampled_tokens(dsv3):
+def test_dsv3_from_x_route_and_schedule_all_tokens(dsv3, dsv3_run):
     w, inp, dev = dsv3
+    r = dsv3_run
     P = w.T * w.k
-    m = layer(w, dev, P, P)
-    say("dsv3 full layer from x, b = C =", P)
+    xb, wrb = synth.bits(inp["x"]), synth.bits(inp["w_router"])
+    say("dsv3 fp64 router logits and their fp32 bound over all tokens")
+    L64 = ref.router_logits(xb, wrb)
+    bound = ref.logit_bound(xb, wrb)
+    lg = r["logits"]
+    assert np.all(np.abs(lg.astype(np.float64) - L64) <= bound), "router logits outside the fp32 summation bound"
+    gi = r["idx"]
+    assert np.array_equal(ref.topk(lg, w.k), gi), "top-k differs from the oracle's on the same fp32 logits"
+    g, gref = r["gate"].astype(np.float64), ref.gates(lg, gi)
+    tol = gate_tolerance(np.take_along_axis(lg, gi.astype(np.int64), 1).astype(np.float64), w.k)
+    assert np.all(np.abs(g - gref) <= tol * gref)
+    want = ref.schedule(gi.reshape(1, -1), 0, w.E)
+    for n in ("counts", "offsets", "route_dst"):
+        assert np.array_equal(r[n], want[n]), n
+    assert np.array_equal(r["sched"][:P], want["sched"])
+    check_schedule_properties(r, gi, w.E, P)
+    out32 = torch.from_numpy(r["out32"])
+    assert np.array_equal(r["out"], out32.to(torch.bfloat16).view(torch.int16).numpy())
+
+
+def test_dsv3_output_every_expert(dsv3, dsv3_run):
+    w, inp, dev = dsv3
+    r = dsv3_run
+    gi, lg = r["idx"], r["logits"]
+    tok = cover_tokens(gi, 512, seed=2, sched=r["sched"], offsets=r["offsets"], k=w.k)
+    assert len(tok) >= 512 and len(np.unique(gi[tok])) == w.E
+    say("dsv3 oracle on", len(tok), "tokens covering all", w.E, "experts (thread pool)")
+    xb = synth.bits(inp["x"])
+    Y = oracle_routed_pooled(xb, fetch_bf16(inp), [(gi, tok)])[0]
+    shared = {n: synth.bits(inp[n]) for n in ("ws_gate", "ws_up", "ws_down")}
+    want = ref.combine(ref.shared_output(xb, shared, tok), ref.gates(lg, gi)[tok], Y)
+    err = rel_err(r["out32"][tok], want)
+    say("dsv3 max|err|/RMS over", len(tok), "tokens =", err)
+    assert err <= 1e-2
+
+
+@pytest.mark.parametrize("b,C", [(2048, 4096), (8192, 32768)])
+def test_dsv3_ring_mode_bitwise_equal(dsv3, dsv3_run, b, C):
+    # minibatches of b rows cycling a ring of C rows give the bits of the
+    # single-minibatch run (table-order gather, 256-row tiles at b = 2048)
+    w, inp, dev = dsv3
+    m = layer(w, dev, b, C)
+    say("dsv3 ring mode from x, b =", b, "C =", C)
     r = m(inp["x"], inp["w_router"], inp)
     torch.cuda.synchronize()
     assert m.device_error() == 0
-    check_schedule_properties(r, r["idx"], w.E, P)
-    tok = np.array(SAMPLE)
-    xb = synth.bits(inp["x"][torch.as_tensor(tok, device=dev)])
-    wrb = synth.bits(inp["w_router"])
-    L64 = ref.router_logits(xb, wrb)
-    bound = ref.logit_bound(xb, wrb)
-    lg = r["logits"][torch.as_tensor(tok, device=dev)].cpu().numpy().astype(np.float64)
-    assert np.all(np.abs(lg - L64) <= bound)
-    # the selection must be valid under the worst-case bound for every token,
-    # and equal the oracle's where the gap beats the probabilistic bound
-    gi = r["idx"].cpu().numpy()[tok]
-    for i in range(len(tok)):
-        sel = set(gi[i].tolist())
-        lo = min(L64[i, e] + bound[i, e] for e in sel)
-        hi = max(L64[i, f] - bound[i, f] for f in range(w.E) if f not in sel)
-        assert lo >= hi
-    pb = ref.logit_bound_probabilistic(xb, wrb)
-    srt = np.sort(L64, axis=1)[:, ::-1]
-    clear = srt[:, w.k - 1] - srt[:, w.k] > 2 * pb.max(axis=1)
-    oi = ref.topk(L64.astype(np.float32), w.k)
-    assert np.array_equal(np.sort(gi[clear], 1), np.sort(oi[clear], 1))
-    keep = np.nonzero(clear)[0]
-    say("dsv3 unambiguous sampled tokens:", len(keep), "of", len(tok))
-    assert len(keep) >= len(tok) // 2
-    # host copies of the experts the kept tokens use, and the oracle per token
-    experts = np.unique(oi[keep])
-    say("dsv3 oracle on", len(keep), "tokens,", len(experts), "experts")
-    host = {n: synth.bits(inp[n]) for n in ("ws_gate", "ws_up", "ws_down")}
-    for n in ("w_gate", "w_up", "w_down"):
-        sub = synth.bits(inp[n][torch.as_tensor(experts, device=dev)])
-        host[n] = {int(e): sub[i] for i, e in enumerate(experts)}
-    want = ref.forward(xb[keep], host, L64[keep].astype(np.float32), w.k)
-    got = r["out32"].cpu().numpy()[tok[keep]]
-    err = rel_err(got, want["out"])
-    say("dsv3 sampled max|err|/RMS =", err)
-    assert err <= 1e-2
-    assert torch.equal(r["out"][torch.as_tensor(tok, device=dev)].cpu().view(torch.int16),
-                       r["out32"][torch.as_tensor(tok, device=dev)].cpu().to(torch.bfloat16).view(torch.int16))
+    assert np.array_equal(r["idx"].cpu().numpy(), dsv3_run["idx"])
+    assert np.array_equal(r["out32"].cpu().numpy().view(np.int32), dsv3_run["out32"].view(np.int32))
+    assert np.array_equal(r["out"].cpu().view(torch.int16).numpy(), dsv3_run["out"])
+    del m, r
+    torch.cuda.empty_cache()

@@ -6,7 +6,9 @@ output against the oracle's ep_share_forward.
 The last case is the DeepSeek-V3 one-rank share at EP = 64 in the launch
 configuration the benchmark times: 4 local experts (D=7168, I=2048)
 receiving 32,768 routed rows with Zipf(1.2)-skewed counts, the shared expert
-on the rank's 4,096 tokens, b = C = 32,768; sampled rows and tokens.
+on the rank's 4,096 tokens, b = C = 32,768.  The oracle checks every region
+and row-tile edge plus 512 seeded rows of the outbox, and 512 seeded local
+tokens; ring mode (b = 4,096, C = 8,192) must give the same bits.
 """
 
 import numpy as np
@@ -106,7 +108,27 @@ def test_ep_share_parity(name, R, N, k, L, c, D, I, Is, counts, bcs, prec):
             assert np.array_equal(first[0], rows) and torch.equal(first[1].view(torch.int32), out32.cpu().view(torch.int32))
 
 
-def test_ep64_dsv3_share_sampled():
+def tile_edges(offsets, heights=(256, 320)):
+    """First and last schedule position of every expert region and of every
+    row tile in it, for the routed tile heights (a region of n rows is cut
+    into ceil(n / BM) tiles of equal height, rounded up to 32 rows)."""
+    pos = set()
+    for a, b in zip(offsets[:-1], offsets[1:]):
+        n = int(b - a)
+        if n == 0:
+            continue
+        for bm in heights:
+            tiles = -(-n // bm)
+            h = -(-(-(-n // tiles)) // 32) * 32
+            for i in range(tiles):
+                lo, hi = a + i * h, min(a + (i + 1) * h, b)
+                if lo < b:
+                    pos.update((int(lo), int(hi) - 1))
+    return pos
+
+
+@pytest.mark.timeout(600)
+def test_ep64_dsv3_share_every_edge():
     dev = need_gpu()
     R, N, k, L, c = 64, 4096, 8, 4, 0
     counts = synth.zipf_counts(32768, L, 1.2)
@@ -116,22 +138,34 @@ def test_ep64_dsv3_share_sampled():
     A = synth.ep_share_routes(R, N, k, R * L, c, L, counts, seed=50)
     g = local_gates(N, k, seed=50)
     P = sum(counts)
+    say("ep64: b = C =", P)
     m, sched, out, out32 = run_share(w, inp, A, c, R, L, g, P, P, P, local_weights(inp, c, L))
     offsets = sched["offsets"].cpu().numpy()
     assert offsets.tolist() == [0] + np.cumsum(counts).tolist()
-    # sampled schedule positions (region edges and inside) and local tokens
-    pos = np.unique(np.concatenate([offsets[:-1], offsets[1:] - 1, [5, 1000, 20000, 30000]]))
+    rows_all = m.routed_rows()[:P].cpu().view(torch.int16).numpy()
+    out32_all = out32.cpu().numpy()
+    # ring mode: minibatches of 4,096 rows cycling an 8,192-row ring give the same bits
+    say("ep64: ring mode, b = 4096, C = 8192")
+    m2, sched2, out_2, out32_2 = run_share(w, inp, A, c, R, L, g, 4096, 8192, P, local_weights(inp, c, L))
+    assert np.array_equal(m2.routed_rows()[:P].cpu().view(torch.int16).numpy(), rows_all)
+    assert np.array_equal(out32_2.cpu().numpy().view(np.int32), out32_all.view(np.int32))
+    del m2, out_2, out32_2
+    # every region and tile edge, plus 512 seeded rows; 512 seeded local tokens
+    rng = np.random.default_rng(50)
+    pos = np.array(sorted(tile_edges(offsets) | set(rng.choice(P, 512, replace=False).tolist())))
+    tok = np.sort(rng.choice(N, 512, replace=False))
     host_x = synth.bits(inp["x"])
-    tok = np.array([0, 1, 100, 2047, 3000, 4095])
     wts = {n: synth.bits(inp[n]) for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
     say("ep64: oracle on", len(pos), "rows and", len(tok), "tokens")
     want = ref.ep_share_forward(host_x, wts, A, c, L, k, g.numpy().astype(np.float64), positions=pos, tokens=tok)
     assert np.array_equal(sched["sched"].cpu().numpy()[:P], want["sched"])
     assert np.array_equal(sched["route_dst"].cpu().numpy(), want["route_dst"])
-    rows = m.routed_rows()[torch.as_tensor(pos, device=dev)].float().cpu().numpy()
+    rows = torch.from_numpy(rows_all[pos]).view(torch.bfloat16).float().numpy()
     e_rows = rel_err(rows, want["rows"])
-    e_out = rel_err(out32[torch.as_tensor(tok, device=dev)].cpu().numpy(), want["out"])
-    say("ep64 sampled rows max|err|/RMS =", e_rows, "out =", e_out)
+    e_out = rel_err(out32_all[tok], want["out"])
+    say("ep64 rows max|err|/RMS =", e_rows, "over", len(pos), "rows; out =", e_out, "over", len(tok), "tokens")
     assert rows_ok(rows, want["rows"], 1e-2) and e_out <= 1e-2
+    assert np.array_equal(out.cpu().view(torch.int16).numpy(),
+                          torch.from_numpy(out32_all).to(torch.bfloat16).view(torch.int16).numpy())
     del inp, m
     torch.cuda.empty_cache()

@@ -33,8 +33,16 @@ def test_route_from_x(w):
     xb, wb = synth.bits(inp["x"]), synth.bits(inp["w_router"])
     L64 = ref.router_logits(xb, wb)
     bound = ref.logit_bound(xb, wb)
-    lg = logits.cpu().numpy().astype(np.float64)
+    lg32 = logits.cpu().numpy()
+    lg = lg32.astype(np.float64)
     assert np.all(np.abs(lg - L64) <= bound), "router logits outside the fp32 summation bound"
+    # given its own fp32 logits, the selection is the oracle's on every token,
+    # and the gates are within the fp32 gate bound of the oracle's
+    gi32 = idx.cpu().numpy()
+    assert np.array_equal(ref.topk(lg32, w.k), gi32)
+    g32, gref32 = gate.cpu().numpy().astype(np.float64), ref.gates(lg32, gi32)
+    sel32 = np.take_along_axis(lg, gi32.astype(np.int64), 1)
+    assert np.all(np.abs(g32 - gref32) <= gate_tolerance(sel32, w.k) * gref32)
     # selection: where the fp64 logits leave no doubt the choice must be the
     # oracle's; everywhere it must be a valid top-k under the error bound
     gi = idx.cpu().numpy().astype(np.int64)

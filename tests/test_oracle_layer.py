@@ -126,6 +126,18 @@ def test_sampled_tokens_equal_full_layer():
     assert np.allclose(part, full[tok], rtol=1e-13, atol=1e-13)
 
 
+def test_routed_outputs_over_disjoint_expert_sets_add_up():
+    # evaluating the routes expert set by expert set (as the full-shape GPU
+    # tests do in a thread pool) gives the full routed outputs, bit for bit
+    w, inp, host, l = small(T=40, E=8, k=3, seed=5)
+    idx = moe.topk(l, w.k)
+    full = moe.routed_outputs(host["x"], host, idx)
+    parts = [moe.routed_outputs(host["x"], host, idx, experts=g) for g in ([0, 3, 5], [1, 2], [4, 6, 7])]
+    assert np.array_equal(parts[0] + parts[1] + parts[2], full)
+    for g, p in zip(([0, 3, 5], [1, 2], [4, 6, 7]), parts):  # rows of other experts stay zero
+        assert np.all(p[~np.isin(idx, g)] == 0)
+
+
 def test_mx_mode_is_lossless_on_grid_inputs():
     # weights and x chosen on the MX grid: quantisation is then the identity,
     # so the MXFP8 layer equals the bf16 layer when h is left unrounded
