@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -167,6 +167,31 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* w_router
 moe_status moe_schedule(const moe_shape* shape, const int32_t* routes, int32_t* expert_counts,
                         int32_t* expert_offsets, int32_t* sched_src, int32_t* route_dst, void* ws,
                         size_t ws_bytes, void* stream);
+
+/*
+ * moe_schedule for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * computes exactly what moe_schedule computes, with the same outputs, but
+ * takes no workspace.  Its scratch (per-route ordinals, per-chunk histograms
+ * and the per-(rank, expert) counts: 4*(R*N*k + R*ceil(N*k/1024)*L + R*L)
+ * bytes, each piece rounded up to 256) lives in a fixed device array of the
+ * library, MOE_SCHEDULE_STATIC_SCRATCH_BYTES bytes on each GPU, which the
+ * GPU holds until the process ends; shapes that need more return
+ * MOE_ERR_UNSUPPORTED before any device work.
+ *   dev_error  device int32, caller-owned: the kernels OR MOE_DEVERR_* bits
+ *              into it (clear it first for a fresh reading); never NULL
+ * The call runs on the current device (the stream's); its first call on a
+ * device looks up that device's copy of the array (a host query, no
+ * allocation, no synchronisation).  Every call on one GPU shares that GPU's
+ * array and leaves its contents behind: calls that overlap in time on one GPU
+ * (streams not ordered against each other) race and must not be issued;
+ * calls ordered on one stream are safe.  The same rule holds for graph
+ * replays.
+ */
+#define MOE_SCHEDULE_STATIC_SCRATCH_BYTES (16u << 20)
+moe_status moe_schedule_static(const moe_shape* shape, const int32_t* routes, int32_t* expert_counts,
+                               int32_t* expert_offsets, int32_t* sched_src, int32_t* route_dst, int32_t* dev_error,
+                               void* stream);
 
 /*
  * The layer forward from a schedule (MoK paper §2.1 MoE equation; §3.3 ring

@@ -50,6 +50,7 @@ _SIGS = {
     "moe_workspace_init": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_size_t, _P]),
     "moe_route": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_schedule": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_schedule_static": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_routed_rows": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_size_t, ctypes.POINTER(_P),

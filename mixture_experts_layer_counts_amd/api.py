@@ -188,6 +188,29 @@ class MoELayer:
         return code.value
 
 
+def schedule_static(shape: _lib.MoeShape, routes: torch.Tensor, dev_error: torch.Tensor) -> Dict[str, torch.Tensor]:
+    """moe_schedule_static: the schedule of ``routes`` [R, N*k] int32 with no
+    workspace (the library's fixed scratch array); device error bits are
+    OR-ed into ``dev_error`` (one int32 on the same device)."""
+    lib = _lib.load()
+    dev = routes.device
+    NK = shape.T * shape.k
+    routes = routes.reshape(shape.num_src_ranks, NK)
+    _need(routes, "routes", torch.int32, (shape.num_src_ranks, NK), dev)
+    _need(dev_error, "dev_error", torch.int32, (1,), dev)
+    L = shape.experts_per_rank
+    out = {
+        "counts": torch.empty(L, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(L + 1, dtype=torch.int32, device=dev),
+        "sched": torch.empty((max(shape.max_rows, 1),), dtype=torch.int32, device=dev),
+        "route_dst": torch.empty(shape.num_src_ranks * NK, dtype=torch.int32, device=dev),
+    }
+    _lib.check("moe_schedule_static", lib.moe_schedule_static(
+        ctypes.byref(shape), _ptr(routes), _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["sched"]),
+        _ptr(out["route_dst"]), _ptr(dev_error), _stream()))
+    return out
+
+
 def quantize_mxfp8(src: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     """MX-quantise a bf16 tensor along its last axis (moe_quantize_mxfp8)."""
     lib = _lib.load()

@@ -3,11 +3,20 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/moe.h"
 #include "common.h"
 #include "kernels.h"
+
+// Scratch of moe_schedule_static, the entry point that allocates nothing:
+// per-route ordinals, per-chunk histograms and M of the schedule kernels.
+// Each GPU holds its own copy until the process ends.  Host code must not
+// pass `scratch` itself to a kernel (on the host it is only a stand-in for
+// the symbol): it uses the device address looked up by static_scratch().
+constexpr size_t kStaticScratchBytes = MOE_SCHEDULE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -182,6 +191,41 @@ moe_status check_ws(const moe_shape* s, const void* ws, size_t ws_bytes, Layout*
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < L->total) return MOE_ERR_WORKSPACE;
   return MOE_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (each GPU has its own copy of the array).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status static_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// The schedule kernels' scratch carved from one base (256-byte aligned pieces).
+struct SchedPieces {
+  size_t ord_local, chunk_cnt, M, total;
+};
+
+SchedPieces sched_pieces(const moe_shape* s) {
+  const int64_t R = s->num_src_ranks, NK = s->T * s->k, Lx = s->experts_per_rank;
+  SchedPieces p{};
+  p.ord_local = 0;
+  p.chunk_cnt = align_up(sizeof(int32_t) * R * NK);
+  p.M = p.chunk_cnt + align_up(sizeof(int32_t) * R * moe::sched_chunks(static_cast<int>(NK)) * Lx);
+  p.total = p.M + align_up(sizeof(int32_t) * R * Lx);
+  return p;
 }
 
 // The shared expert in MXFP8, an option beside the MoK paper's bf16 shared
@@ -419,6 +463,30 @@ moe_status moe_schedule(const moe_shape* shape, const int32_t* routes, int32_t* 
       routes, static_cast<int>(shape->num_src_ranks), static_cast<int>(NK), static_cast<int>(shape->rank),
       static_cast<int>(shape->experts_per_rank), static_cast<int>(shape->E_total), shape->max_rows, expert_counts,
       expert_offsets, sched_src, route_dst, sc, at<int>(ws, L.err), static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_schedule_static(const moe_shape* shape, const int32_t* routes, int32_t* expert_counts,
+                               int32_t* expert_offsets, int32_t* sched_src, int32_t* route_dst, int32_t* dev_error,
+                               void* stream) {
+  moe_status why;
+  if (!valid_shape(shape, &why)) return why;
+  const int64_t NK = shape->T * shape->k;
+  if (!expert_counts || !expert_offsets || !route_dst || !dev_error || (NK > 0 && !routes) ||
+      (shape->max_rows > 0 && !sched_src))
+    return MOE_ERR_INVALID_ARG;
+  const SchedPieces pc = sched_pieces(shape);
+  if (pc.total > kStaticScratchBytes) return MOE_ERR_UNSUPPORTED;
+  void* base = nullptr;
+  const moe_status st = static_scratch(&base);
+  if (st != MOE_OK) return st;
+  // every scratch entry a later kernel reads is written first by the same
+  // call, so nothing needs clearing between calls
+  moe::SchedScratch sc{at<int32_t>(base, pc.ord_local), at<int32_t>(base, pc.chunk_cnt), at<int32_t>(base, pc.M)};
+  ProbeScope probe(MOE_K_SCHEDULE, static_cast<hipStream_t>(stream));
+  return hip_status(moe::launch_schedule(
+      routes, static_cast<int>(shape->num_src_ranks), static_cast<int>(NK), static_cast<int>(shape->rank),
+      static_cast<int>(shape->experts_per_rank), static_cast<int>(shape->E_total), shape->max_rows, expert_counts,
+      expert_offsets, sched_src, route_dst, sc, dev_error, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void* x_src, const void* x_local,

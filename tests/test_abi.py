@@ -184,3 +184,20 @@ def test_mxfp8_operands_are_one_byte_per_element(lib):
     kw = dict(T=64, D=7168, I=128, E=8, k=2, I_shared=128, minibatch_rows=150016, ring_rows=150016)
     assert ws_bytes(lib, shape_for(**kw))[0] == -2
     assert ws_bytes(lib, shape_for(**kw, precision="mxfp8"))[0] == 0
+
+
+def test_schedule_static_validates_before_any_device_work(lib):
+    fake = ctypes.c_void_p(4096)  # never dereferenced: every call below returns first
+    s = shape_for(T=64, D=128, I=64, E=8, k=2)
+    # a null error word or null outputs
+    assert lib.moe_schedule_static(ctypes.byref(s), fake, fake, fake, fake, fake, None, None) == -1
+    assert lib.moe_schedule_static(ctypes.byref(s), fake, None, fake, fake, fake, fake, None) == -1
+    # a bad shape
+    bad = shape_for(T=64, D=128, I=64, E=8, k=2)
+    bad.k = 0
+    assert lib.moe_schedule_static(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None) == -1
+    # more scratch than the library's fixed array holds: 4 bytes per route
+    # alone exceed it past 4 Mi routes
+    big = shape_for(T=16384, D=128, I=64, E=256, k=8, R=64, max_rows=65536)
+    assert 64 * 16384 * 8 * 4 > (16 << 20)
+    assert lib.moe_schedule_static(ctypes.byref(big), fake, fake, fake, fake, fake, fake, None) == -2
