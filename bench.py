@@ -31,6 +31,7 @@ import hashlib
 import json
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -61,8 +62,9 @@ def parse():
     ap.add_argument("--ring", type=int, default=0, help="ring rows C (0: b)")
     ap.add_argument("--routing", default="x", choices=["x", "gaussian", "zipf"],
                     help="x: router projection from x; gaussian/zipf: given fp32 logits")
-    ap.add_argument("--cpu-sample", type=int, default=-1,
-                    help="tokens of the oracle's timed CPU sample (0: skip; default 48, 8 in MXFP8, 4096 for ep64)")
+    ap.add_argument("--cpu-fraction", type=float, default=-1.0,
+                    help="fraction of the layer's expert work in the oracle's timed CPU sample (0: skip; default "
+                         "the whole layer (or rank share), 1/4 in MXFP8)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
     ap.add_argument("--sweep", default="", metavar="B[:C],...",
                     help="after the main run, time the step at these minibatch sizes b (ring C, default b) and "
@@ -305,12 +307,18 @@ def main():
     dominant = "up_gate"
     n_launch_per_step = (job.P + job.b - 1) // job.b
     _lib.check("moe_probe_begin", lib.moe_probe_begin(_lib.KERNELS[dominant], args.steps * n_launch_per_step))
+    # one event pair per step on the stream the library launches on (torch's
+    # current stream), for the per-step median the MoK paper's protocol reports
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        evs[i][0].record()
         job.step()
+        evs[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    med_ms = statistics.median(a.elapsed_time(b) for a, b in evs)
     tot, n = ctypes.c_double(), ctypes.c_int32()
     _lib.check("moe_probe_end", lib.moe_probe_end(ctypes.byref(tot), ctypes.byref(n)))
     ms = (t1 - t0) * 1e3 / args.steps
@@ -387,6 +395,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(med_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -399,6 +408,11 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if "router_gemm" in kernels or "topk" in kernels:
+        # the MoK paper times the layer from given router logits: the step
+        # without the router projection and top-k
+        route_ms = sum(kernels[n]["ms_per_step"] for n in ("router_gemm", "topk") if n in kernels)
+        result["ms_per_step_excl_route"] = round(ms - route_ms, 4)
 
     if getattr(job, "weight_quantize", None):
         result["weight_quantize"] = job.weight_quantize  # ahead of time, not part of the step
@@ -415,10 +429,11 @@ def main():
         result["copy_calibration_bytes"] = nb
         del src_t, dst_t
 
-    n_cpu = args.cpu_sample if args.cpu_sample >= 0 else (4096 if job.name == "ep64" else (8 if mx else 48))
-    if n_cpu > 0:
-        result["cpu_baseline"] = (cpu_baseline_ep(job, n_cpu) if job.name == "ep64"
-                                  else cpu_baseline(job, n_cpu))
+    frac = args.cpu_fraction if args.cpu_fraction >= 0 else (0.25 if mx else 1.0)
+    if frac > 0:
+        log(f"timing the CPU oracle on {frac:g} of the layer's work")
+        result["cpu_baseline"] = (cpu_baseline_ep(job, max(1, int(round(job.T * frac)))) if job.name == "ep64"
+                                  else cpu_baseline(job, frac))
     print(json.dumps(result), flush=True)
 
 
@@ -498,45 +513,59 @@ def _oracle_mx(host, experts):
         host["s_" + n] = _ExpertTable({int(e): res[(n, int(e))][1] for e in experts})
 
 
-def cpu_baseline(job, n_tok):
-    """The oracle, as it stands, on the first n_tok tokens of the same workload."""
+def cpu_baseline(job, frac):
+    """The oracle, as it stands, on a fixed fraction of the layer's work.
+
+    The sample is the first ``frac`` of the routed experts with every route
+    they receive, so each sampled expert sees its whole batch of rows and the
+    widening of its weights is spread over those rows as in the full layer;
+    plus the router projection, top-k and gates of all T tokens, and the
+    shared expert and the combine on the first frac*T tokens.  That is a
+    fraction frac of the layer's expert work (a little more of its routing),
+    reported as frac*T tokens."""
     import numpy as np
-    import torch
 
     import synth
     from oracle import moe as ref
 
     w, inp = job.w, job.inp
     threads = _threads()
-    tok = np.arange(n_tok)
-    xb = synth.bits(inp["x"][:n_tok])
+    n_exp = max(1, int(round(w.E * frac)))
+    n_tok = max(1, int(round(w.T * frac)))
+    experts = np.arange(n_exp)
+    xb = synth.bits(inp["x"])
     wrb = synth.bits(inp["w_router"])
     logits_given = inp.get("logits")
-    t0 = time.perf_counter()
-    if logits_given is None:
-        lg = ref.router_logits(xb, wrb).astype(np.float32)
-    else:
-        lg = synth.host_f32(logits_given[:n_tok])
-    t_route = time.perf_counter() - t0
-    idx = ref.topk(lg, w.k)
-    experts = np.unique(idx)
-    # host copies of the weights the sample touches (copy time not counted)
+    # host copies of the sampled experts' weights (copy time not counted)
     host = {"ws_gate": synth.bits(inp["ws_gate"]), "ws_up": synth.bits(inp["ws_up"]),
             "ws_down": synth.bits(inp["ws_down"])}
     for n in ("w_gate", "w_up", "w_down"):
-        sub = synth.bits(inp[n][torch.as_tensor(experts, device=inp[n].device)])
-        host[n] = _ExpertTable({int(e): sub[i] for i, e in enumerate(experts)})
+        host[n] = _ExpertTable({int(e): synth.bits(inp[n][int(e)]) for e in experts})
     if job.precision == "mxfp8":
         _oracle_mx(host, experts)
     sp = getattr(job, "shared_precision", "bf16")
     if sp == "mxfp8":  # the oracle's own MX quantisation of the shared weights (ahead of time, not timed)
         host = ref.quantize_shared_mx(host)
     t0 = time.perf_counter()
-    ref.forward(xb, host, lg, w.k, precision=job.precision, tokens=tok, shared_precision=sp)
-    secs = t_route + time.perf_counter() - t0
+    lg = ref.router_logits(xb, wrb).astype(np.float32) if logits_given is None else synth.host_f32(logits_given)
+    idx = ref.topk(lg, w.k)
+    g = ref.gates(lg, idx)
+    tok_routed = np.nonzero((idx < n_exp).any(axis=1))[0]
+    Y = ref.routed_outputs(xb, host, idx, job.precision, tokens=tok_routed, experts=experts)
+    tok = np.arange(n_tok)
+    sh = ref.shared_output(xb, host, tokens=tok, precision=sp)
+    pos = np.searchsorted(tok_routed, tok)
+    hit = (pos < len(tok_routed)) & (tok_routed[np.minimum(pos, len(tok_routed) - 1)] == tok)
+    Yt = np.zeros((n_tok,) + Y.shape[1:])
+    Yt[hit] = Y[pos[hit]]
+    ref.combine(sh, g[tok], Yt)
+    secs = time.perf_counter() - t0
+    rows = int(np.count_nonzero(idx < n_exp))
     return {"value": round(n_tok / secs, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n_tok} tokens of the {w.name} workload ({len(experts)} distinct routed experts + "
-                      f"the shared expert), numpy fp64 on {platform.processor() or platform.machine()}, "
+            "sample": f"{frac:g} of the {w.name} layer's expert work: experts 0..{n_exp - 1} of {w.E} with all "
+                      f"{rows} routes they receive (each expert its whole batch), the router projection, top-k and "
+                      f"gates of all {w.T} tokens, the shared expert and combine on {n_tok} tokens; counted as "
+                      f"{n_tok} tokens; numpy fp64 on {platform.processor() or platform.machine()}, "
                       f"os.cpu_count()={os.cpu_count()}; {secs:.1f}s"}
 
 
