@@ -61,7 +61,8 @@ struct GemmArgs {
   int64_t c_sub;
   const int4* tiles;         // routed: {expert, p0, rows, 0}; NULL: dense rows 0..dense_rows-1
   const int32_t* tile_count;  // routed: number of valid tiles
-  int tile_rows;              // routed: the height the tile lists were built with (gemm_routed_bm)
+  int tile_rows;              // routed: the height the tile lists were built with (gemm_routed_tiling)
+  int tile_cols;              // routed: output columns per work item (gemm_routed_tiling's bn_up or bn_down)
   int dense_rows;
   int max_tiles;
   int k_splits;            // dense only: K is cut into this many equal ranges, one output plane each
@@ -99,10 +100,15 @@ hipError_t launch_gemm_mx(const MxGemmArgs& args, int epilogue, hipStream_t stre
 // Tile rows of the routed MXFP8 GEMM kernels (their tile lists are built with it).
 int gemm_mx_routed_bm();
 
-// Tile rows of the routed bf16 GEMM kernels for minibatches of mb_rows rows,
-// max_rows routed rows in all over `experts` local experts, and up/gate
-// outputs n_up wide (the tile lists are built with it).
-int gemm_routed_bm(int64_t mb_rows, int64_t max_rows, int64_t experts, int64_t n_up);
+// Tiling of the routed bf16 GEMMs for minibatches of mb_rows rows, max_rows
+// routed rows in all over `experts` local experts, intermediate width I and
+// hidden width D: the tile height bm (the tile lists are built with it) and
+// the output columns per work item of the up/gate (gate and up columns each)
+// and of the down projection.
+struct RoutedTiling {
+  int bm, bn_up, bn_down;
+};
+RoutedTiling gemm_routed_tiling(int64_t mb_rows, int64_t max_rows, int64_t experts, int64_t I, int64_t D);
 hipError_t launch_gemm(const GemmArgs& args, int epilogue, hipStream_t stream);
 int gemm_tiles_bound(int64_t rows, int groups, int bm);
 

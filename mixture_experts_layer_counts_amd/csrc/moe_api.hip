@@ -30,7 +30,8 @@ struct Layout {
   int router_splits;
   int64_t n_minibatches;
   int max_tiles;
-  int routed_bm;  // tile height of the routed GEMMs' tile lists
+  int routed_bm;      // tile height of the routed GEMMs' tile lists
+  int bn_up, bn_down;  // output columns per work item of the routed bf16 GEMMs
   int64_t y_rows;
 };
 
@@ -104,8 +105,13 @@ Layout layout_of(const moe_shape* s) {
   L.router_splits = router_splits(s);
   const int64_t R = s->num_src_ranks, NK = s->T * s->k, Lx = s->experts_per_rank;
   const int64_t mb_rows = std::min<int64_t>(s->minibatch_rows, std::max<int64_t>(s->max_rows, 1));
-  const int bm = s->precision == MOE_MXFP8 ? moe::gemm_mx_routed_bm() : moe::gemm_routed_bm(mb_rows, s->max_rows, Lx, s->I);
+  const moe::RoutedTiling tiling = s->precision == MOE_MXFP8
+                                       ? moe::RoutedTiling{moe::gemm_mx_routed_bm(), 0, 0}
+                                       : moe::gemm_routed_tiling(mb_rows, s->max_rows, Lx, s->I, s->D);
+  const int bm = tiling.bm;
   L.routed_bm = bm;
+  L.bn_up = tiling.bn_up;
+  L.bn_down = tiling.bn_down;
   L.n_minibatches = s->max_rows > 0 ? (s->max_rows + s->minibatch_rows - 1) / s->minibatch_rows : 0;
   L.max_tiles = moe::gemm_tiles_bound(mb_rows, static_cast<int>(Lx), bm);
   L.y_rows = (R == 1) ? NK : s->max_rows;
@@ -608,6 +614,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     u.tile_count = tile_count + m;
     u.max_tiles = L.max_tiles;
     u.tile_rows = L.routed_bm;
+    u.tile_cols = L.bn_up;
     {
       ProbeScope probe(MOE_K_UP_GATE, s);
       MOE_TRY_HIP(moe::launch_gemm(u, moe::kEpiSwiGLU, s));
@@ -631,6 +638,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     d.tile_count = tile_count + m;
     d.max_tiles = L.max_tiles;
     d.tile_rows = L.routed_bm;
+    d.tile_cols = L.bn_down;
     ProbeScope probe(MOE_K_DOWN, s);
     MOE_TRY_HIP(moe::launch_gemm(d, moe::kEpiBF16, s));
   }

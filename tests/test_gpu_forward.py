@@ -25,9 +25,13 @@ CASES = [
      [(None, None), (100, 300), (256, 512)]),
     ("skewed", synth.Workload("skewed", T=257, D=192, I=128, E=24, k=6, I_shared=320, seed=8, routing="zipf"),
      [(None, None), (200, 400)]),
-    # 4096-row minibatches take 256-row routed tiles, all rows at once 320-row
-    # tiles (>= 192 rows per expert and >= 128 up/gate work items)
-    ("mid", synth.workload("mid", routing="gaussian"), [(4096, 8192), (None, None)]),
+    # all rows at once take 320-row routed tiles (>= 192 rows per expert and
+    # >= 128 up/gate work items); minibatches of 512-4096 rows, whose few
+    # expert segments leave most CUs idle with 256-row tiles, take 128-row
+    # tiles with up/gate items 64 columns wide and down items 64, 128 and 256
+    # wide
+    ("mid", synth.workload("mid", routing="gaussian"),
+     [(4096, 8192), (None, None), (512, 1024), (1024, 1024), (2048, 4096)]),
     # 320-row tiles with Zipf routing: experts of one to four such tiles and
     # of a few rows, in one minibatch and in two
     ("skewed320", synth.Workload("skewed320", T=1024, D=256, I=1024, E=24, k=6, I_shared=128, seed=9,
