@@ -60,15 +60,20 @@ def parse():
                     help="shared-expert precision (bf16 as the pages keep it; mxfp8 is an option)")
     ap.add_argument("--minibatch", type=int, default=0, help="rows per minibatch b (0: all routed rows)")
     ap.add_argument("--ring", type=int, default=0, help="ring rows C (0: b)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="run the routed minibatch loop as one persistent kernel (bf16 routed experts)")
+    ap.add_argument("--mem-workgroups", type=int, default=16,
+                    help="with --pipeline: workgroups that gather the minibatches past the ring (multiple of 8)")
     ap.add_argument("--routing", default="x", choices=["x", "gaussian", "zipf"],
                     help="x: router projection from x; gaussian/zipf: given fp32 logits")
     ap.add_argument("--cpu-fraction", type=float, default=-1.0,
                     help="fraction of the layer's expert work in the oracle's timed CPU sample (0: skip; default "
                          "the whole layer (or rank share), 1/4 in MXFP8)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
-    ap.add_argument("--sweep", default="", metavar="B[:C],...",
-                    help="after the main run, time the step at these minibatch sizes b (ring C, default b) and "
-                         "report them under 'granularity_sweep'")
+    ap.add_argument("--sweep", default="", metavar="B[:C[:M]],...",
+                    help="after the main run, time the step at these minibatch sizes b (ring C, default b; with "
+                         "--pipeline, M memory workgroups, default --mem-workgroups) and report them under "
+                         "'granularity_sweep'")
     ap.add_argument("--graph", action="store_true",
                     help="in the sweep, also time the step captured once in a HIP graph and replayed "
                          "(launch overhead removed)")
@@ -160,9 +165,11 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
     x, wr, logits_in = inp["x"], inp["w_router"], inp.get("logits")
     out = torch.empty((w.T, w.D), dtype=torch.bfloat16, device=dev)
 
-    def make(b, C):
+    def make(b, C, mem=None):
         layer = MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
-                                   precision=precision, shared_precision=args.shared_precision), device=dev)
+                                   precision=precision, shared_precision=args.shared_precision,
+                                   pipeline=args.pipeline,
+                                   mem_workgroups=args.mem_workgroups if mem is None else mem), device=dev)
 
         def step():
             if logits_in is not None:
@@ -221,9 +228,10 @@ def setup_ep64(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
     x_local = x_pool[c * N:(c + 1) * N]
     out = torch.empty((N, w.D), dtype=torch.bfloat16, device=dev)
 
-    def make(b, C):
+    def make(b, C, mem=None):
         layer = MoELayer(shape_for(N, w.D, w.I, E_total, k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
-                                   precision=precision, R=R, rank=c, max_rows=P), device=dev)
+                                   precision=precision, R=R, rank=c, max_rows=P, pipeline=args.pipeline,
+                                   mem_workgroups=args.mem_workgroups if mem is None else mem), device=dev)
 
         def step():
             _, _, gate = router.route(x_local, wr)
@@ -268,6 +276,10 @@ def kernel_model(job, offsets, sched_src):
         "down": (touched * D * I * wb + P * I * wb + P * D * 2, 2.0 * P * D * I),
         "combine": (local_routes * D * 2 + T * D * 4 + T * D * 2 + T * k * 8, 0.0),
     }
+    # the persistent routed kernel: up/gate and down, plus the gathers of the
+    # minibatches past the ring (read and written once in the kernel)
+    in_kernel = max(0, P - min(job.C // job.b, -(-P // job.b)) * job.b)
+    m["pipeline"] = (m["up_gate"][0] + m["down"][0] + in_kernel * D * 2 * 2, m["up_gate"][1] + m["down"][1])
     return m
 
 
@@ -304,8 +316,10 @@ def main():
         f"{int(np.diff(offsets).min())}/{int(np.diff(offsets).max())}")
 
     # timed region, with the dominant kernel bracketed by HIP events on its stream
-    dominant = "up_gate"
-    n_launch_per_step = (job.P + job.b - 1) // job.b
+    dominant = "pipeline" if args.pipeline else "up_gate"
+    n_launch_per_step = 1 if args.pipeline else (job.P + job.b - 1) // job.b
+    if args.pipeline:
+        job.config["pipeline"] = {"persistent_routed_kernel": True, "mem_workgroups": args.mem_workgroups}
     _lib.check("moe_probe_begin", lib.moe_probe_begin(_lib.KERNELS[dominant], args.steps * n_launch_per_step))
     # one event pair per step on the stream the library launches on (torch's
     # current stream), for the per-step median the MoK paper's protocol reports
@@ -358,14 +372,17 @@ def main():
     counts = np.diff(offsets)
     wb = 1.0 + 1.0 / 32 if mx else 2.0
     launches = []
-    for m in range(n_launch_per_step):
+    for m in range((job.P + job.b - 1) // job.b):
         lo, hi = m * job.b, min((m + 1) * job.b, job.P)
         touched = int(np.count_nonzero((offsets[:-1] < hi) & (offsets[1:] > lo) & (counts > 0)))
         rows = hi - lo
         launches.append((touched * 2 * w.I * w.D * wb + rows * w.D * wb + rows * w.I * wb,
                          2.0 * rows * 2 * w.I * w.D))
-    alg_bytes = float(np.mean([l[0] for l in launches]))
-    alg_flops = float(np.mean([l[1] for l in launches]))
+    if args.pipeline:  # one launch holds every minibatch's up/gate and down, and the in-kernel gathers
+        alg_bytes, alg_flops = model["pipeline"]
+    else:
+        alg_bytes = float(np.mean([l[0] for l in launches]))
+        alg_flops = float(np.mean([l[1] for l in launches]))
     t_dom = dom_ms * 1e-3
     bound = "hbm" if alg_bytes / PEAK_HBM >= alg_flops / peak_mma else "mfma"
     if bound == "hbm":
@@ -443,10 +460,11 @@ def sweep(job, args, torch):
     out = []
     job.layer = None  # release the main workspace first
     for item in args.sweep.split(","):
-        b, _, C = item.partition(":")
-        b = min(int(b), job.P)
-        C = int(C) if C else b
-        layer, step = job.make(b, C)
+        parts = item.split(":")
+        b = min(int(parts[0]), job.P)
+        C = int(parts[1]) if len(parts) > 1 and parts[1] else b
+        mem = int(parts[2]) if len(parts) > 2 else args.mem_workgroups
+        layer, step = job.make(b, C, mem)
         for _ in range(2):
             step()
         torch.cuda.synchronize()
@@ -460,6 +478,8 @@ def sweep(job, args, torch):
             raise RuntimeError(f"device error word {layer.device_error():#x} at b={b} C={C}")
         e = {"minibatch_rows": b, "ring_rows": C, "minibatches": (job.P + b - 1) // b,
              "ms_per_step": round(ms, 4), "tokens_per_s": round(job.T / (ms * 1e-3), 1)}
+        if args.pipeline:
+            e["mem_workgroups"] = mem
         if args.graph:
             # the same step captured once (the library allocates nothing and
             # never synchronises, so it can be captured) and replayed
@@ -483,7 +503,8 @@ def sweep(job, args, torch):
                 raise RuntimeError(f"device error word {layer.device_error():#x} at b={b} C={C} (graph)")
             del g
         out.append(e)
-        log(f"sweep b={b} C={C}: {ms:.3f} ms/step" + (f", graph {e['graph_ms_per_step']:.3f}" if args.graph else ""))
+        log(f"sweep b={b} C={C}" + (f" mem={mem}" if args.pipeline else "") + f": {ms:.3f} ms/step" +
+            (f", graph {e['graph_ms_per_step']:.3f}" if args.graph else ""))
         del layer, step
         torch.cuda.empty_cache()
     return out

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -70,6 +70,8 @@ typedef enum { MOE_BF16 = 0, MOE_MXFP8 = 1 } moe_precision;
 #define MOE_DEVERR_EXPERT_RANGE 0x1 /* a route names an expert outside [0, E_total) */
 #define MOE_DEVERR_ROW_OVERFLOW 0x2 /* routed rows exceed max_rows; extra rows skipped */
 #define MOE_DEVERR_NONFINITE 0x4    /* a router logit is NaN or infinite */
+#define MOE_DEVERR_PIPELINE 0x8     /* a persistent-kernel wait gave up (about 1 s):
+                                       its workgroups were not all resident */
 
 /*
  * Sizes and tunables.  On one GPU: num_src_ranks = 1, rank = 0,
@@ -98,6 +100,18 @@ typedef struct {
                                   the MoK paper keeps it (§3.4, "MXFP8 Support"),
                                   or MOE_MXFP8 as an option (D and I_shared then
                                   multiples of 128) */
+  int32_t pipeline;            /* 0: the routed minibatch loop as stream-ordered
+                                  launches (gather, up/gate, down per minibatch);
+                                  1: as one persistent kernel whose workgroups
+                                  wait on device-side counters (MoK paper §3.2,
+                                  "Maximally Deferred Synchronization", "Kernel
+                                  Fusion"); routed precision MOE_BF16 only */
+  int32_t mem_workgroups;      /* pipeline == 1: workgroups of the persistent
+                                  kernel that gather minibatches C/b and later
+                                  (MoK paper §3.4, "Computation-Communication SM
+                                  Tuning"); a multiple of 8, at least 8 when
+                                  the ring holds fewer than all minibatches,
+                                  and leaving at least 8 for the GEMMs */
 } moe_shape;
 
 /* Expert weights, all K-contiguous (each output row is a contiguous K vector):
@@ -284,7 +298,9 @@ typedef enum {
   MOE_K_UP_GATE = 7,     /* routed grouped up/gate + SwiGLU */
   MOE_K_DOWN = 8,        /* routed grouped down projection */
   MOE_K_COMBINE = 9,     /* gate-weighted combine */
-  MOE_K_COUNT = 10
+  MOE_K_PIPELINE = 10,   /* pipeline == 1: the persistent routed kernel (gathers
+                            of minibatches C/b and later, up/gate, down) */
+  MOE_K_COUNT = 11
 } moe_kernel_id;
 
 moe_status moe_probe_begin(int32_t kernel_id, int32_t max_launches);

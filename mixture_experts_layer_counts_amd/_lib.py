@@ -18,16 +18,17 @@ MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE",
           -4: "MOE_ERR_HIP"}
 MOE_BF16, MOE_MXFP8 = 0, 1
-DEVERR_EXPERT_RANGE, DEVERR_ROW_OVERFLOW, DEVERR_NONFINITE = 0x1, 0x2, 0x4
+DEVERR_EXPERT_RANGE, DEVERR_ROW_OVERFLOW, DEVERR_NONFINITE, DEVERR_PIPELINE = 0x1, 0x2, 0x4, 0x8
 KERNELS = {"router_gemm": 0, "topk": 1, "schedule": 2, "tiles": 3, "shared_up": 4, "shared_down": 5, "gather": 6,
-           "up_gate": 7, "down": 8, "combine": 9}
+           "up_gate": 7, "down": 8, "combine": 9, "pipeline": 10}
 
 
 class MoeShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "T", "D", "I", "I_shared", "E_total", "k", "num_src_ranks", "rank", "experts_per_rank",
         "tokens_per_src_rank", "max_rows", "minibatch_rows", "ring_rows")] + [
-        ("precision", ctypes.c_int32), ("shared_precision", ctypes.c_int32)]
+        ("precision", ctypes.c_int32), ("shared_precision", ctypes.c_int32), ("pipeline", ctypes.c_int32),
+        ("mem_workgroups", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):

@@ -39,10 +39,12 @@ def _need(t: torch.Tensor, name: str, dtype, shape, device: torch.device) -> Non
 def shape_for(T: int, D: int, I: int, E: int, k: int, I_shared: Optional[int] = None,
               minibatch_rows: Optional[int] = None, ring_rows: Optional[int] = None,
               precision: str = "bf16", R: int = 1, rank: int = 0, max_rows: Optional[int] = None,
-              shared_precision: str = "bf16") -> _lib.MoeShape:
+              shared_precision: str = "bf16", pipeline: bool = False, mem_workgroups: int = 0) -> _lib.MoeShape:
     """A moe_shape for one GPU (R = 1) or for rank ``rank`` of R source ranks.
     ``precision`` is that of the routed experts, ``shared_precision`` that of
-    the shared expert (bf16 unless MXFP8 is asked for)."""
+    the shared expert (bf16 unless MXFP8 is asked for).  ``pipeline`` runs the
+    routed minibatch loop as one persistent kernel, ``mem_workgroups`` of
+    whose workgroups gather the minibatches the ring does not hold at once."""
     L = E // R
     max_rows = T * k if max_rows is None else max_rows
     b = minibatch_rows or max(max_rows, 1)
@@ -53,6 +55,7 @@ def shape_for(T: int, D: int, I: int, E: int, k: int, I_shared: Optional[int] = 
     s.max_rows, s.minibatch_rows, s.ring_rows = max_rows, b, C
     s.precision = {"bf16": _lib.MOE_BF16, "mxfp8": _lib.MOE_MXFP8}[precision]
     s.shared_precision = {"bf16": _lib.MOE_BF16, "mxfp8": _lib.MOE_MXFP8}[shared_precision]
+    s.pipeline, s.mem_workgroups = int(bool(pipeline)), mem_workgroups
     return s
 
 

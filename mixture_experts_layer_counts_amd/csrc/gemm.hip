@@ -503,6 +503,210 @@ hipError_t run(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// The routed minibatch loop as one persistent kernel.
+//
+// MoK paper §3.2 ("Maximally Deferred Synchronization", "Kernel Fusion") and
+// §3.4 ("Computation-Communication SM Tuning"): one resident kernel walks the
+// minibatches; a set of workgroups moves rows (the gathers into the ring) while
+// the rest run the expert GEMMs, and each step waits only for the steps whose
+// data it reads, through device-side counters, instead of for everything
+// launched before it.  On one GPU the gathers are local copies rather than
+// pulls over a fabric, but the overlap is the same: while the GEMMs of
+// minibatch m run, the rows of later minibatches are gathered, and the up/gate
+// GEMM of minibatch m+1 runs beside the down GEMM of m.
+//
+// Steps and what each waits for (counters count finished work items):
+//   G(m)  gather of minibatch m into ring slots p mod C: done by the memory
+//         workgroups for m >= C/b (the first C/b are gathered before the
+//         kernel, by the whole chip); waits until U(m - C/b) has read the
+//         slots it overwrites;
+//   U(m)  up/gate + SwiGLU of minibatch m into h buffer m mod 2: waits for
+//         G(m) and for D(m - 2), the last reader of that h buffer;
+//   D(m)  down projection of minibatch m: waits for U(m).
+// The GEMM workgroups take the U and D work items in the order U(0), then for
+// each m: U(m+1), D(m), so that a workgroup has up/gate work to do while the
+// last items of U(m) finish.  Every step waits only for steps earlier in that
+// order (and G(m) only for U(m - C/b), earlier still), and all workgroups are
+// resident at once (the grid is the chip's occupancy), so the step earliest in
+// the order that is not finished can always run: the kernel cannot deadlock.
+// Each workgroup takes its items statically: the items of a step are cut into
+// 8 runs, one per XCD, as in the stream-ordered launches, and the GEMM
+// workgroups of an XCD deal its run among themselves.  A wait that spins past
+// about a second (a workgroup that cannot be resident, for instance) sets
+// MOE_DEVERR_PIPELINE and stops waiting, so the kernel always ends.
+//
+// Visibility: a finished step's writers drain their stores (s_waitcnt), pass a
+// barrier, and one thread adds to the counter with an agent-scope release,
+// which writes the XCD's L2 back; waiters poll with agent-scope acquires,
+// which invalidate their caches before the data is read.  The work items are
+// the stream-ordered path's own (gemm_item), so results are bitwise the same.
+// ---------------------------------------------------------------------------
+constexpr int kErrPipeline = 0x8;  // MOE_DEVERR_PIPELINE
+constexpr int kSpinCap = 1 << 23;  // polls of about 0.1 us each
+
+// Wait until *ctr >= target.  One lane polls with relaxed loads (which read
+// past the caches and invalidate nothing), then one agent-scope acquire
+// invalidates this CU's stale lines once, and a barrier releases the
+// workgroup.  An acquire per poll would invalidate the caches the working
+// GEMMs of the same XCD depend on at every poll (measured: 2-20x slower).
+// Every wave of the workgroup must call this at the same point.
+__device__ __forceinline__ void wait_count(int* ctr, int target, int* err) {
+  if (target > 0 && threadIdx.x == 0) {
+    for (int spins = 0;; ++spins) {
+      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+      if ((spins & 63) == 63 &&
+          (spins > kSpinCap || (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kErrPipeline))) {
+        raise_error(err, kErrPipeline);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+// This workgroup's writes are visible device-wide, then *ctr += n.
+__device__ __forceinline__ void signal_count(int* ctr, int n) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have completed
+  __syncthreads();                                   // and every wave's
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, n, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int BMU, int BNU, int WMU, int WNU, int BMD, int BND, int WMD, int WND>
+__global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
+  static_assert(WMU * WNU == 8 && WMD * WND == 8, "8 waves");
+  constexpr int LDS_U = ring_bytes(BMU, 2 * BNU, kStageK), LDS_D = ring_bytes(BMD, BND, kStageK);
+  constexpr int LDS_BYTES = LDS_U > LDS_D ? LDS_U : LDS_D;
+  static_assert(LDS_BYTES <= kLdsBytes, "LDS rings");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  const int xcd = static_cast<int>(blockIdx.x) % kXcds, rx = static_cast<int>(blockIdx.x) / kXcds;
+  const int mem_per_xcd = pa.n_mem / kXcds;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int lane = lane_id();
+  const int64_t P = pa.offsets[pa.L] < pa.max_rows ? static_cast<int64_t>(pa.offsets[pa.L]) : pa.max_rows;
+  const int nbu = (pa.up.N + BNU - 1) / BNU, nbd = (pa.down.N + BND - 1) / BND;
+  const int64_t ring_mb = pa.C / pa.b;  // minibatches the ring holds
+  auto n_items = [&](int m, int nb) { return __builtin_amdgcn_readfirstlane(pa.up.tile_count[m]) * nb; };
+
+  if (rx < mem_per_xcd) {
+    // ---- memory workgroup j: G(m) for m >= C/b ----
+    const int j = rx * kXcds + xcd;
+    for (int m = static_cast<int>(ring_mb); m < pa.n_mb; ++m) {
+      wait_count(pa.upg + (m - ring_mb), n_items(static_cast<int>(m - ring_mb), nbu), pa.err);
+      const int64_t lo = static_cast<int64_t>(m) * pa.b, hi = lo + pa.b < P ? lo + pa.b : P;
+      const int n16 = pa.D / 8;  // 16-byte chunks per row
+      for (int64_t p = lo + static_cast<int64_t>(j) * 8 + wave; p < hi; p += static_cast<int64_t>(pa.n_mem) * 8) {
+        const int32_t route = pa.sched_src[p];
+        const int64_t src_row = route / pa.k;
+        if (route < 0 || src_row >= pa.src_rows) {  // a table not built by the schedule kernels
+          if (lane == 0) raise_error(pa.err, kErrExpertRange);
+          continue;
+        }
+        const uint4* __restrict__ s = reinterpret_cast<const uint4*>(pa.x_src + src_row * pa.D);
+        uint4* __restrict__ d = reinterpret_cast<uint4*>(pa.ring + (p % pa.C) * pa.D);
+        // eight 16-byte loads in flight per lane, then their stores; the
+        // row's last chunks one at a time
+        int c = lane;
+        for (; c + 7 * kWave < n16; c += 8 * kWave) {
+          const uint4 v0 = s[c], v1 = s[c + kWave], v2 = s[c + 2 * kWave], v3 = s[c + 3 * kWave];
+          const uint4 v4 = s[c + 4 * kWave], v5 = s[c + 5 * kWave], v6 = s[c + 6 * kWave], v7 = s[c + 7 * kWave];
+          d[c] = v0;
+          d[c + kWave] = v1;
+          d[c + 2 * kWave] = v2;
+          d[c + 3 * kWave] = v3;
+          d[c + 4 * kWave] = v4;
+          d[c + 5 * kWave] = v5;
+          d[c + 6 * kWave] = v6;
+          d[c + 7 * kWave] = v7;
+        }
+        for (; c < n16; c += kWave) d[c] = s[c];
+      }
+      signal_count(pa.gathered + m, 1);
+    }
+    return;
+  }
+
+  // ---- GEMM workgroup: the U and D items of its XCD's runs ----
+  const int r = rx - mem_per_xcd, nr = static_cast<int>(gridDim.x) / kXcds - mem_per_xcd;
+  // The items of the steps are dealt to the XCD's GEMM workgroups round-robin
+  // in step order, each step starting where the last one stopped (`cursor`),
+  // so that consecutive steps (U(m+1) and D(m)) land on different workgroups
+  // and run side by side; this workgroup takes positions j0, j0 + nr, ... of
+  // its XCD's run of the step's n items.
+  int cursor = 0;
+  auto my_items = [&](int n, int& lo, int& hi) __attribute__((always_inline)) {
+    const int chunk = (n + kXcds - 1) / kXcds;
+    const int run0 = xcd * chunk, run1 = min(n, (xcd + 1) * chunk);
+    const int len = run1 > run0 ? run1 - run0 : 0;
+    lo = run0 + (r - cursor + nr) % nr;
+    hi = run1;
+    cursor = (cursor + len) % nr;
+  };
+  auto run_up = [&](int m) __attribute__((always_inline)) {
+    int lo, hi;
+    my_items(n_items(m, nbu), lo, hi);
+    if (lo >= hi) return;
+    // G(m) (memory workgroups, or before the kernel) and D(m - 2), the last reader of h buffer m mod 2
+    if (m >= ring_mb) wait_count(pa.gathered + m, pa.n_mem, pa.err);
+    if (m >= 2) wait_count(pa.down_done + (m - 2), n_items(m - 2, nbd), pa.err);
+    GemmArgs a = pa.up;
+    a.tiles = pa.up.tiles + static_cast<int64_t>(m) * pa.up.max_tiles;
+    a.tile_count = pa.up.tile_count + m;
+    a.C = pa.h + static_cast<int64_t>(m & 1) * pa.b * pa.up.N;
+    a.c_sub = static_cast<int64_t>(m) * pa.b;
+    int done = 0;
+    for (int w = lo; w < hi; w += nr, ++done) {
+      if (done) __syncthreads();  // the previous item's copy-out has read the LDS
+      gemm_item<BMU, BNU, WMU, WNU, kEpiSwiGLU, true, kStageK>(a, __builtin_amdgcn_readfirstlane(w), nbu, 1, smem,
+                                                               wave);
+    }
+    signal_count(pa.upg + m, done);
+  };
+  auto run_down = [&](int m) __attribute__((always_inline)) {
+    int lo, hi;
+    my_items(n_items(m, nbd), lo, hi);
+    if (lo >= hi) return;
+    wait_count(pa.upg + m, n_items(m, nbu), pa.err);
+    GemmArgs a = pa.down;
+    a.tiles = pa.up.tiles + static_cast<int64_t>(m) * pa.up.max_tiles;
+    a.tile_count = pa.up.tile_count + m;
+    a.A = pa.h + static_cast<int64_t>(m & 1) * pa.b * pa.up.N;
+    a.a_sub = static_cast<int64_t>(m) * pa.b;
+    int done = 0;
+    for (int w = lo; w < hi; w += nr, ++done) {
+      if (done) __syncthreads();
+      gemm_item<BMD, BND, WMD, WND, kEpiBF16, true, kStageK>(a, __builtin_amdgcn_readfirstlane(w), nbd, 1, smem,
+                                                             wave);
+    }
+    signal_count(pa.down_done + m, done);
+  };
+  if (pa.n_mb > 0) run_up(0);
+  for (int m = 0; m < pa.n_mb; ++m) {
+    if (m + 1 < pa.n_mb) run_up(m + 1);
+    run_down(m);
+  }
+}
+
+template <int BMU, int BNU, int WMU, int WNU, int BMD, int BND, int WMD, int WND>
+hipError_t run_pipeline(const PipeArgs& pa, hipStream_t stream) {
+  auto kernel = pipeline_kernel<BMU, BNU, WMU, WNU, BMD, BND, WMD, WND>;
+  static std::atomic<int64_t> resident_cache{0};
+  int64_t resident = resident_cache.load(std::memory_order_relaxed);
+  if (resident <= 0) {
+    resident = resident_workgroups(reinterpret_cast<const void*>(kernel), 512);
+    if (resident <= 0) return hipErrorInvalidValue;
+    resident_cache.store(resident, std::memory_order_relaxed);
+  }
+  const int64_t grid = resident / kXcds * kXcds;
+  // GEMM workgroups on every XCD, and memory workgroups when some minibatch is gathered in the kernel
+  if (pa.n_mem % kXcds || grid - pa.n_mem < kXcds) return hipErrorInvalidValue;
+  if (pa.n_mb > pa.C / pa.b && pa.n_mem <= 0) return hipErrorInvalidValue;
+  kernel<<<static_cast<unsigned>(grid), 512, 0, stream>>>(pa);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Routed tiles: 320 rows on a 2 x 4 wave grid (five 32-row blocks per row
@@ -614,6 +818,34 @@ hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t stream) {
     default:
       return hipErrorInvalidValue;
   }
+}
+
+// Workgroups the persistent routed kernel runs with for `tiling` (all
+// resident at once): 0 when the runtime cannot say.
+int pipeline_workgroups(const RoutedTiling& t) {
+  const void* k = nullptr;
+  if (t.bm == kRoutedBM) k = reinterpret_cast<const void*>(pipeline_kernel<320, 128, 2, 4, 320, 256, 2, 4>);
+  else if (t.bm == kSmallBM) k = reinterpret_cast<const void*>(pipeline_kernel<256, 128, 4, 2, 256, 256, 4, 2>);
+  else if (t.bn_down == 256) k = reinterpret_cast<const void*>(pipeline_kernel<128, 64, 4, 2, 128, 256, 4, 2>);
+  else if (t.bn_down == 128) k = reinterpret_cast<const void*>(pipeline_kernel<128, 64, 4, 2, 128, 128, 4, 2>);
+  else k = reinterpret_cast<const void*>(pipeline_kernel<128, 64, 4, 2, 128, 64, 4, 2>);
+  return static_cast<int>(resident_workgroups(k, 512) / kXcds * kXcds);
+}
+
+hipError_t launch_pipeline(const PipeArgs& pa, const RoutedTiling& t, hipStream_t stream) {
+  if (pa.up.tile_rows != t.bm || pa.down.tile_rows != t.bm || pa.up.tile_cols != t.bn_up ||
+      pa.down.tile_cols != t.bn_down || pa.b <= 0 || pa.C % pa.b || pa.D % 8)
+    return hipErrorInvalidValue;
+  if (t.bm == kRoutedBM && t.bn_up == 128 && t.bn_down == 256)
+    return run_pipeline<320, 128, 2, 4, 320, 256, 2, 4>(pa, stream);
+  if (t.bm == kSmallBM && t.bn_up == 128 && t.bn_down == 256)
+    return run_pipeline<256, 128, 4, 2, 256, 256, 4, 2>(pa, stream);
+  if (t.bm == kShortBM && t.bn_up == 64) {
+    if (t.bn_down == 256) return run_pipeline<128, 64, 4, 2, 128, 256, 4, 2>(pa, stream);
+    if (t.bn_down == 128) return run_pipeline<128, 64, 4, 2, 128, 128, 4, 2>(pa, stream);
+    if (t.bn_down == 64) return run_pipeline<128, 64, 4, 2, 128, 64, 4, 2>(pa, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -112,6 +112,31 @@ RoutedTiling gemm_routed_tiling(int64_t mb_rows, int64_t max_rows, int64_t exper
 hipError_t launch_gemm(const GemmArgs& args, int epilogue, hipStream_t stream);
 int gemm_tiles_bound(int64_t rows, int groups, int bm);
 
+// The routed minibatch loop as one persistent kernel (gather, up/gate +
+// SwiGLU, down for every minibatch, with device-side counters between them).
+// `up` and `down` are minibatch 0's GEMM arguments (tiles, tile_count of
+// minibatch 0; the kernel steps them by minibatch); h holds two buffers of
+// b * I bf16 (minibatch m uses buffer m mod 2).  gathered / upg / down_done
+// count finished work per minibatch and must be zero at launch.  Minibatches
+// below C / b are gathered before the launch; n_mem workgroups (a multiple of
+// 8) gather the others.
+struct PipeArgs {
+  GemmArgs up, down;
+  const uint16_t* x_src;
+  int64_t src_rows;
+  const int32_t* sched_src;
+  const int32_t* offsets;
+  int L, k, D, n_mb, n_mem;
+  int64_t b, C, max_rows;
+  uint16_t* ring;
+  uint16_t* h;
+  int *gathered, *upg, *down_done;
+  int* err;
+};
+// Workgroups the persistent kernel runs with for a tiling (all resident).
+int pipeline_workgroups(const RoutedTiling& tiling);
+hipError_t launch_pipeline(const PipeArgs& args, const RoutedTiling& tiling, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // Data movement
 // ---------------------------------------------------------------------------

@@ -32,6 +32,7 @@ struct Layout {
   int max_tiles;
   int routed_bm;      // tile height of the routed GEMMs' tile lists
   int bn_up, bn_down;  // output columns per work item of the routed bf16 GEMMs
+  size_t pipe_counters;  // pipeline == 1: 3 * n_minibatches ints
   int64_t y_rows;
 };
 
@@ -72,7 +73,10 @@ bool valid_shape(const moe_shape* s, moe_status* why) {
   if (s->num_src_ranks == 1 && s->max_rows != s->T * s->k) return false;
   if (s->max_rows > s->num_src_ranks * s->T * s->k) return false;
   if (s->precision != MOE_BF16 && s->precision != MOE_MXFP8) return false;
+  if (s->pipeline != 0 && s->pipeline != 1) return false;
+  if (s->pipeline && (s->mem_workgroups < 0 || s->mem_workgroups % 8)) return false;
   *why = MOE_ERR_UNSUPPORTED;
+  if (s->pipeline && s->precision != MOE_BF16) return false;
   if (s->D % 64 || s->I % 64 || s->I_shared % 64) return false;
   if (s->k > 16 || s->E_total > 1024 || s->experts_per_rank > 1024) return false;
   if (s->num_src_ranks * s->T * s->k >= (int64_t(1) << 31)) return false;
@@ -134,8 +138,10 @@ Layout layout_of(const moe_shape* s) {
     L.h_s = take(s->minibatch_rows * (s->I / 32));
   } else {
     L.ring = take(sizeof(uint16_t) * s->ring_rows * s->D);
-    L.h = take(sizeof(uint16_t) * s->minibatch_rows * s->I);
+    // the persistent kernel overlaps minibatch m+1's up/gate with m's down: two h buffers
+    L.h = take(sizeof(uint16_t) * s->minibatch_rows * s->I * (s->pipeline ? 2 : 1));
   }
+  L.pipe_counters = take(s->pipeline ? sizeof(int32_t) * 3 * std::max<int64_t>(L.n_minibatches, 1) : 0);
   L.Y = take(sizeof(uint16_t) * L.y_rows * s->D);
   L.shared_out = take(sizeof(float) * s->T * s->D);
   if (s->shared_precision == MOE_MXFP8) {  // x and h of the shared expert in E4M3 + stage-major E8M0
@@ -516,6 +522,15 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
   const int Lx = static_cast<int>(shape->experts_per_rank);
   const int64_t b = shape->minibatch_rows, C = shape->ring_rows, R = shape->num_src_ranks;
   if (T == 0 && shape->max_rows == 0) return MOE_OK;
+  if (shape->pipeline) {
+    // the persistent kernel's grid is every workgroup the chip holds at once
+    // (a host query): at least 8 of them must be left for the GEMMs, and some
+    // must gather when the ring holds fewer than all minibatches
+    const int grid = moe::pipeline_workgroups(moe::RoutedTiling{L.routed_bm, L.bn_up, L.bn_down});
+    if (grid <= 0) return MOE_ERR_HIP;
+    if (shape->mem_workgroups > grid - 8) return MOE_ERR_INVALID_ARG;
+    if (L.n_minibatches > C / b && shape->mem_workgroups == 0) return MOE_ERR_INVALID_ARG;
+  }
 
   uint16_t* ring = at<uint16_t>(ws, L.ring);
   uint16_t* h = at<uint16_t>(ws, L.h);
@@ -577,23 +592,10 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
   }
 
   // 3. routed experts, one minibatch of b schedule rows at a time
-  for (int64_t m = 0; m < L.n_minibatches; ++m) {
-    const int64_t p_begin = m * b;
-    const int64_t rows = std::min<int64_t>(b, shape->max_rows - p_begin);
-    if (mx) {
-      MOE_TRY_HIP(
-          routed_minibatch_mx(shape, w, x_src, sched_src, expert_offsets, route_dst, L, ws, m, p_begin, rows, s));
-      continue;
-    }
-    {
-      ProbeScope probe(MOE_K_GATHER, s);
-      if (R == 1 && L.n_minibatches == 1)  // one minibatch holds every row: read each token once
-        MOE_TRY_HIP(moe::launch_gather_src(static_cast<const uint16_t*>(x_src), T, D, k, route_dst, shape->max_rows,
-                                           C, ring, at<int>(ws, L.err), s));
-      else
-        MOE_TRY_HIP(moe::launch_gather(static_cast<const uint16_t*>(x_src), R * shape->T, D, k, sched_src,
-                                       expert_offsets, Lx, p_begin, rows, C, ring, at<int>(ws, L.err), s));
-    }
+  // (bf16 GEMM arguments of minibatch m: up/gate reads ring slots p mod C and
+  // writes h rows p - m*b; down reads them and writes each row to its route,
+  // or to outbox row p when R > 1)
+  auto up_args = [&](int64_t m, uint16_t* hbuf) {
     moe::GemmArgs u{};
     u.k_splits = 1;
     u.A = ring;
@@ -606,25 +608,24 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     u.b_expert_stride = static_cast<int64_t>(I) * D;
     u.N = I;
     u.K = D;
-    u.C = h;
+    u.C = hbuf;
     u.ldc = I;
     u.c_idx = nullptr;
-    u.c_sub = p_begin;
+    u.c_sub = m * b;
     u.tiles = tiles + m * L.max_tiles;
     u.tile_count = tile_count + m;
     u.max_tiles = L.max_tiles;
     u.tile_rows = L.routed_bm;
     u.tile_cols = L.bn_up;
-    {
-      ProbeScope probe(MOE_K_UP_GATE, s);
-      MOE_TRY_HIP(moe::launch_gemm(u, moe::kEpiSwiGLU, s));
-    }
+    return u;
+  };
+  auto down_args = [&](int64_t m, const uint16_t* hbuf) {
     moe::GemmArgs d{};
     d.k_splits = 1;
-    d.A = h;
+    d.A = hbuf;
     d.a_bytes = b * I * 2;
     d.lda = I;
-    d.a_sub = p_begin;
+    d.a_sub = m * b;
     d.a_mod = INT64_MAX;
     d.B0 = static_cast<const uint16_t*>(w->w_down);
     d.b_expert_stride = static_cast<int64_t>(D) * I;
@@ -639,8 +640,66 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     d.max_tiles = L.max_tiles;
     d.tile_rows = L.routed_bm;
     d.tile_cols = L.bn_down;
-    ProbeScope probe(MOE_K_DOWN, s);
-    MOE_TRY_HIP(moe::launch_gemm(d, moe::kEpiBF16, s));
+    return d;
+  };
+  auto gather = [&](int64_t m) {
+    const int64_t p_begin = m * b, rows = std::min<int64_t>(b, shape->max_rows - p_begin);
+    ProbeScope probe(MOE_K_GATHER, s);
+    if (R == 1 && L.n_minibatches == 1)  // one minibatch holds every row: read each token once
+      return moe::launch_gather_src(static_cast<const uint16_t*>(x_src), T, D, k, route_dst, shape->max_rows, C, ring,
+                                    at<int>(ws, L.err), s);
+    return moe::launch_gather(static_cast<const uint16_t*>(x_src), R * shape->T, D, k, sched_src, expert_offsets, Lx,
+                              p_begin, rows, C, ring, at<int>(ws, L.err), s);
+  };
+  if (shape->pipeline && L.n_minibatches > 0) {
+    // the minibatches the ring holds at once are gathered by the whole chip;
+    // the persistent kernel gathers the rest while it runs the GEMMs
+    const int64_t pre = std::min<int64_t>(C / b, L.n_minibatches);
+    int32_t* counters = at<int32_t>(ws, L.pipe_counters);
+    MOE_TRY_HIP(moe::launch_clear_int(counters, static_cast<int>(3 * L.n_minibatches), s));
+    for (int64_t m = 0; m < pre; ++m) MOE_TRY_HIP(gather(m));
+    moe::PipeArgs pa{};
+    pa.up = up_args(0, h);
+    pa.down = down_args(0, h);
+    pa.x_src = static_cast<const uint16_t*>(x_src);
+    pa.src_rows = R * shape->T;
+    pa.sched_src = sched_src;
+    pa.offsets = expert_offsets;
+    pa.L = Lx;
+    pa.k = k;
+    pa.D = D;
+    pa.n_mb = static_cast<int>(L.n_minibatches);
+    pa.n_mem = shape->mem_workgroups;
+    pa.b = b;
+    pa.C = C;
+    pa.max_rows = shape->max_rows;
+    pa.ring = ring;
+    pa.h = h;
+    pa.gathered = counters;
+    pa.upg = counters + L.n_minibatches;
+    pa.down_done = counters + 2 * L.n_minibatches;
+    pa.err = at<int>(ws, L.err);
+    {
+      ProbeScope probe(MOE_K_PIPELINE, s);
+      MOE_TRY_HIP(moe::launch_pipeline(pa, moe::RoutedTiling{L.routed_bm, L.bn_up, L.bn_down}, s));
+    }
+  } else {
+    for (int64_t m = 0; m < L.n_minibatches; ++m) {
+      const int64_t p_begin = m * b;
+      const int64_t rows = std::min<int64_t>(b, shape->max_rows - p_begin);
+      if (mx) {
+        MOE_TRY_HIP(
+            routed_minibatch_mx(shape, w, x_src, sched_src, expert_offsets, route_dst, L, ws, m, p_begin, rows, s));
+        continue;
+      }
+      MOE_TRY_HIP(gather(m));
+      {
+        ProbeScope probe(MOE_K_UP_GATE, s);
+        MOE_TRY_HIP(moe::launch_gemm(up_args(m, h), moe::kEpiSwiGLU, s));
+      }
+      ProbeScope probe(MOE_K_DOWN, s);
+      MOE_TRY_HIP(moe::launch_gemm(down_args(m, h), moe::kEpiBF16, s));
+    }
   }
 
   // 4. fixed-order gate-weighted combine

@@ -201,3 +201,19 @@ def test_schedule_static_validates_before_any_device_work(lib):
     big = shape_for(T=16384, D=128, I=64, E=256, k=8, R=64, max_rows=65536)
     assert 64 * 16384 * 8 * 4 > (16 << 20)
     assert lib.moe_schedule_static(ctypes.byref(big), fake, fake, fake, fake, fake, fake, None) == -2
+
+
+def test_pipeline_shape_fields(lib):
+    # the persistent routed kernel: memory workgroups in multiples of 8, bf16 routed experts only
+    ok = shape_for(T=64, D=128, I=64, E=8, k=2, minibatch_rows=32, ring_rows=64, pipeline=True, mem_workgroups=8)
+    assert ws_bytes(lib, ok)[0] == 0
+    assert ws_bytes(lib, shape_for(T=64, D=128, I=64, E=8, k=2, pipeline=True, mem_workgroups=12))[0] == -1
+    assert ws_bytes(lib, shape_for(T=64, D=128, I=64, E=8, k=2, pipeline=True, mem_workgroups=-8))[0] == -1
+    bad = shape_for(T=64, D=128, I=64, E=8, k=2)
+    bad.pipeline = 2
+    assert ws_bytes(lib, bad)[0] == -1
+    assert ws_bytes(lib, shape_for(T=64, D=128, I=128, E=8, k=2, I_shared=128, precision="mxfp8",
+                                   pipeline=True))[0] == -2
+    # it keeps two h buffers and per-minibatch counters in the workspace
+    plain = shape_for(T=64, D=128, I=64, E=8, k=2, minibatch_rows=32, ring_rows=64)
+    assert ws_bytes(lib, ok)[1] >= ws_bytes(lib, plain)[1] + 32 * 64 * 2 + 3 * 4 * 4
