@@ -523,7 +523,8 @@ hipError_t run(const GemmArgs& a, hipStream_t stream) {
 //         slots it overwrites;
 //   U(m)  up/gate + SwiGLU of minibatch m into h buffer m mod 2: waits for
 //         G(m) and for D(m - 2), the last reader of that h buffer;
-//   D(m)  down projection of minibatch m: waits for U(m).
+//   D(m)  down projection of minibatch m: each item waits for the up/gate
+//         items of its own row tile (all N blocks of that tile's h rows).
 // The GEMM workgroups take the U and D work items in the order U(0), then for
 // each m: U(m+1), D(m), so that a workgroup has up/gate work to do while the
 // last items of U(m) finish.  Every step waits only for steps earlier in that
@@ -644,6 +645,13 @@ __global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
     hi = run1;
     cursor = (cursor + len) % nr;
   };
+  // row tile of item w of a step with nb N blocks (the decoding gemm_item uses)
+  auto item_tile = [&](const int4* tiles, int w, int nb) __attribute__((always_inline)) {
+    const int4 g = load_uniform(tiles + w / nb);
+    int nblk, lt;
+    grouped_item(w - g.w * nb, g.x >> 10, nb, nblk, lt);
+    return g.w + lt;
+  };
   auto run_up = [&](int m) __attribute__((always_inline)) {
     int lo, hi;
     my_items(n_items(m, nbu), lo, hi);
@@ -656,11 +664,14 @@ __global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
     a.tile_count = pa.up.tile_count + m;
     a.C = pa.h + static_cast<int64_t>(m & 1) * pa.b * pa.up.N;
     a.c_sub = static_cast<int64_t>(m) * pa.b;
+    int* const tile_ctr = pa.upg_tile + static_cast<int64_t>(m) * pa.up.max_tiles;
     int done = 0;
     for (int w = lo; w < hi; w += nr, ++done) {
-      if (done) __syncthreads();  // the previous item's copy-out has read the LDS
-      gemm_item<BMU, BNU, WMU, WNU, kEpiSwiGLU, true, kStageK>(a, __builtin_amdgcn_readfirstlane(w), nbu, 1, smem,
-                                                               wave);
+      const int wu = __builtin_amdgcn_readfirstlane(w);
+      gemm_item<BMU, BNU, WMU, WNU, kEpiSwiGLU, true, kStageK>(a, wu, nbu, 1, smem, wave);
+      // the tile's h columns of this item are written (the barrier inside
+      // also lets the next item refill the LDS)
+      signal_count(tile_ctr + item_tile(a.tiles, wu, nbu), 1);
     }
     signal_count(pa.upg + m, done);
   };
@@ -668,17 +679,19 @@ __global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
     int lo, hi;
     my_items(n_items(m, nbd), lo, hi);
     if (lo >= hi) return;
-    wait_count(pa.upg + m, n_items(m, nbu), pa.err);
     GemmArgs a = pa.down;
     a.tiles = pa.up.tiles + static_cast<int64_t>(m) * pa.up.max_tiles;
     a.tile_count = pa.up.tile_count + m;
     a.A = pa.h + static_cast<int64_t>(m & 1) * pa.b * pa.up.N;
     a.a_sub = static_cast<int64_t>(m) * pa.b;
+    int* const tile_ctr = pa.upg_tile + static_cast<int64_t>(m) * pa.up.max_tiles;
     int done = 0;
     for (int w = lo; w < hi; w += nr, ++done) {
-      if (done) __syncthreads();
-      gemm_item<BMD, BND, WMD, WND, kEpiBF16, true, kStageK>(a, __builtin_amdgcn_readfirstlane(w), nbd, 1, smem,
-                                                             wave);
+      const int wd = __builtin_amdgcn_readfirstlane(w);
+      // every up/gate item of this item's row tile: its h rows (the barrier
+      // inside also lets this item refill the LDS)
+      wait_count(tile_ctr + item_tile(a.tiles, wd, nbd), nbu, pa.err);
+      gemm_item<BMD, BND, WMD, WND, kEpiBF16, true, kStageK>(a, wd, nbd, 1, smem, wave);
     }
     signal_count(pa.down_done + m, done);
   };
@@ -737,13 +750,24 @@ constexpr int kShortBM = 128;
 // minibatches took 18.8 instead of 26.3 ms (DeepSeek-V3), 6.7 instead of 12.3
 // ms (EP-64 share) and 3.2 instead of 5.0 ms (mid).  No choice changes the K
 // order of any output, so the results stay bitwise the same.
-RoutedTiling gemm_routed_tiling(int64_t mb_rows, int64_t max_rows, int64_t experts, int64_t I, int64_t D) {
+//
+// The persistent routed kernel runs the up/gate of minibatch m+1 beside the
+// down of m, so the chip is shared by two steps and a step needs fewer items
+// of its own: there the larger tiles are kept down to a sixth of the CUs'
+// worth of items per step (measured on the same workloads: DeepSeek-V3 at
+// 512 rows 14.8 ms with 256-row tiles against 18.9 ms with 128-row tiles, at
+// 1,024 rows 12.8 ms with 320-row tiles against 16.6 ms; the mid layer at
+// 2,048 rows 1.09 against 1.69 ms; the EP-64 share at 512 rows keeps 128-row
+// tiles, 5.7 against 6.5 ms).
+RoutedTiling gemm_routed_tiling(int64_t mb_rows, int64_t max_rows, int64_t experts, int64_t I, int64_t D,
+                                bool pipeline) {
   experts = experts > 0 ? experts : 1;
+  const int64_t cus = device_compute_units();
+  const double cu = cus > 0 ? static_cast<double>(cus) : 256.0;
   const bool big_segments = max_rows >= 192 * experts;
   const int64_t items = mb_rows / kRoutedBM * ((I + 127) / 128);  // up/gate tiles are 128 columns wide
-  if (big_segments && items >= 128) return RoutedTiling{kRoutedBM, 128, 256};
-  const int64_t cus = device_compute_units();
-  const double half = cus > 0 ? 0.5 * static_cast<double>(cus) : 128.0;
+  if (big_segments && items >= (pipeline ? cu / 6.0 : 128.0)) return RoutedTiling{kRoutedBM, 128, 256};
+  const double half = pipeline ? cu / 6.0 : 0.5 * cu;
   // expert segments of one minibatch: how many experts it overlaps (b / rows
   // per expert + 1 when it is cut from a longer schedule) and their rows
   const double avg = std::max(1.0, static_cast<double>(max_rows) / static_cast<double>(experts));

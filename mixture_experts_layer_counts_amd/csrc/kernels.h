@@ -104,11 +104,12 @@ int gemm_mx_routed_bm();
 // routed rows in all over `experts` local experts, intermediate width I and
 // hidden width D: the tile height bm (the tile lists are built with it) and
 // the output columns per work item of the up/gate (gate and up columns each)
-// and of the down projection.
+// and of the down projection; `pipeline` for the persistent routed kernel.
 struct RoutedTiling {
   int bm, bn_up, bn_down;
 };
-RoutedTiling gemm_routed_tiling(int64_t mb_rows, int64_t max_rows, int64_t experts, int64_t I, int64_t D);
+RoutedTiling gemm_routed_tiling(int64_t mb_rows, int64_t max_rows, int64_t experts, int64_t I, int64_t D,
+                                bool pipeline);
 hipError_t launch_gemm(const GemmArgs& args, int epilogue, hipStream_t stream);
 int gemm_tiles_bound(int64_t rows, int groups, int bm);
 
@@ -117,7 +118,8 @@ int gemm_tiles_bound(int64_t rows, int groups, int bm);
 // `up` and `down` are minibatch 0's GEMM arguments (tiles, tile_count of
 // minibatch 0; the kernel steps them by minibatch); h holds two buffers of
 // b * I bf16 (minibatch m uses buffer m mod 2).  gathered / upg / down_done
-// count finished work per minibatch and must be zero at launch.  Minibatches
+// count finished work per minibatch, upg_tile per row tile; all must be zero
+// at launch.  Minibatches
 // below C / b are gathered before the launch; n_mem workgroups (a multiple of
 // 8) gather the others.
 struct PipeArgs {
@@ -131,6 +133,7 @@ struct PipeArgs {
   uint16_t* ring;
   uint16_t* h;
   int *gathered, *upg, *down_done;
+  int* upg_tile;  // [n_mb][up.max_tiles]: finished up/gate items of each row tile
   int* err;
 };
 // Workgroups the persistent kernel runs with for a tiling (all resident).

@@ -32,7 +32,7 @@ struct Layout {
   int max_tiles;
   int routed_bm;      // tile height of the routed GEMMs' tile lists
   int bn_up, bn_down;  // output columns per work item of the routed bf16 GEMMs
-  size_t pipe_counters;  // pipeline == 1: 3 * n_minibatches ints
+  size_t pipe_counters;  // pipeline == 1: (3 + max_tiles) * n_minibatches ints
   int64_t y_rows;
 };
 
@@ -111,7 +111,8 @@ Layout layout_of(const moe_shape* s) {
   const int64_t mb_rows = std::min<int64_t>(s->minibatch_rows, std::max<int64_t>(s->max_rows, 1));
   const moe::RoutedTiling tiling = s->precision == MOE_MXFP8
                                        ? moe::RoutedTiling{moe::gemm_mx_routed_bm(), 0, 0}
-                                       : moe::gemm_routed_tiling(mb_rows, s->max_rows, Lx, s->I, s->D);
+                                       : moe::gemm_routed_tiling(mb_rows, s->max_rows, Lx, s->I, s->D,
+                                                                 s->pipeline != 0);
   const int bm = tiling.bm;
   L.routed_bm = bm;
   L.bn_up = tiling.bn_up;
@@ -141,7 +142,8 @@ Layout layout_of(const moe_shape* s) {
     // the persistent kernel overlaps minibatch m+1's up/gate with m's down: two h buffers
     L.h = take(sizeof(uint16_t) * s->minibatch_rows * s->I * (s->pipeline ? 2 : 1));
   }
-  L.pipe_counters = take(s->pipeline ? sizeof(int32_t) * 3 * std::max<int64_t>(L.n_minibatches, 1) : 0);
+  L.pipe_counters = take(s->pipeline ? sizeof(int32_t) * (3 + L.max_tiles) * std::max<int64_t>(L.n_minibatches, 1)
+                                     : 0);
   L.Y = take(sizeof(uint16_t) * L.y_rows * s->D);
   L.shared_out = take(sizeof(float) * s->T * s->D);
   if (s->shared_precision == MOE_MXFP8) {  // x and h of the shared expert in E4M3 + stage-major E8M0
@@ -656,7 +658,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     // the persistent kernel gathers the rest while it runs the GEMMs
     const int64_t pre = std::min<int64_t>(C / b, L.n_minibatches);
     int32_t* counters = at<int32_t>(ws, L.pipe_counters);
-    MOE_TRY_HIP(moe::launch_clear_int(counters, static_cast<int>(3 * L.n_minibatches), s));
+    MOE_TRY_HIP(moe::launch_clear_int(counters, static_cast<int>((3 + L.max_tiles) * L.n_minibatches), s));
     for (int64_t m = 0; m < pre; ++m) MOE_TRY_HIP(gather(m));
     moe::PipeArgs pa{};
     pa.up = up_args(0, h);
@@ -678,6 +680,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     pa.gathered = counters;
     pa.upg = counters + L.n_minibatches;
     pa.down_done = counters + 2 * L.n_minibatches;
+    pa.upg_tile = counters + 3 * L.n_minibatches;
     pa.err = at<int>(ws, L.err);
     {
       ProbeScope probe(MOE_K_PIPELINE, s);
