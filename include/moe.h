@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum {
   MOE_OK = 0,
@@ -239,6 +239,77 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ---- Backward pass (one GPU: num_src_ranks == 1; bf16 routed and shared) ----
+ *
+ * The gradients of the layer for an output gradient dout (MoK paper §2.1 MoE
+ * equation; §3.1: the dispatch table read in reverse; §3.3 "Ring-Aware
+ * Forward Replay": the up/gate projections are recomputed, not kept; §3.4
+ * "Router Weight Gradient Computation": the gate gradients <dout, y> from the
+ * routed rows the forward stored).  With g the renormalised gates:
+ *   dg_s = <dout, y_s>,  dy_s = g_s dout,  dl_s = g_s (dg_s - sum g dg)
+ *   per expert: a_g = W_gate x, a_u = W_up x (replayed, stored bf16),
+ *     dh = W_down^T dy, da_g = dh a_u SiLU'(a_g), da_u = dh SiLU(a_g) (bf16),
+ *     dx += W_gate^T da_g + W_up^T da_u, dW_down += dy h^T,
+ *     dW_gate += da_g x^T, dW_up += da_u x^T   (h = SiLU(a_g) a_u, bf16)
+ *   the shared expert the same with dy = dout; the router: dx += W_r^T dl,
+ *   dW_r = dl x^T (dl stored bf16 for these two products).
+ * Every sum runs in a fixed order: results are bitwise repeatable.
+ */
+
+/* The weights rearranged for the backward (caller-allocated device memory,
+ * filled once per weight set by moe_backward_prepare; bf16):
+ *   w_gu [L, 2I, D]: W_gate and W_up of each expert stacked (the replay's
+ *     operand); w_gu_t [L, D, 2I]: [W_gate^T | W_up^T]; w_down_t [L, I, D];
+ *   ws_gu [2I_s, D], ws_gu_t [D, 2I_s], ws_down_t [I_s, D]: the shared expert;
+ *   w_router_t [D, Ep]: W_r^T with Ep = E_total rounded up to 64 (zero past
+ *     E_total). */
+typedef struct {
+  void *w_gu, *w_gu_t, *w_down_t;
+  void *ws_gu, *ws_gu_t, *ws_down_t;
+  void* w_router_t;
+} moe_bwd_weights;
+
+/* Gradient outputs (caller-allocated device memory): dx [T, D] fp32;
+ * dw_gate, dw_up [L, I, D], dw_down [L, D, I] bf16; dws_gate, dws_up
+ * [I_s, D], dws_down [D, I_s] bf16; dw_router [E_total, D] fp32. */
+typedef struct {
+  float* dx;
+  void *dw_gate, *dw_up, *dw_down;
+  void *dws_gate, *dws_up, *dws_down;
+  float* dw_router;
+} moe_grads;
+
+/* Fill `bw` from the forward's weights and the router weights (transposes and
+ * copies on `stream`, run once per weight set).  MOE_ERR_UNSUPPORTED unless
+ * num_src_ranks == 1 and both precisions are MOE_BF16. */
+moe_status moe_backward_prepare(const moe_shape* shape, const moe_weights* weights, const void* w_router,
+                                const moe_bwd_weights* bw, void* stream);
+
+/* Bytes of device workspace moe_backward needs (a separate allocation from
+ * the forward's: about 140 bytes per routed row and hidden column at the
+ * DeepSeek-V3 shape, 9 GB). */
+moe_status moe_backward_workspace_bytes(const moe_shape* shape, size_t* bytes);
+
+/*
+ * The backward pass, for the tokens of one moe_route + moe_schedule +
+ * moe_forward (R == 1).
+ *   x          [T, D] bf16, the forward's input
+ *   topk_idx, topk_gate, expert_offsets, sched_src, route_dst: as moe_route
+ *              and moe_schedule produced them for that forward
+ *   y_routes   [T*k, D] bf16: the forward's routed rows (moe_routed_rows of
+ *              its workspace)
+ *   dout       [T, D] bf16: the output gradient
+ *   grads      the outputs (every one written)
+ *   dev_error  device int32, caller-owned: MOE_DEVERR_* bits are OR-ed in
+ * Shapes are validated before any launch, as for the forward; every GEMM
+ * operand of the backward must stay below 2^31 bytes (MOE_ERR_UNSUPPORTED).
+ */
+moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const void* x, const int32_t* topk_idx,
+                        const float* topk_gate, const int32_t* expert_offsets, const int32_t* sched_src,
+                        const int32_t* route_dst, const void* y_routes, const void* dout, const moe_grads* grads,
+                        int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Where moe_forward leaves the routed output rows inside the workspace (bf16,
  * row stride D): with R == 1, [T*k, D] indexed by route t*k + s; with R > 1,
  * the outbox [max_rows, D] indexed by schedule position p (rows >= P are not
@@ -300,7 +371,10 @@ typedef enum {
   MOE_K_COMBINE = 9,     /* gate-weighted combine */
   MOE_K_PIPELINE = 10,   /* pipeline == 1: the persistent routed kernel (gathers
                             of minibatches C/b and later, up/gate, down) */
-  MOE_K_COUNT = 11
+  MOE_K_BWD_REPLAY = 11, /* moe_backward: up/gate replay of the routed rows */
+  MOE_K_BWD_DGRAD = 12,  /* moe_backward: the routed data-gradient GEMMs (dh, dx) */
+  MOE_K_BWD_WGRAD = 13,  /* moe_backward: the routed weight-gradient GEMMs */
+  MOE_K_COUNT = 14
 } moe_kernel_id;
 
 moe_status moe_probe_begin(int32_t kernel_id, int32_t max_launches);

@@ -20,7 +20,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
 MOE_BF16, MOE_MXFP8 = 0, 1
 DEVERR_EXPERT_RANGE, DEVERR_ROW_OVERFLOW, DEVERR_NONFINITE, DEVERR_PIPELINE = 0x1, 0x2, 0x4, 0x8
 KERNELS = {"router_gemm": 0, "topk": 1, "schedule": 2, "tiles": 3, "shared_up": 4, "shared_down": 5, "gather": 6,
-           "up_gate": 7, "down": 8, "combine": 9, "pipeline": 10}
+           "up_gate": 7, "down": 8, "combine": 9, "pipeline": 10, "bwd_replay": 11, "bwd_dgrad": 12,
+           "bwd_wgrad": 13}
 
 
 class MoeShape(ctypes.Structure):
@@ -35,6 +36,16 @@ class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "ws_gate", "ws_up", "ws_down", "ss_gate", "ss_up",
         "ss_down")]
+
+
+class MoeBwdWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_gu", "w_gu_t", "w_down_t", "ws_gu", "ws_gu_t", "ws_down_t",
+                                              "w_router_t")]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dx", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down",
+                                              "dw_router")]
 
 
 class MoeError(RuntimeError):
@@ -60,6 +71,11 @@ _SIGS = {
     "moe_mxfp8_pack_scales": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P]),
     "moe_get_device_error": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_size_t, _P,
                                             ctypes.POINTER(ctypes.c_int32)]),
+    "moe_backward_prepare": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _P,
+                                            ctypes.POINTER(MoeBwdWeights), _P]),
+    "moe_backward_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_backward": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeBwdWeights), _P, _P, _P, _P, _P, _P,
+                                    _P, _P, ctypes.POINTER(MoeGrads), _P, _P, ctypes.c_size_t, _P]),
     "moe_probe_begin": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32]),
     "moe_probe_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),

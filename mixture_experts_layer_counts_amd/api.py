@@ -214,6 +214,82 @@ def schedule_static(shape: _lib.MoeShape, routes: torch.Tensor, dev_error: torch
     return out
 
 
+def _weights_struct(shape: _lib.MoeShape, weights: Dict[str, torch.Tensor], dev) -> _lib.MoeWeights:
+    L, D, I, Is = shape.experts_per_rank, shape.D, shape.I, shape.I_shared
+    w = _lib.MoeWeights()
+    for n, shp in (("w_gate", (L, I, D)), ("w_up", (L, I, D)), ("w_down", (L, D, I)), ("ws_gate", (Is, D)),
+                   ("ws_up", (Is, D)), ("ws_down", (D, Is))):
+        _need(weights[n], n, torch.bfloat16, shp, dev)
+        setattr(w, n, _ptr(weights[n]))
+    return w
+
+
+def prepare_backward(shape: _lib.MoeShape, weights: Dict[str, torch.Tensor], w_router: torch.Tensor
+                     ) -> Dict[str, torch.Tensor]:
+    """The weights rearranged for moe_backward (moe_backward_prepare), once per
+    weight set: w_gu, w_gu_t, w_down_t, ws_gu, ws_gu_t, ws_down_t, w_router_t."""
+    lib = _lib.load()
+    dev = w_router.device
+    L, D, I, Is, E = shape.experts_per_rank, shape.D, shape.I, shape.I_shared, shape.E_total
+    Ep = (E + 63) // 64 * 64
+    w = _weights_struct(shape, weights, dev)
+    _need(w_router, "w_router", torch.bfloat16, (E, D), dev)
+    out = {"w_gu": (L, 2 * I, D), "w_gu_t": (L, D, 2 * I), "w_down_t": (L, I, D), "ws_gu": (2 * Is, D),
+           "ws_gu_t": (D, 2 * Is), "ws_down_t": (Is, D), "w_router_t": (D, Ep)}
+    out = {n: torch.empty(shp, dtype=torch.bfloat16, device=dev) for n, shp in out.items()}
+    bw = _lib.MoeBwdWeights(*[_ptr(out[n]) for n, _ in _lib.MoeBwdWeights._fields_])
+    _lib.check("moe_backward_prepare", lib.moe_backward_prepare(ctypes.byref(shape), ctypes.byref(w), _ptr(w_router),
+                                                                ctypes.byref(bw), _stream()))
+    return out
+
+
+class MoEBackward:
+    """The workspace of moe_backward for one layer shape, on ``device``."""
+
+    def __init__(self, shape: _lib.MoeShape, device="cuda"):
+        self.lib = _lib.load()
+        self.shape = shape
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        nbytes = ctypes.c_size_t(0)
+        _lib.check("moe_backward_workspace_bytes",
+                   self.lib.moe_backward_workspace_bytes(ctypes.byref(shape), ctypes.byref(nbytes)))
+        self.ws_bytes = nbytes.value
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=self.device)
+        self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
+
+    def __call__(self, bw: Dict[str, torch.Tensor], x: torch.Tensor, idx: torch.Tensor, gate: torch.Tensor,
+                 sched: Dict[str, torch.Tensor], y_routes: torch.Tensor, dout: torch.Tensor,
+                 grads: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+        s, dev = self.shape, self.device
+        T, D, I, Is, E, k, L = s.T, s.D, s.I, s.I_shared, s.E_total, s.k, s.experts_per_rank
+        _need(x, "x", torch.bfloat16, (T, D), dev)
+        _need(dout, "dout", torch.bfloat16, (T, D), dev)
+        _need(idx, "idx", torch.int32, (T, k), dev)
+        _need(gate, "gate", torch.float32, (T, k), dev)
+        _need(y_routes, "y_routes", torch.bfloat16, (T * k, D), dev)
+        shapes = {"dx": ((T, D), torch.float32), "dw_gate": ((L, I, D), torch.bfloat16),
+                  "dw_up": ((L, I, D), torch.bfloat16), "dw_down": ((L, D, I), torch.bfloat16),
+                  "dws_gate": ((Is, D), torch.bfloat16), "dws_up": ((Is, D), torch.bfloat16),
+                  "dws_down": ((D, Is), torch.bfloat16), "dw_router": ((E, D), torch.float32)}
+        if grads is None:
+            grads = {n: torch.empty(shp, dtype=dt, device=dev) for n, (shp, dt) in shapes.items()}
+        for n, (shp, dt) in shapes.items():
+            _need(grads[n], n, dt, shp, dev)
+        g = _lib.MoeGrads(*[_ptr(grads[n]) for n, _ in _lib.MoeGrads._fields_])
+        b = _lib.MoeBwdWeights(*[_ptr(bw[n]) for n, _ in _lib.MoeBwdWeights._fields_])
+        _lib.check("moe_backward", self.lib.moe_backward(
+            ctypes.byref(s), ctypes.byref(b), _ptr(x), _ptr(idx), _ptr(gate), _ptr(sched["offsets"]),
+            _ptr(sched["sched"]), _ptr(sched["route_dst"]), _ptr(y_routes), _ptr(dout), ctypes.byref(g),
+            _ptr(self.err), _ptr(self.ws), self.ws_bytes, _stream()))
+        return grads
+
+    def device_error(self) -> int:
+        torch.cuda.current_stream().synchronize()
+        return int(self.err.item())
+
+
 def quantize_mxfp8(src: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     """MX-quantise a bf16 tensor along its last axis (moe_quantize_mxfp8)."""
     lib = _lib.load()

@@ -251,7 +251,7 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
   const int lane = tid & (kWave - 1), wave = kItemLoop ? wave0 : __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
 
-  int e = 0, nrows, tile, nb, ks = 0;
+  int e = 0, nrows, tile, nb, ks = 0, group = 0;
   int64_t p0;
   if constexpr (ROUTED) {
     // a tile of the expert group that owns item w
@@ -268,6 +268,11 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
     // dense: row tile outer, so the workgroups of one XCD share activation
     // rows in L2 and stream the (small) weight matrix; the K ranges of one
     // output tile are neighbours
+    if (args.k_groups) {  // grouped K: the group's items are contiguous
+      const int per = ((args.dense_rows + BM - 1) / BM) * n_blocks;
+      group = w / per;
+      w -= group * per;
+    }
     ks = w % S;
     nb = (w / S) % n_blocks;
     tile = w / S / n_blocks;
@@ -276,8 +281,16 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
   }
   const int n0 = nb * BN;
   const int K = args.K;
-  const int k0 = ks * (K / S);  // first K element of this workgroup's range
-  char* const cbase = static_cast<char*>(args.C) + ks * args.c_split_stride * (EPI == kEpiF32 ? 4 : 2);
+  int k0 = ks * (K / S);  // first K element of this workgroup's range
+  int nk = K / S / BK;    // its K stages
+  if (!ROUTED && args.k_groups) {
+    const int2 kg = args.k_groups[group];
+    k0 = kg.x;
+    nk = kg.y;
+  }
+  const int64_t ldb = args.ldb ? args.ldb : K;
+  char* const cbase = static_cast<char*>(args.C) +
+                      (ks * args.c_split_stride + group * args.c_group_stride) * (EPI == kEpiF32 ? 4 : 2);
 
   // ---- byte offsets of the 16-byte chunks this lane fetches ----
   // Direct load j of wave w fills rows ROWS_PER_LD (w * AI + j) + lane / CH of
@@ -303,13 +316,13 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
     const int half = row / BN;
     int n = n0 + (row - half * BN);
     n = n < args.N ? n : args.N - 1;
-    b_off[j] = static_cast<uint32_t>((static_cast<int64_t>(n) * K + k0 + c * 8) * 2);
+    b_off[j] = static_cast<uint32_t>((static_cast<int64_t>(n) * ldb + k0 + c * 8) * 2);
   }
   constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
   TileSrc src;
   src.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(args.A), 0, static_cast<int>(args.a_bytes),
                                             kRsrcWord3);
-  const int b_bytes = args.N * K * 2;
+  const int b_bytes = static_cast<int>(args.N * ldb * 2);
   src.b0 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(args.B0 + static_cast<int64_t>(e) * args.b_expert_stride), 0, b_bytes, kRsrcWord3);
   src.b1 = NB == 2 ? __builtin_amdgcn_make_buffer_rsrc(
@@ -328,8 +341,9 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
   // K loop is instantiated per count so that its body is one straight block
   int fm_live = ((nrows + 31) / 32 - wm + WM - 1) / WM;
   fm_live = fm_live < 0 ? 0 : (fm_live > FM ? FM : fm_live);
-  const int nk = K / S / BK;
-  switch (fm_live) {
+  // an empty K range (a grouped-K group with no rows) skips the K loop: its
+  // accumulators stay zero and the epilogue stores zeros
+  switch (nk > 0 ? fm_live : -1) {
 #define MOE_CASE(n)                                                                       \
   case n:                                                                                 \
     if constexpr (n <= FM)                                                                \
@@ -456,7 +470,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args)
   const int n_blocks = (args.N + BN - 1) / BN;
   const int tcount = ROUTED ? *args.tile_count : (args.dense_rows + BM - 1) / BM;
   const int S = ROUTED ? 1 : args.k_splits;  // K ranges (dense only), each with its own output plane
-  const int W = tcount * n_blocks * S;
+  const int W = tcount * n_blocks * S * (!ROUTED && args.k_groups ? args.n_groups : 1);
   const int chunk = (W + kXcds - 1) / kXcds;
   const int run0 = (static_cast<int>(blockIdx.x) % kXcds) * chunk;
   const int first = static_cast<int>(blockIdx.x) / kXcds;
@@ -479,7 +493,7 @@ template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK = kStageK
 hipError_t run(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles = ROUTED ? a.max_tiles : (a.dense_rows + BM - 1) / BM;
   const int64_t n_blocks = (a.N + BN - 1) / BN;
-  const int64_t work = tiles * n_blocks * (ROUTED ? 1 : a.k_splits);
+  const int64_t work = tiles * n_blocks * (ROUTED ? 1 : a.k_splits) * (!ROUTED && a.k_groups ? a.n_groups : 1);
   if (work <= 0) return hipSuccess;
   if (work > 0x7ffffff0) return hipErrorInvalidValue;
   auto kernel = gemm_kernel<BM, BN, WM, WN, EPI, ROUTED, BK>;
@@ -806,10 +820,13 @@ int gemm_tiles_bound(int64_t rows, int groups, int bm) {
 hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t stream) {
   const bool routed = a.tiles != nullptr;
   if (a.N <= 0 || a.k_splits < 1 || (routed && a.k_splits != 1)) return hipErrorInvalidValue;
-  if (a.K % (kStageK * a.k_splits) != 0) return hipErrorInvalidValue;
+  if (a.k_groups && (routed || a.k_splits != 1 || a.n_groups < 1)) return hipErrorInvalidValue;
+  if (!a.k_groups && a.K % (kStageK * a.k_splits) != 0) return hipErrorInvalidValue;
+  const int64_t ldb = a.ldb ? a.ldb : a.K;
+  if (ldb % 8 != 0) return hipErrorInvalidValue;  // 16-byte aligned B rows
   // buffer resources address at most 2^31 bytes per operand here
   if (a.a_bytes <= 0 || a.a_bytes >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  if (static_cast<int64_t>(a.N) * a.K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (static_cast<int64_t>(a.N) * ldb * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   if (routed && a.tile_rows != kRoutedBM && a.tile_rows != kSmallBM && a.tile_rows != kShortBM)
     return hipErrorInvalidValue;
   const bool big = routed && a.tile_rows == kRoutedBM;

@@ -67,6 +67,13 @@ struct GemmArgs {
   int max_tiles;
   int k_splits;            // dense only: K is cut into this many equal ranges, one output plane each
   int64_t c_split_stride;  // elements between the output planes of the K ranges
+  int64_t ldb;             // B row stride in elements (0: K)
+  // Dense only, grouped K: group g multiplies K elements [k_groups[g].x,
+  // + 64 * k_groups[g].y) of the A and B rows (a zero count gives zeros) into
+  // its own output block at C + g * c_group_stride; k_splits must be 1.
+  const int2* k_groups;
+  int n_groups;
+  int64_t c_group_stride;
 };
 
 // Grouped MXFP8 GEMM over a tile list (routed experts, or a dense GEMM through
@@ -139,6 +146,37 @@ struct PipeArgs {
 // Workgroups the persistent kernel runs with for a tiling (all resident).
 int pipeline_workgroups(const RoutedTiling& tiling);
 hipError_t launch_pipeline(const PipeArgs& args, const RoutedTiling& tiling, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Backward pass (backward.hip)
+// ---------------------------------------------------------------------------
+// dY[p] = bf16(gate[j] * dout[j / k]) for j = sched_src[p], p < P
+hipError_t launch_dy_gather(const uint16_t* dout, const float* gate, const int32_t* sched_src, int64_t P, int T, int D,
+                            int k, uint16_t* dy, int* err, hipStream_t s);
+// dg[j] = <dout[j / k], y[j]> (fp32, fixed order) for the n_routes routes
+hipError_t launch_route_grad(const uint16_t* dout, const uint16_t* y, int64_t n_routes, int D, int k, float* dg,
+                             hipStream_t s);
+// dl [T][ld] bf16: g_s (dg_s - sum g dg) at the selected experts, zero elsewhere
+hipError_t launch_gate_grad(const float* gate, const float* dg, const int32_t* idx, int T, int E, int ld, int k,
+                            uint16_t* dl, hipStream_t s);
+// act [rows][2I] = [a_g | a_u], dh [rows][I] fp32 -> h [rows][I], da [rows][2I] = [da_g | da_u] (bf16)
+hipError_t launch_swiglu_bwd(const uint16_t* act, const float* dh, int64_t rows, int I, uint16_t* h, uint16_t* da,
+                             hipStream_t s);
+// segments of offsets[] padded to 64 rows: padded [L+1], k_groups [L] = {padded[e], stages}
+hipError_t launch_pad_offsets(const int32_t* offsets, int L, int32_t* padded, int2* k_groups, hipStream_t s);
+// out [W][ld_out]: column padded[e] + i = row offsets[e] + i of src [.][lda] (zero past the segment)
+hipError_t launch_seg_transpose(const uint16_t* src, int64_t lda, int W, const int32_t* offsets,
+                                const int32_t* padded, int L, int64_t max_cols, uint16_t* out, int64_t ld_out,
+                                hipStream_t s);
+// offsets {0, rows}, padded {0, ceil64(rows)}, k_groups[0] = {0, ceil(rows / 64)} for one dense segment
+hipError_t launch_single_segment(int rows, int32_t* offsets, int32_t* padded, int2* k_groups, hipStream_t s);
+// out[b][c][col0 + r] = in[b][r][c], in [B][R][Cn] contiguous, out rows ld_out, batches out_b apart
+hipError_t launch_transpose(const uint16_t* in, int B, int R, int Cn, uint16_t* out, int64_t ld_out, int64_t out_b,
+                            int col0, hipStream_t s);
+// dx[t] = dx_shared[t] + dx_router[t] + sum_s dx_ring[route_dst[t k + s]] (fp32, in that order)
+hipError_t launch_dx_assemble(const float* dx_shared, const float* dx_router, const float* dx_ring,
+                              const int32_t* route_dst, int T, int D, int k, int64_t P, float* dx, int* err,
+                              hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Data movement

@@ -795,3 +795,308 @@ moe_status moe_get_device_error(const moe_shape* shape, const void* ws, size_t w
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward pass
+// ---------------------------------------------------------------------------
+namespace {
+
+int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
+
+struct BwdLayout {
+  size_t tiles, tile_count, padded, k_groups, seg_off, seg_pad, seg_kg, ring, dy, act, dh, h, da, dx_ring, dyT, hT, daT,
+      xT, dg, dl, dlT, act_s, dh_s, h_s, da_s, dx_s, doutT, h_sT, da_sT, x_T, dx_r, total;
+  int64_t P, Ppad, Tpad, Ep;
+  moe::RoutedTiling tiling;
+  int max_tiles;
+};
+
+// Backward shapes: one GPU, bf16 routed and shared experts; every GEMM
+// operand (read through a buffer resource) below 2^31 bytes.
+bool valid_bwd_shape(const moe_shape* s, moe_status* why) {
+  if (!valid_shape(s, why)) return false;
+  *why = MOE_ERR_UNSUPPORTED;
+  if (s->num_src_ranks != 1 || s->precision != MOE_BF16 || s->shared_precision != MOE_BF16) return false;
+  constexpr int64_t kLimit = int64_t(1) << 31;
+  const int64_t P = s->T * s->k, Ppad = pad64(P) + 64 * s->experts_per_rank, Tpad = pad64(s->T);
+  const int64_t Ep = pad64(s->E_total);
+  const int64_t bytes[] = {P * s->D * 2,       P * 2 * s->I * 2,         s->D * Ppad * 2,        2 * s->I * Ppad * 2,
+                           s->T * 2 * s->I_shared * 2, s->D * Tpad * 2, 2 * s->I_shared * Tpad * 2, s->T * Ep * 2,
+                           Ep * Tpad * 2,      s->D * Ep * 2,            2 * s->I * s->D * 2};
+  for (const int64_t v : bytes)
+    if (v >= kLimit) return false;
+  *why = MOE_OK;
+  return true;
+}
+
+BwdLayout bwd_layout_of(const moe_shape* s) {
+  BwdLayout L{};
+  const int64_t T = s->T, D = s->D, I = s->I, Is = s->I_shared, Lx = s->experts_per_rank;
+  L.P = T * s->k;
+  L.Ppad = pad64(L.P) + 64 * Lx;  // every segment padded to 64 rows
+  L.Tpad = pad64(T);
+  L.Ep = pad64(s->E_total);
+  L.tiling = moe::gemm_routed_tiling(L.P, L.P, Lx, I, D, false);
+  L.max_tiles = moe::gemm_tiles_bound(L.P, static_cast<int>(Lx), L.tiling.bm);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.tiles = take(sizeof(int4) * L.max_tiles);
+  L.tile_count = take(sizeof(int32_t));
+  L.padded = take(sizeof(int32_t) * (Lx + 1));
+  L.k_groups = take(sizeof(int2) * Lx);
+  L.seg_off = take(sizeof(int32_t) * 2);
+  L.seg_pad = take(sizeof(int32_t) * 2);
+  L.seg_kg = take(sizeof(int2));
+  L.ring = take(2 * L.P * D);
+  L.dy = take(2 * L.P * D);
+  L.act = take(2 * L.P * 2 * I);
+  L.dh = take(4 * L.P * I);
+  L.h = take(2 * L.P * I);
+  L.da = take(2 * L.P * 2 * I);
+  L.dx_ring = take(4 * L.P * D);
+  L.dyT = take(2 * D * L.Ppad);
+  L.hT = take(2 * I * L.Ppad);
+  L.daT = take(2 * 2 * I * L.Ppad);
+  L.xT = take(2 * D * L.Ppad);
+  L.dg = take(4 * L.P);
+  L.dl = take(2 * T * L.Ep);
+  L.dlT = take(2 * L.Ep * L.Tpad);
+  L.act_s = take(2 * T * 2 * Is);
+  L.dh_s = take(4 * T * Is);
+  L.h_s = take(2 * T * Is);
+  L.da_s = take(2 * T * 2 * Is);
+  L.dx_s = take(4 * T * D);
+  L.doutT = take(2 * D * L.Tpad);
+  L.h_sT = take(2 * Is * L.Tpad);
+  L.da_sT = take(2 * 2 * Is * L.Tpad);
+  L.x_T = take(2 * D * L.Tpad);
+  L.dx_r = take(4 * T * D);
+  L.total = off;
+  return L;
+}
+
+// C = A B^T over dense rows (M x N, K-contiguous operands), optionally with
+// grouped K ranges (groups stacked in the output `group_stride` elements
+// apart).
+moe::GemmArgs dense_args(const void* A, int64_t lda, int64_t M, const void* B, int64_t ldb, int N, int K, void* C,
+                         int64_t ldc) {
+  moe::GemmArgs g{};
+  g.k_splits = 1;
+  g.A = static_cast<const uint16_t*>(A);
+  g.a_bytes = M * lda * 2;
+  g.lda = lda;
+  g.a_sub = 0;
+  g.a_mod = INT64_MAX;
+  g.B0 = static_cast<const uint16_t*>(B);
+  g.ldb = ldb;
+  g.N = N;
+  g.K = K;
+  g.C = C;
+  g.ldc = ldc;
+  g.dense_rows = static_cast<int>(M);
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_backward_workspace_bytes(const moe_shape* shape, size_t* bytes) {
+  moe_status why;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  if (!valid_bwd_shape(shape, &why)) return why;
+  *bytes = bwd_layout_of(shape).total;
+  return MOE_OK;
+}
+
+moe_status moe_backward_prepare(const moe_shape* shape, const moe_weights* w, const void* w_router,
+                                const moe_bwd_weights* bw, void* stream) {
+  moe_status why;
+  if (!valid_bwd_shape(shape, &why)) return why;
+  if (!w || !bw || !w_router || !w->w_gate || !w->w_up || !w->w_down || !w->ws_gate || !w->ws_up || !w->ws_down)
+    return MOE_ERR_INVALID_ARG;
+  if (!bw->w_gu || !bw->w_gu_t || !bw->w_down_t || !bw->ws_gu || !bw->ws_gu_t || !bw->ws_down_t || !bw->w_router_t)
+    return MOE_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int L = static_cast<int>(shape->experts_per_rank), D = static_cast<int>(shape->D);
+  const int I = static_cast<int>(shape->I), Is = static_cast<int>(shape->I_shared), E = static_cast<int>(shape->E_total);
+  const int64_t Ep = pad64(E);
+  const size_t slab = static_cast<size_t>(I) * D * 2;  // bytes of one expert's gate (or up) matrix
+  auto* gu = static_cast<char*>(bw->w_gu);
+  // w_gu: gate rows then up rows of each expert
+  MOE_TRY_HIP(hipMemcpy2DAsync(gu, 2 * slab, w->w_gate, slab, slab, L, hipMemcpyDeviceToDevice, s));
+  MOE_TRY_HIP(hipMemcpy2DAsync(gu + slab, 2 * slab, w->w_up, slab, slab, L, hipMemcpyDeviceToDevice, s));
+  const uint16_t* wg = static_cast<const uint16_t*>(w->w_gate);
+  const uint16_t* wu = static_cast<const uint16_t*>(w->w_up);
+  const uint16_t* wd = static_cast<const uint16_t*>(w->w_down);
+  auto* gut = static_cast<uint16_t*>(bw->w_gu_t);
+  MOE_TRY_HIP(moe::launch_transpose(wg, L, I, D, gut, 2 * I, static_cast<int64_t>(D) * 2 * I, 0, s));
+  MOE_TRY_HIP(moe::launch_transpose(wu, L, I, D, gut, 2 * I, static_cast<int64_t>(D) * 2 * I, I, s));
+  MOE_TRY_HIP(moe::launch_transpose(wd, L, D, I, static_cast<uint16_t*>(bw->w_down_t), D,
+                                    static_cast<int64_t>(I) * D, 0, s));
+  const size_t sslab = static_cast<size_t>(Is) * D * 2;
+  MOE_TRY_HIP(hipMemcpyAsync(bw->ws_gu, w->ws_gate, sslab, hipMemcpyDeviceToDevice, s));
+  MOE_TRY_HIP(hipMemcpyAsync(static_cast<char*>(bw->ws_gu) + sslab, w->ws_up, sslab, hipMemcpyDeviceToDevice, s));
+  auto* sgut = static_cast<uint16_t*>(bw->ws_gu_t);
+  MOE_TRY_HIP(moe::launch_transpose(static_cast<const uint16_t*>(w->ws_gate), 1, Is, D, sgut, 2 * Is, 0, 0, s));
+  MOE_TRY_HIP(moe::launch_transpose(static_cast<const uint16_t*>(w->ws_up), 1, Is, D, sgut, 2 * Is, 0, Is, s));
+  MOE_TRY_HIP(moe::launch_transpose(static_cast<const uint16_t*>(w->ws_down), 1, D, Is,
+                                    static_cast<uint16_t*>(bw->ws_down_t), D, 0, 0, s));
+  // W_r^T with its columns past E_total zero
+  MOE_TRY_HIP(moe::launch_clear_int(static_cast<int*>(bw->w_router_t), static_cast<int>(D * Ep / 2), s));
+  MOE_TRY_HIP(moe::launch_transpose(static_cast<const uint16_t*>(w_router), 1, E, D,
+                                    static_cast<uint16_t*>(bw->w_router_t), Ep, 0, 0, s));
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const void* x, const int32_t* topk_idx,
+                        const float* topk_gate, const int32_t* expert_offsets, const int32_t* sched_src,
+                        const int32_t* route_dst, const void* y_routes, const void* dout, const moe_grads* g,
+                        int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
+  moe_status why;
+  if (!valid_bwd_shape(shape, &why)) return why;
+  const BwdLayout L = bwd_layout_of(shape);
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!bw || !g || !dev_error || !x || !topk_idx || !topk_gate || !expert_offsets || !sched_src || !route_dst ||
+      !y_routes || !dout)
+    return MOE_ERR_INVALID_ARG;
+  if (!bw->w_gu || !bw->w_gu_t || !bw->w_down_t || !bw->ws_gu || !bw->ws_gu_t || !bw->ws_down_t || !bw->w_router_t)
+    return MOE_ERR_INVALID_ARG;
+  if (!g->dx || !g->dw_gate || !g->dw_up || !g->dw_down || !g->dws_gate || !g->dws_up || !g->dws_down ||
+      !g->dw_router)
+    return MOE_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = static_cast<int>(shape->T), D = static_cast<int>(shape->D), I = static_cast<int>(shape->I);
+  const int Is = static_cast<int>(shape->I_shared), k = static_cast<int>(shape->k);
+  const int E = static_cast<int>(shape->E_total), Lx = static_cast<int>(shape->experts_per_rank);
+  const int64_t P = L.P, Ppad = L.Ppad, Tpad = L.Tpad, Ep = L.Ep;
+  if (T == 0) return MOE_OK;
+  int4* tiles = at<int4>(ws, L.tiles);
+  int32_t* tile_count = at<int32_t>(ws, L.tile_count);
+  uint16_t* ring = at<uint16_t>(ws, L.ring);
+  uint16_t* dy = at<uint16_t>(ws, L.dy);
+  uint16_t* act = at<uint16_t>(ws, L.act);
+  float* dh = at<float>(ws, L.dh);
+  uint16_t* h = at<uint16_t>(ws, L.h);
+  uint16_t* da = at<uint16_t>(ws, L.da);
+  float* dx_ring = at<float>(ws, L.dx_ring);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* dob = static_cast<const uint16_t*>(dout);
+
+  // ---- routed experts: the forward's rows again, in schedule order ----
+  MOE_TRY_HIP(moe::launch_build_tiles(expert_offsets, Lx, P, P, L.tiling.bm, 1, L.max_tiles, tiles, tile_count, s));
+  MOE_TRY_HIP(moe::launch_gather_src(xb, T, D, k, route_dst, P, P, ring, dev_error, s));
+  MOE_TRY_HIP(moe::launch_dy_gather(dob, topk_gate, sched_src, P, T, D, k, dy, dev_error, s));
+  auto routed = [&](const void* A, int64_t lda, const void* B, int64_t b_stride, int N, int K, void* C, int64_t ldc) {
+    moe::GemmArgs a{};
+    a.k_splits = 1;
+    a.A = static_cast<const uint16_t*>(A);
+    a.a_bytes = P * lda * 2;
+    a.lda = lda;
+    a.a_sub = 0;
+    a.a_mod = INT64_MAX;
+    a.B0 = static_cast<const uint16_t*>(B);
+    a.b_expert_stride = b_stride;
+    a.N = N;
+    a.K = K;
+    a.C = C;
+    a.ldc = ldc;
+    a.tiles = tiles;
+    a.tile_count = tile_count;
+    a.max_tiles = L.max_tiles;
+    a.tile_rows = L.tiling.bm;
+    a.tile_cols = 256;
+    return a;
+  };
+  {
+    ProbeScope probe(MOE_K_BWD_REPLAY, s);  // act = [a_g | a_u] of every routed row
+    MOE_TRY_HIP(moe::launch_gemm(routed(ring, D, bw->w_gu, int64_t(2) * I * D, 2 * I, D, act, 2 * I),
+                                 moe::kEpiBF16, s));
+  }
+  {
+    ProbeScope probe(MOE_K_BWD_DGRAD, s);  // dh = dY W_down, then dx_ring = da [W_gate; W_up]
+    MOE_TRY_HIP(moe::launch_gemm(routed(dy, D, bw->w_down_t, int64_t(I) * D, I, D, dh, I), moe::kEpiF32, s));
+    MOE_TRY_HIP(moe::launch_swiglu_bwd(act, dh, P, I, h, da, s));
+    MOE_TRY_HIP(moe::launch_gemm(routed(da, 2 * I, bw->w_gu_t, int64_t(D) * 2 * I, D, 2 * I, dx_ring, D),
+                                 moe::kEpiF32, s));
+  }
+  {
+    // weight gradients: per expert, K = its rows (padded to 64 with zeros)
+    ProbeScope probe(MOE_K_BWD_WGRAD, s);
+    int32_t* padded = at<int32_t>(ws, L.padded);
+    int2* kg = at<int2>(ws, L.k_groups);
+    uint16_t* dyT = at<uint16_t>(ws, L.dyT);
+    uint16_t* hT = at<uint16_t>(ws, L.hT);
+    uint16_t* daT = at<uint16_t>(ws, L.daT);
+    uint16_t* xT = at<uint16_t>(ws, L.xT);
+    MOE_TRY_HIP(moe::launch_pad_offsets(expert_offsets, Lx, padded, kg, s));
+    MOE_TRY_HIP(moe::launch_seg_transpose(dy, D, D, expert_offsets, padded, Lx, Ppad, dyT, Ppad, s));
+    MOE_TRY_HIP(moe::launch_seg_transpose(h, I, I, expert_offsets, padded, Lx, Ppad, hT, Ppad, s));
+    MOE_TRY_HIP(moe::launch_seg_transpose(da, 2 * I, 2 * I, expert_offsets, padded, Lx, Ppad, daT, Ppad, s));
+    MOE_TRY_HIP(moe::launch_seg_transpose(ring, D, D, expert_offsets, padded, Lx, Ppad, xT, Ppad, s));
+    auto grouped = [&](const uint16_t* A, int64_t M, const uint16_t* B, int N, void* C, int64_t ldc, int64_t gs) {
+      moe::GemmArgs a = dense_args(A, Ppad, M, B, Ppad, N, 0, C, ldc);
+      a.k_groups = kg;
+      a.n_groups = Lx;
+      a.c_group_stride = gs;
+      return a;
+    };
+    MOE_TRY_HIP(moe::launch_gemm(grouped(dyT, D, hT, I, g->dw_down, I, int64_t(D) * I), moe::kEpiBF16, s));
+    MOE_TRY_HIP(moe::launch_gemm(grouped(daT, I, xT, D, g->dw_gate, D, int64_t(I) * D), moe::kEpiBF16, s));
+    MOE_TRY_HIP(moe::launch_gemm(grouped(daT + I * Ppad, I, xT, D, g->dw_up, D, int64_t(I) * D), moe::kEpiBF16, s));
+  }
+
+  // ---- the shared expert, on every token with dy = dout ----
+  uint16_t* act_s = at<uint16_t>(ws, L.act_s);
+  float* dh_s = at<float>(ws, L.dh_s);
+  uint16_t* h_s = at<uint16_t>(ws, L.h_s);
+  uint16_t* da_s = at<uint16_t>(ws, L.da_s);
+  float* dx_s = at<float>(ws, L.dx_s);
+  MOE_TRY_HIP(moe::launch_gemm(dense_args(xb, D, T, bw->ws_gu, 0, 2 * Is, D, act_s, 2 * Is), moe::kEpiBF16, s));
+  MOE_TRY_HIP(moe::launch_gemm(dense_args(dob, D, T, bw->ws_down_t, 0, Is, D, dh_s, Is), moe::kEpiF32, s));
+  MOE_TRY_HIP(moe::launch_swiglu_bwd(act_s, dh_s, T, Is, h_s, da_s, s));
+  MOE_TRY_HIP(moe::launch_gemm(dense_args(da_s, 2 * Is, T, bw->ws_gu_t, 0, D, 2 * Is, dx_s, D), moe::kEpiF32, s));
+  int32_t* seg_off = at<int32_t>(ws, L.seg_off);
+  int32_t* seg_pad = at<int32_t>(ws, L.seg_pad);
+  int2* seg_kg = at<int2>(ws, L.seg_kg);
+  uint16_t* doutT = at<uint16_t>(ws, L.doutT);
+  uint16_t* h_sT = at<uint16_t>(ws, L.h_sT);
+  uint16_t* da_sT = at<uint16_t>(ws, L.da_sT);
+  uint16_t* x_T = at<uint16_t>(ws, L.x_T);
+  MOE_TRY_HIP(moe::launch_single_segment(T, seg_off, seg_pad, seg_kg, s));
+  MOE_TRY_HIP(moe::launch_seg_transpose(dob, D, D, seg_off, seg_pad, 1, Tpad, doutT, Tpad, s));
+  MOE_TRY_HIP(moe::launch_seg_transpose(h_s, Is, Is, seg_off, seg_pad, 1, Tpad, h_sT, Tpad, s));
+  MOE_TRY_HIP(moe::launch_seg_transpose(da_s, 2 * Is, 2 * Is, seg_off, seg_pad, 1, Tpad, da_sT, Tpad, s));
+  MOE_TRY_HIP(moe::launch_seg_transpose(xb, D, D, seg_off, seg_pad, 1, Tpad, x_T, Tpad, s));
+  auto one_group = [&](const uint16_t* A, int64_t M, const uint16_t* B, int N, void* C, int64_t ldc) {
+    moe::GemmArgs a = dense_args(A, Tpad, M, B, Tpad, N, 0, C, ldc);
+    a.k_groups = seg_kg;
+    a.n_groups = 1;
+    return a;
+  };
+  MOE_TRY_HIP(moe::launch_gemm(one_group(doutT, D, h_sT, Is, g->dws_down, Is), moe::kEpiBF16, s));
+  MOE_TRY_HIP(moe::launch_gemm(one_group(da_sT, Is, x_T, D, g->dws_gate, D), moe::kEpiBF16, s));
+  MOE_TRY_HIP(moe::launch_gemm(one_group(da_sT + Is * Tpad, Is, x_T, D, g->dws_up, D), moe::kEpiBF16, s));
+
+  // ---- router: gate gradients, the selected logits' gradient, its two products ----
+  float* dg = at<float>(ws, L.dg);
+  uint16_t* dl = at<uint16_t>(ws, L.dl);
+  uint16_t* dlT = at<uint16_t>(ws, L.dlT);
+  float* dx_r = at<float>(ws, L.dx_r);
+  MOE_TRY_HIP(moe::launch_route_grad(dob, static_cast<const uint16_t*>(y_routes), P, D, k, dg, s));
+  MOE_TRY_HIP(moe::launch_gate_grad(topk_gate, dg, topk_idx, T, E, static_cast<int>(Ep), k, dl, s));
+  MOE_TRY_HIP(moe::launch_gemm(dense_args(dl, Ep, T, bw->w_router_t, 0, D, static_cast<int>(Ep), dx_r, D),
+                               moe::kEpiF32, s));
+  MOE_TRY_HIP(moe::launch_seg_transpose(dl, Ep, static_cast<int>(Ep), seg_off, seg_pad, 1, Tpad, dlT, Tpad, s));
+  MOE_TRY_HIP(moe::launch_gemm(one_group(dlT, E, x_T, D, g->dw_router, D), moe::kEpiF32, s));
+
+  // ---- dx, in a fixed order ----
+  return hip_status(moe::launch_dx_assemble(dx_s, dx_r, dx_ring, route_dst, T, D, k, P, g->dx, dev_error, s));
+}
+
+}  // extern "C"

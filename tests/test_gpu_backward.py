@@ -1,0 +1,104 @@
+"""GPU parity of moe_backward (through the C ABI) with the backward oracle.
+
+Each case runs the forward (moe_route from given logits, moe_schedule,
+moe_forward), prepares the backward weights (moe_backward_prepare) and runs
+moe_backward on a seeded bf16 output gradient.  Every gradient is compared
+with oracle.backward, which mirrors the bf16 storage of the intermediates:
+  - fp32 outputs (dx, dW_router): max|err| <= 1e-2 * RMS(ref);
+  - bf16 outputs (the expert weight gradients): RMS(err) <= 2e-3 RMS(ref),
+    at most 1e-5 of the elements beyond 1e-2 RMS(ref) plus one bf16 step of
+    their own value, and max|err| <= 1e-1 RMS(ref).
+The bf16 bound is statistical because the stored intermediates (a_g, a_u,
+g dout, da) are rounded on both sides from values that differ in their last
+fp32 bits: where one lands on the other side of a bf16 rounding boundary the
+two differ by a full bf16 step.  da = dh a_u SiLU'(a_g) is a product of three
+near-normal factors, so its largest entries sit tens of standard deviations
+out; one step on such an entry moves a whole row of dW by a few percent of
+RMS(dW).  Measured (mid: 256 rows an expert): RMS(err) <= 3e-4 RMS, at most
+2.4e-7 of the elements beyond, max 0.057 RMS.  A wrong row, tile or scale
+moves every element of an expert's gradient by ~1/sqrt(rows) RMS and fails
+both the RMS and the share bound by orders of magnitude.
+The device error word must stay clear, and a second run must give the same
+bits.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from mixture_experts_layer_counts_amd import MoEBackward, prepare_backward
+from oracle import backward as bwd
+from tests._gpu import host_weights, layer, need_gpu, rel_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+CASES = [
+    synth.workload("tiny", routing="gaussian"),
+    synth.Workload("ragged", T=300, D=256, I=192, E=16, k=4, I_shared=128, seed=7, routing="gaussian"),
+    synth.Workload("skewed", T=257, D=192, I=128, E=24, k=6, I_shared=320, seed=8, routing="zipf"),
+    synth.Workload("wideE", T=96, D=128, I=64, E=100, k=8, I_shared=64, seed=21, routing="gaussian"),
+    synth.workload("mid", routing="gaussian"),
+]
+
+
+def bf16_stats(got, want, tol):
+    """(RMS of the error / RMS(want), share of elements beyond tol * RMS(want)
+    plus one bf16 step, max|err| / RMS(want))."""
+    want = np.asarray(want, dtype=np.float64)
+    err = np.abs(np.asarray(got, dtype=np.float64) - want)
+    rms = np.sqrt(np.mean(want ** 2))
+    out = err > 2.0 ** -7 * np.abs(want) + tol * rms
+    return float(np.sqrt(np.mean(err ** 2)) / rms), float(np.mean(out)), float(err.max() / rms)
+
+
+def run_backward(w, inp_dev, dout):
+    m = layer(w, inp_dev["x"].device)
+    r = m(inp_dev["x"], inp_dev["w_router"], inp_dev, logits=inp_dev["logits"])
+    y = m.routed_rows()
+    bw = prepare_backward(m.shape, inp_dev, inp_dev["w_router"])
+    b = MoEBackward(m.shape, device=inp_dev["x"].device)
+    g = b(bw, inp_dev["x"], r["idx"], r["gate"], r, y, dout)
+    torch.cuda.synchronize()
+    assert m.device_error() == 0 and b.device_error() == 0
+    return {n: (v.float() if v.dtype == torch.bfloat16 else v).cpu().numpy() for n, v in g.items()}
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_backward_parity(w):
+    dev = need_gpu()
+    say("backward", w)
+    inp = synth.make_inputs(w)
+    dout = torch.randn((w.T, w.D), generator=torch.Generator().manual_seed(w.seed + 5)).to(torch.bfloat16)
+    inp_dev = to_dev(inp, dev)
+    got = run_backward(w, inp_dev, dout.to(dev))
+    host = host_weights(inp)
+    want = bwd.backward(host["x"], host, inp["logits"].numpy(), w.k, synth.bits(dout),
+                        w_router_bits=host["w_router"])
+    for gpu, ref in (("dx", "dx"), ("dw_router", "dW_router")):
+        err = rel_err(got[gpu], want[ref])
+        say("  ", gpu, "max|err|/RMS =", err)
+        assert err <= TOL, gpu
+    for gpu, ref in (("dw_gate", "dW_gate"), ("dw_up", "dW_up"), ("dw_down", "dW_down"), ("dws_gate", "dWs_gate"),
+                     ("dws_up", "dWs_up"), ("dws_down", "dWs_down")):
+        rms_err, share, mx = bf16_stats(got[gpu], want[ref], TOL)
+        say("  ", gpu, "RMS(err)/RMS =", rms_err, "share beyond =", share, "max|err|/RMS =", mx)
+        assert rms_err <= 2e-3 and share <= 1e-5 and mx <= 1e-1, gpu
+    again = run_backward(w, inp_dev, dout.to(dev))
+    for n in got:
+        assert np.array_equal(got[n].view(np.int32), again[n].view(np.int32)), n
+
+
+def test_backward_expert_without_rows_gets_zero_gradient():
+    # an expert no token routes to: its weight gradients are exactly zero
+    dev = need_gpu()
+    w = synth.Workload("idle", T=64, D=128, I=64, E=8, k=2, I_shared=64, seed=31, routing="gaussian")
+    inp = synth.make_inputs(w)
+    inp["logits"][:, 5] = -30.0  # expert 5 is never selected
+    dout = torch.randn((w.T, w.D), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    got = run_backward(w, to_dev(inp, dev), dout.to(dev))
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert np.all(got[n][5] == 0), n
+        assert np.any(got[n][4] != 0), n
