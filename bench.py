@@ -70,6 +70,8 @@ def parse():
                     help="fraction of the layer's expert work in the oracle's timed CPU sample (0: skip; default "
                          "the whole layer (or rank share), 1/4 in MXFP8)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time moe_backward on the step's routes and a seeded output gradient (bf16, R = 1)")
     ap.add_argument("--sweep", default="", metavar="B[:C[:M]],...",
                     help="after the main run, time the step at these minibatch sizes b (ring C, default b; with "
                          "--pipeline, M memory workgroups, default --mem-workgroups) and report them under "
@@ -431,6 +433,9 @@ def main():
         route_ms = sum(kernels[n]["ms_per_step"] for n in ("router_gemm", "topk") if n in kernels)
         result["ms_per_step_excl_route"] = round(ms - route_ms, 4)
 
+    if args.backward:
+        result["backward"] = backward_leg(job, args, torch, offsets)
+
     if getattr(job, "weight_quantize", None):
         result["weight_quantize"] = job.weight_quantize  # ahead of time, not part of the step
     if args.sweep:
@@ -452,6 +457,102 @@ def main():
         result["cpu_baseline"] = (cpu_baseline_ep(job, max(1, int(round(job.T * frac)))) if job.name == "ep64"
                                   else cpu_baseline(job, frac))
     print(json.dumps(result), flush=True)
+
+
+def backward_model(job, offsets):
+    """Algorithmic HBM bytes and FLOP of the backward's three timed groups:
+    every operand read once and every result written once.  The routed rows
+    replay up/gate (4 P D I), take dh = dY W_down and dx = da [W_gate; W_up]
+    (6 P D I) and the weight gradients dW = dY^T h, da^T x (6 P D I); the
+    transposed copies that feed the weight-gradient GEMMs are counted as one
+    read and one write of each operand."""
+    import numpy as np
+    w, P = job.w, job.P
+    D, I = w.D, w.I
+    touched = int(np.count_nonzero(np.diff(offsets)))
+    wexp = touched * I * D * 2  # one bf16 expert matrix of I x D, over the touched experts
+    return {
+        "bwd_replay": (P * D * 2 + 2 * wexp + P * 2 * I * 2, 4.0 * P * D * I),
+        # dh GEMM, SwiGLU backward, dx GEMM
+        "bwd_dgrad": ((P * D * 2 + wexp + P * I * 4) + (P * 2 * I * 2 + P * I * 4 + P * I * 2 + P * 2 * I * 2) +
+                      (P * 2 * I * 2 + 2 * wexp + P * D * 4), 6.0 * P * D * I),
+        # transposes of dY, h, da, x (read + write), then the three GEMMs
+        "bwd_wgrad": (2 * (P * D * 2 + P * I * 2 + P * 2 * I * 2 + P * D * 2) +
+                      (P * D * 2 + P * I * 2 + P * 2 * I * 2 + P * D * 2 + 3 * wexp), 6.0 * P * D * I),
+    }
+
+
+def backward_leg(job, args, torch, offsets):
+    """moe_backward after the forward: the routes, schedule and routed rows of
+    the step just timed, a seeded N(0,1) bf16 output gradient.  Timed like the
+    forward (warmup, then K calls between synchronisations, with a per-call
+    event median), then once more per group with the library's probes.
+    FLOP: executed 16 (P + T I_s / I) D I + 4 T E D (routed and shared:
+    replay 4, data gradients 6, weight gradients 6; router 2 + 2), of which
+    the replay's 4 is recomputation; the usual training count leaves it out."""
+    from mixture_experts_layer_counts_amd import MoEBackward, _lib, prepare_backward
+    if job.R != 1 or job.precision != "bf16" or getattr(job, "shared_precision", "bf16") != "bf16":
+        raise SystemExit("--backward is for the bf16 single-GPU workloads")
+    w, inp, layer = job.w, job.inp, job.layer
+    lib = _lib.load()
+    x, wr, logits_in = inp["x"], inp["w_router"], inp.get("logits")
+    if logits_in is not None:
+        _, idx, gate = layer.route(None, None, logits_in)
+    else:
+        _, idx, gate = layer.route(x, wr)
+    sched = layer.schedule(idx)
+    out = torch.empty((w.T, w.D), dtype=torch.bfloat16, device=x.device)
+    layer.forward(inp, x, x, gate, sched, out32=False, out=out)
+    y = layer.routed_rows()
+    t0 = time.perf_counter()
+    bw = prepare_backward(layer.shape, inp, wr)
+    torch.cuda.synchronize()
+    prep_ms = (time.perf_counter() - t0) * 1e3
+    b = MoEBackward(layer.shape, device=x.device)
+    dout = torch.randn((w.T, w.D), generator=torch.Generator(device=x.device).manual_seed(w.seed + 5),
+                       device=x.device).to(torch.bfloat16)
+    grads = None
+    for _ in range(max(1, args.warmup)):
+        grads = b(bw, x, idx, gate, sched, y, dout, grads)
+    torch.cuda.synchronize()
+    if b.device_error():
+        raise RuntimeError(f"backward device error word {b.device_error():#x}")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        b(bw, x, idx, gate, sched, y, dout, grads)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    med = statistics.median(a.elapsed_time(c) for a, c in evs)
+    model = backward_model(job, offsets)
+    groups = {}
+    tot, n = ctypes.c_double(), ctypes.c_int32()
+    reps = max(3, min(args.steps, 10))
+    for name, (nbytes, flops) in model.items():
+        _lib.check("moe_probe_begin", lib.moe_probe_begin(_lib.KERNELS[name], reps + 2))
+        for _ in range(reps):
+            b(bw, x, idx, gate, sched, y, dout, grads)
+        _lib.check("moe_probe_end", lib.moe_probe_end(ctypes.byref(tot), ctypes.byref(n)))
+        t = tot.value / max(n.value, 1) * 1e-3
+        groups[name] = {"ms": round(t * 1e3, 4), "alg_bytes": int(nbytes), "GB_per_s": round(nbytes / t / 1e9, 1),
+                        "hbm_frac": round(nbytes / t / PEAK_HBM, 4), "alg_flop": flops,
+                        "TFLOP_per_s": round(flops / t / 1e12, 1), "mfma_frac": round(flops / t / PEAK_BF16, 4)}
+    D, I, Is, T, P, E = w.D, w.I, w.I_shared, w.T, job.P, w.E
+    executed = 16.0 * (P * I + T * Is) * D + 4.0 * T * E * D
+    useful = 12.0 * (P * I + T * Is) * D + 4.0 * T * E * D
+    r = {"ms_per_call": round(ms, 4), "ms_per_call_median": round(med, 4), "calls": args.steps,
+         "tokens_per_s": round(T / (ms * 1e-3), 1),
+         "flop_executed": executed, "flop_without_replay": useful,
+         "tflops_executed": round(executed / (ms * 1e-3) / 1e12, 2),
+         "mfma_peak_frac_executed": round(executed / (ms * 1e-3) / PEAK_BF16, 4),
+         "prepare_ms": round(prep_ms, 2), "workspace_bytes": b.ws_bytes, "groups": groups}
+    log("backward:", json.dumps(r))
+    del b, bw, grads
+    torch.cuda.empty_cache()
+    return r
 
 
 def sweep(job, args, torch):

@@ -303,6 +303,7 @@ moe_status moe_backward_workspace_bytes(const moe_shape* shape, size_t* bytes);
  *   dev_error  device int32, caller-owned: MOE_DEVERR_* bits are OR-ed in
  * Shapes are validated before any launch, as for the forward; every GEMM
  * operand of the backward must stay below 2^31 bytes (MOE_ERR_UNSUPPORTED).
+ * x, y_routes and dout must be 16-byte aligned (MOE_ERR_INVALID_ARG).
  */
 moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const void* x, const int32_t* topk_idx,
                         const float* topk_gate, const int32_t* expert_offsets, const int32_t* sched_src,

@@ -35,8 +35,7 @@ __global__ __launch_bounds__(256) void dy_gather_kernel(const uint16_t* __restri
   const float g = gate[j];
   const uint16_t* __restrict__ src = dout + static_cast<int64_t>(j / k) * D;
   uint16_t* __restrict__ dst = dy + p * D;
-  for (int c = lane_id() * 8; c < D; c += kWave * 8) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + c);
+  auto scale = [g](const u32x4_t& v) {
     u32x4_t o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -44,8 +43,23 @@ __global__ __launch_bounds__(256) void dy_gather_kernel(const uint16_t* __restri
       const float hi = g * bf16_to_f32(static_cast<uint16_t>(v[q] >> 16));
       o[q] = pack_bf16x2(lo, hi);
     }
-    *reinterpret_cast<u32x4_t*>(dst + c) = o;
+    return o;
+  };
+  constexpr int kStep = kWave * 8;  // elements one pass of the wave covers
+  int c = lane_id() * 8;
+  // four 16-byte loads in flight per lane, then their stores; the row's last
+  // chunks one at a time
+  for (; c + 3 * kStep < D; c += 4 * kStep) {
+    const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(src + c);
+    const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(src + c + kStep);
+    const u32x4_t v2 = *reinterpret_cast<const u32x4_t*>(src + c + 2 * kStep);
+    const u32x4_t v3 = *reinterpret_cast<const u32x4_t*>(src + c + 3 * kStep);
+    *reinterpret_cast<u32x4_t*>(dst + c) = scale(v0);
+    *reinterpret_cast<u32x4_t*>(dst + c + kStep) = scale(v1);
+    *reinterpret_cast<u32x4_t*>(dst + c + 2 * kStep) = scale(v2);
+    *reinterpret_cast<u32x4_t*>(dst + c + 3 * kStep) = scale(v3);
   }
+  for (; c < D; c += kStep) *reinterpret_cast<u32x4_t*>(dst + c) = scale(*reinterpret_cast<const u32x4_t*>(src + c));
 }
 
 // One wave per route j: dg[j] = <dout[j / k], y[j]>, each lane summing its
@@ -157,14 +171,17 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __rest
 
 // Transpose of row segments into padded columns: out [W][ld_out], column
 // padded[e] + i holds row offsets[e] + i of src [rows][lda] (bf16), zero past
-// the segment's rows.  A block moves a 64 x 64 tile through LDS; a 64-column
-// chunk of the output lies in one segment, since padded starts are multiples
-// of 64.
+// the segment's rows.  A block moves a 64 x 64 tile through LDS with 16-byte
+// global loads (8 columns of one source row) and 16-byte global stores (8
+// rows of one source column); a 64-column chunk of the output lies in one
+// segment, since padded starts are multiples of 64.  W, lda and ld_out are
+// multiples of 8 and the bases 16-byte aligned (checked by the launcher).
 __global__ __launch_bounds__(256) void seg_transpose_kernel(const uint16_t* __restrict__ src, int64_t lda, int W,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ padded, int L,
                                                             uint16_t* __restrict__ out, int64_t ld_out) {
-  __shared__ uint16_t tile[64][66];
+  constexpr int kStride = 72;  // LDS row stride in elements (144 bytes: 16-byte aligned rows, spread banks)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kStride];
   const int64_t q0 = static_cast<int64_t>(blockIdx.x) * 64;  // output column chunk
   const int w0 = blockIdx.y * 64;                            // output row chunk (source column)
   if (q0 >= padded[L]) return;
@@ -177,17 +194,27 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(const uint16_t* __re
   const int e = lo;
   const int64_t i0 = q0 - padded[e];
   const int64_t n_e = offsets[e + 1] - offsets[e];
-  for (int v = threadIdx.x; v < 64 * 64; v += 256) {
-    const int r = v / 64, c = v % 64;  // r: row within the chunk, c: source column
-    const int64_t i = i0 + r;
-    uint16_t val = 0;
-    if (i < n_e && w0 + c < W) val = src[(offsets[e] + i) * lda + w0 + c];
-    tile[c][r] = val;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int v = threadIdx.x + 256 * j;
+    const int r = v >> 3, c = (v & 7) * 8;  // source row within the chunk, first of 8 source columns
+    u32x4_t val = {0u, 0u, 0u, 0u};
+    if (i0 + r < n_e && w0 + c < W)
+      val = *reinterpret_cast<const u32x4_t*>(src + (offsets[e] + i0 + r) * lda + w0 + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[(c + 2 * q) * kStride + r] = static_cast<uint16_t>(val[q] & 0xffffu);
+      tile[(c + 2 * q + 1) * kStride + r] = static_cast<uint16_t>(val[q] >> 16);
+    }
   }
   __syncthreads();
-  for (int v = threadIdx.x; v < 64 * 64; v += 256) {
-    const int c = v / 64, r = v % 64;
-    if (w0 + c < W) out[static_cast<int64_t>(w0 + c) * ld_out + q0 + r] = tile[c][r];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int v = threadIdx.x + 256 * j;
+    const int c = v >> 3, r = (v & 7) * 8;  // output row (source column), first of 8 output columns
+    if (w0 + c < W)
+      *reinterpret_cast<u32x4_t*>(out + static_cast<int64_t>(w0 + c) * ld_out + q0 + r) =
+          *reinterpret_cast<const u32x4_t*>(tile + c * kStride + r);
   }
 }
 
@@ -300,6 +327,9 @@ hipError_t launch_seg_transpose(const uint16_t* src, int64_t lda, int W, const i
                                 const int32_t* padded, int L, int64_t max_cols, uint16_t* out, int64_t ld_out,
                                 hipStream_t s) {
   if (max_cols <= 0 || W <= 0) return hipSuccess;
+  if (W % 8 || lda % 8 || ld_out % 64 || reinterpret_cast<uintptr_t>(src) % 16 ||
+      reinterpret_cast<uintptr_t>(out) % 16)
+    return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>((max_cols + 63) / 64), static_cast<unsigned>((W + 63) / 64));
   seg_transpose_kernel<<<grid, 256, 0, s>>>(src, lda, W, offsets, padded, L, out, ld_out);
   return hipGetLastError();

@@ -965,6 +965,9 @@ moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const
   if (!bw || !g || !dev_error || !x || !topk_idx || !topk_gate || !expert_offsets || !sched_src || !route_dst ||
       !y_routes || !dout)
     return MOE_ERR_INVALID_ARG;
+  // rows are read in 16-byte pieces
+  for (const void* p : {x, y_routes, dout})
+    if (reinterpret_cast<uintptr_t>(p) % 16) return MOE_ERR_INVALID_ARG;
   if (!bw->w_gu || !bw->w_gu_t || !bw->w_down_t || !bw->ws_gu || !bw->ws_gu_t || !bw->ws_down_t || !bw->w_router_t)
     return MOE_ERR_INVALID_ARG;
   if (!g->dx || !g->dw_gate || !g->dw_up || !g->dw_down || !g->dws_gate || !g->dws_up || !g->dws_down ||

@@ -118,10 +118,7 @@ def backward(x_bits: np.ndarray, weights: Dict[str, np.ndarray], logits: np.ndar
     dW = {n: np.zeros(weights[w].shape, dtype=np.float64)
           for n, w in (("dW_gate", "w_gate"), ("dW_up", "w_up"), ("dW_down", "w_down"))}
     for e in np.unique(idx):
-        ti, si = np.nonzero(idx == e)
-        dy = r(g[ti, si][:, None] * dout[ti])
-        b = ffn_backward(x[ti], dy, _bf16.to_f64(weights["w_gate"][e]), _bf16.to_f64(weights["w_up"][e]),
-                         _bf16.to_f64(weights["w_down"][e]), exact)
+        ti, b = expert_backward(x_bits, weights, idx, g, dout_bits, int(e), exact=exact)
         np.add.at(dx, ti, b["dx"])
         for n in dW:
             dW[n][e] = b[n]
@@ -137,3 +134,87 @@ def backward(x_bits: np.ndarray, weights: Dict[str, np.ndarray], logits: np.ndar
         out["dx"] = dx + dlb @ _bf16.to_f64(w_router_bits)
         out["dW_router"] = dlb.T @ x
     return out
+
+
+# ---- pieces of the same computation, for samples of a large layer ----
+# Every token's dx depends on that token alone, every expert's weight gradient
+# on the routes to that expert alone, and every intermediate column i of the
+# shared expert on column i alone (SwiGLU is elementwise in i), so these give
+# the rows of backward()'s results without evaluating the whole layer.
+
+def expert_backward(x_bits: np.ndarray, weights: Dict[str, np.ndarray], idx: np.ndarray, g: np.ndarray,
+                    dout_bits: np.ndarray, e: int, tokens: Optional[np.ndarray] = None, exact: bool = False):
+    """The routes to expert e (of the given tokens, else of all): returns the
+    token id of each route and ffn_backward of those rows, i.e. each route's
+    dx contribution [n, D] and the weight gradients of e summed over exactly
+    those routes.  idx [T, k] the selection, g [T, k] the gates."""
+    r = _round(exact)
+    idx = np.asarray(idx)
+    pool = np.arange(idx.shape[0]) if tokens is None else np.asarray(tokens)
+    ti, si = np.nonzero(idx[pool] == e)
+    ti = pool[ti]
+    dy = r(np.asarray(g)[ti, si][:, None] * _bf16.to_f64(dout_bits[ti]))
+    b = ffn_backward(_bf16.to_f64(x_bits[ti]), dy, _bf16.to_f64(weights["w_gate"][e]),
+                     _bf16.to_f64(weights["w_up"][e]), _bf16.to_f64(weights["w_down"][e]), exact)
+    return ti, b
+
+
+def logit_grad_rows(logits: np.ndarray, k: int, dout_bits: np.ndarray, Y: np.ndarray,
+                    tokens: np.ndarray) -> np.ndarray:
+    """dlogits rows [n, E] of the given tokens, from their stored routed rows
+    Y [n, k, D] (the forward's rows, as moe.routed_outputs gives them)."""
+    lg = np.asarray(logits)[tokens]
+    sel = _moe.topk(lg, k)
+    g = _moe.gates(lg, sel)
+    dg = np.einsum("td,tkd->tk", _bf16.to_f64(dout_bits[tokens]), Y)
+    out = np.zeros(lg.shape, dtype=np.float64)
+    np.put_along_axis(out, sel.astype(np.int64), gate_logit_grad(g, dg), axis=1)
+    return out
+
+
+def token_dx(x_bits: np.ndarray, weights: Dict[str, np.ndarray], logits: np.ndarray, k: int,
+             dout_bits: np.ndarray, tokens: np.ndarray, Y: np.ndarray, w_router_bits: np.ndarray,
+             exact: bool = False, map_fn=map) -> np.ndarray:
+    """Rows ``tokens`` of backward()'s dx [n, D]: the shared expert's share,
+    every route's share, and the router's share r(dlogits) W_r.  Y [n, k, D]
+    the tokens' stored routed rows; map_fn maps the per-expert evaluations
+    (the builtin map, or a thread pool's)."""
+    r = _round(exact)
+    tokens = np.asarray(tokens)
+    idx = _moe.topk(logits, k)
+    g = _moe.gates(logits, idx)
+    sh = ffn_backward(_bf16.to_f64(x_bits[tokens]), _bf16.to_f64(dout_bits[tokens]),
+                      _bf16.to_f64(weights["ws_gate"]), _bf16.to_f64(weights["ws_up"]),
+                      _bf16.to_f64(weights["ws_down"]), exact)
+    dx = sh["dx"].copy()
+    where = {int(t): n for n, t in enumerate(tokens)}
+    experts = [int(e) for e in np.unique(idx[tokens])]
+    for ti, b in map_fn(lambda e: expert_backward(x_bits, weights, idx, g, dout_bits, e, tokens, exact), experts):
+        np.add.at(dx, [where[int(t)] for t in ti], b["dx"])
+    dl = logit_grad_rows(logits, k, dout_bits, Y, tokens)
+    return dx + r(dl) @ _bf16.to_f64(w_router_bits)
+
+
+def shared_columns_backward(x_bits: np.ndarray, weights: Dict[str, np.ndarray], dout_bits: np.ndarray,
+                            cols: np.ndarray, exact: bool = False) -> Dict[str, np.ndarray]:
+    """Rows ``cols`` of dWs_gate and dWs_up and columns ``cols`` of dWs_down,
+    over all tokens: the shared expert restricted to those intermediate
+    columns."""
+    cols = np.asarray(cols)
+    b = ffn_backward(_bf16.to_f64(x_bits), _bf16.to_f64(dout_bits), _bf16.to_f64(weights["ws_gate"][cols]),
+                     _bf16.to_f64(weights["ws_up"][cols]), _bf16.to_f64(weights["ws_down"][:, cols]), exact)
+    return {"dWs_gate": b["dW_gate"], "dWs_up": b["dW_up"], "dWs_down": b["dW_down"]}
+
+
+def router_weight_rows(x_bits: np.ndarray, logits: np.ndarray, k: int, dout_bits: np.ndarray, Y: np.ndarray,
+                       tokens: np.ndarray, experts: np.ndarray, exact: bool = False) -> np.ndarray:
+    """Rows ``experts`` of backward()'s dW_router [len(experts), D]; ``tokens``
+    must hold every token that selects one of them (the other tokens' logit
+    gradients are zero in those columns), Y [n, k, D] their routed rows."""
+    r = _round(exact)
+    tokens, experts = np.asarray(tokens), np.asarray(experts)
+    every = np.nonzero(np.isin(_moe.topk(logits, k), experts).any(axis=1))[0]
+    if not np.all(np.isin(every, tokens)):
+        raise ValueError("tokens must include every token that selects the given experts")
+    dl = r(logit_grad_rows(logits, k, dout_bits, Y, tokens))
+    return dl[:, experts].T @ _bf16.to_f64(x_bits[tokens])

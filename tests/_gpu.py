@@ -92,6 +92,37 @@ def rel_err(got, want):
     return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - want)) / np.sqrt(np.mean(want ** 2)))
 
 
+def bf16_stats(got, want, tol):
+    """For a gradient stored in bf16: (RMS of the error / RMS(want), share of
+    the elements beyond tol * RMS(want) plus one bf16 step of their own value,
+    max|err| / RMS(want))."""
+    want = np.asarray(want, dtype=np.float64)
+    err = np.abs(np.asarray(got, dtype=np.float64) - want)
+    rms = np.sqrt(np.mean(want ** 2))
+    out = err > 2.0 ** -7 * np.abs(want) + tol * rms
+    return float(np.sqrt(np.mean(err ** 2)) / rms), float(np.mean(out)), float(err.max() / rms)
+
+
+def bf16_grad_ok(got, want, name=""):
+    """The bound for bf16-stored gradients (see test_gpu_backward): RMS(err)
+    <= 2e-3 RMS, at most 1e-5 of the elements beyond 1e-2 RMS plus one bf16
+    step, max|err| <= 1e-1 RMS."""
+    rms_err, share, mx = bf16_stats(got, want, 1e-2)
+    say("  ", name, "RMS(err)/RMS =", rms_err, "share beyond =", share, "max|err|/RMS =", mx)
+    return rms_err <= 2e-3 and share <= 1e-5 and mx <= 1e-1
+
+
+class DeviceExperts:
+    """expert id -> the bf16 bits of that expert's matrix of a device weight
+    tensor [E, ...], copied to the host when asked for."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, e):
+        return synth.bits(self.t[int(e)])
+
+
 def gate_tolerance(logits_sel: np.ndarray, k: int) -> np.ndarray:
     """Relative bound on a gate computed in fp32 from fp32 logits:
     u * (2 * max_s |l_s - l_0| + k + 8), u = 2^-24 (the subtraction, the

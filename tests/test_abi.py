@@ -217,3 +217,36 @@ def test_pipeline_shape_fields(lib):
     # it keeps two h buffers and per-minibatch counters in the workspace
     plain = shape_for(T=64, D=128, I=64, E=8, k=2, minibatch_rows=32, ring_rows=64)
     assert ws_bytes(lib, ok)[1] >= ws_bytes(lib, plain)[1] + 32 * 64 * 2 + 3 * 4 * 4
+
+
+def test_backward_validates_before_any_launch(lib):
+    s = shape_for(T=64, D=128, I=64, E=8, k=2)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == 0 and n.value > 0
+    # the backward is for one GPU's bf16 layer: R > 1 and MXFP8 are refused
+    ep = shape_for(T=64, D=128, I=64, E=16, k=2, R=2, rank=0, max_rows=256)
+    mx = shape_for(T=64, D=128, I=128, E=8, k=2, I_shared=128, precision="mxfp8")
+    for bad in (ep, mx):
+        assert lib.moe_backward_workspace_bytes(ctypes.byref(bad), ctypes.byref(ctypes.c_size_t())) == -2
+    # the transposed routed rows, D x (T k + 64 E) bf16, past 2^31 bytes at a
+    # shape whose forward operands all fit (the ring: 2,146,959,360 bytes)
+    big = shape_for(T=18720, D=7168, I=2048, E=256, k=8)
+    assert ws_bytes(lib, big)[0] == 0
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(big), ctypes.byref(ctypes.c_size_t())) == -2
+    fake = ctypes.c_void_p(4096)  # never dereferenced: every call below returns first
+    bw = _lib.MoeBwdWeights(*([fake.value] * len(_lib.MoeBwdWeights._fields_)))
+    g = _lib.MoeGrads(*([fake.value] * len(_lib.MoeGrads._fields_)))
+
+    def call(x=fake, y=fake, dout=fake, ws=fake, nbytes=n.value, grads=g, weights=bw):
+        return lib.moe_backward(ctypes.byref(s), ctypes.byref(weights), x, fake, fake, fake, fake, fake, y, dout,
+                                ctypes.byref(grads), fake, ws, nbytes, None)
+
+    assert call(nbytes=n.value - 1) == -3                        # workspace too small
+    assert call(ws=ctypes.c_void_p(4096 + 64)) == -1              # workspace not 256-byte aligned
+    for kw in ("x", "y", "dout"):                                 # rows read in 16-byte pieces
+        assert call(**{kw: ctypes.c_void_p(4096 + 8)}) == -1, kw
+        assert call(**{kw: None}) == -1, kw
+    assert call(grads=_lib.MoeGrads()) == -1                      # null gradient outputs
+    assert call(weights=_lib.MoeBwdWeights()) == -1               # weights not prepared
+    w = _lib.MoeWeights()
+    assert lib.moe_backward_prepare(ctypes.byref(s), ctypes.byref(w), fake, ctypes.byref(bw), None) == -1

@@ -14,7 +14,14 @@ mode (minibatches of 2,048 rows cycling a 4,096-row ring).
 * the layer output against the oracle, fed the same fp32 logits, on a sample
   of over 512 tokens that together route to every one of the 256 experts and
   include the first and last row of every expert's region;
-* ring mode: bitwise equal to the single-minibatch run.
+* ring mode: bitwise equal to the single-minibatch run;
+* the backward (moe_backward after the forward from x, seeded N(0,1) bf16
+  output gradient) against the backward oracle's sampled pieces: dx of 16
+  seeded tokens, every weight gradient of four experts (the first, the last,
+  the most and the least loaded), eight intermediate columns of the shared
+  expert's weight gradients over all tokens, and the router-weight gradient
+  row of the least loaded expert (all tokens that select it), under the
+  bounds of the smaller backward cases.
 """
 
 import numpy as np
@@ -23,8 +30,8 @@ import torch
 
 import synth
 from oracle import moe as ref
-from tests._gpu import (cover_tokens, fetch_bf16, gate_tolerance, layer, need_gpu, oracle_routed_pooled, rel_err,
-                        say)
+from tests._gpu import (DeviceExperts, bf16_grad_ok, cover_tokens, fetch_bf16, gate_tolerance, layer, need_gpu,
+                        oracle_routed_pooled, rel_err, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -149,3 +156,68 @@ def test_dsv3_ring_mode_bitwise_equal(dsv3, dsv3_run, b, C):
     assert np.array_equal(r["out"].cpu().view(torch.int16).numpy(), dsv3_run["out"])
     del m, r
     torch.cuda.empty_cache()
+
+
+def test_dsv3_backward_sampled(dsv3):
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from mixture_experts_layer_counts_amd import MoEBackward, prepare_backward
+    from oracle import backward as bwd
+    w, inp, dev = dsv3
+    P = w.T * w.k
+    m = layer(w, dev, P, P)
+    say("dsv3 backward: forward from x at b = C = P, then moe_backward")
+    r = m(inp["x"], inp["w_router"], inp)
+    bw = prepare_backward(m.shape, inp, inp["w_router"])
+    b = MoEBackward(m.shape, device=dev)
+    dout = torch.randn((w.T, w.D), generator=torch.Generator().manual_seed(w.seed + 5)).to(torch.bfloat16)
+    g = b(bw, inp["x"], r["idx"], r["gate"], r, m.routed_rows(), dout.to(dev))
+    torch.cuda.synchronize()
+    assert m.device_error() == 0 and b.device_error() == 0
+    lg, gi = r["logits"].cpu().numpy(), r["idx"].cpu().numpy()
+    counts = np.bincount(gi.ravel(), minlength=w.E)
+    live = np.nonzero(counts)[0]
+    rare = int(live[np.argmin(counts[live])])
+    experts = sorted({0, w.E - 1, int(np.argmax(counts)), rare})
+    tok_dx = np.sort(np.random.default_rng(5).choice(w.T, size=16, replace=False))
+    tok_r = np.nonzero((gi == rare).any(axis=1))[0]
+    rng = np.random.default_rng(6)
+    cols = np.unique(np.concatenate([[0, 1, w.I_shared // 2, w.I_shared - 1], rng.choice(w.I_shared, 4)]))
+    got = {"dx": g["dx"][torch.from_numpy(tok_dx).to(dev)].cpu().numpy(),
+           "dw_router": g["dw_router"][rare].cpu().numpy()}
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        got[n] = {e: g[n][e].float().cpu().numpy() for e in experts}
+    c_dev = torch.from_numpy(cols).to(dev)
+    got["dws_gate"] = g["dws_gate"][c_dev].float().cpu().numpy()
+    got["dws_up"] = g["dws_up"][c_dev].float().cpu().numpy()
+    got["dws_down"] = g["dws_down"][:, c_dev].float().cpu().numpy()
+    del g, b, bw, m, r
+    torch.cuda.empty_cache()
+
+    xb, db, wrb = synth.bits(inp["x"]), synth.bits(dout), synth.bits(inp["w_router"])
+    wts = {n: DeviceExperts(inp[n]) for n in ("w_gate", "w_up", "w_down")}
+    wts.update({n: synth.bits(inp[n]) for n in ("ws_gate", "ws_up", "ws_down")})
+    gates = ref.gates(lg, gi)
+    for e in experts:
+        say("dsv3 backward: expert", e, "with", int(counts[e]), "routes")
+        _, want = bwd.expert_backward(xb, wts, gi, gates, db, e)
+        for gpu, n in (("dw_gate", "dW_gate"), ("dw_up", "dW_up"), ("dw_down", "dW_down")):
+            assert bf16_grad_ok(got[gpu][e], want[n], f"{gpu}[{e}]"), (gpu, e)
+    say("dsv3 backward: shared columns", cols.tolist(), "over all tokens")
+    want = bwd.shared_columns_backward(xb, wts, db, cols)
+    for gpu, n in (("dws_gate", "dWs_gate"), ("dws_up", "dWs_up"), ("dws_down", "dWs_down")):
+        assert bf16_grad_ok(got[gpu], want[n], gpu), gpu
+    tok = np.union1d(tok_dx, tok_r)
+    say("dsv3 backward: routed rows of", len(tok), "tokens (thread pool)")
+    Y = oracle_routed_pooled(xb, fetch_bf16(inp), [(gi, tok)])[0]
+    say("dsv3 backward: dx of", len(tok_dx), "tokens")
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        want_dx = bwd.token_dx(xb, wts, lg, w.k, db, tok_dx, Y[np.searchsorted(tok, tok_dx)], wrb, map_fn=ex.map)
+    err = rel_err(got["dx"], want_dx)
+    say("   dx max|err|/RMS =", err)
+    assert err <= 1e-2
+    want_r = bwd.router_weight_rows(xb, lg, w.k, db, Y[np.searchsorted(tok, tok_r)], tok_r, [rare])[0]
+    err = rel_err(got["dw_router"], want_r)
+    say("   dw_router[%d] (%d tokens) max|err|/RMS =" % (rare, len(tok_r)), err)
+    assert err <= 1e-2

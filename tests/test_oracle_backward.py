@@ -137,3 +137,36 @@ def test_storage_rounding_is_present_and_bounded():
     for n in ("dx", "dW_gate", "dW_up", "dW_down", "dWs_gate", "dWs_down", "dW_router"):
         rel = np.max(np.abs(a[n] - b[n])) / np.sqrt(np.mean(b[n] ** 2))
         assert 0 < rel < 1e-1, (n, rel)
+
+
+def test_sampled_pieces_equal_the_whole_layer():
+    # the per-token, per-expert and per-column pieces used on samples of a
+    # large layer give the rows of the whole-layer result (bf16 storage mode)
+    w, inp, host, dout, L64 = case(T=48, D=64, I=32, E=7, k=3, Is=40, seed=11)
+    lg = L64.astype(np.float32)
+    full = bwd.backward(host["x"], host, lg, w.k, dout, w_router_bits=host["w_router"])
+    idx, g = full["idx"], full["gates"]
+
+    def close(a, b):
+        return np.allclose(a, b, rtol=1e-12, atol=1e-12 * np.abs(b).max())
+
+    for e in (0, 3, 6):
+        ti, b = bwd.expert_backward(host["x"], host, idx, g, dout, e)
+        assert np.array_equal(np.sort(np.unique(ti)), np.nonzero((idx == e).any(axis=1))[0])
+        for n in ("dW_gate", "dW_up", "dW_down"):
+            assert close(b[n], full[n][e]), (e, n)
+    tok = np.array([0, 5, 17, 47])
+    Y = moe.routed_outputs(host["x"], host, idx, tokens=tok)
+    dx = bwd.token_dx(host["x"], host, lg, w.k, dout, tok, Y, host["w_router"])
+    assert close(dx, full["dx"][tok])
+    assert close(bwd.logit_grad_rows(lg, w.k, dout, Y, tok), full["dlogits"][tok])
+    cols = np.array([1, 8, 39])
+    sh = bwd.shared_columns_backward(host["x"], host, dout, cols)
+    assert close(sh["dWs_gate"], full["dWs_gate"][cols]) and close(sh["dWs_up"], full["dWs_up"][cols])
+    assert close(sh["dWs_down"], full["dWs_down"][:, cols])
+    ex = np.array([2, 4])
+    every = np.nonzero(np.isin(idx, ex).any(axis=1))[0]
+    Ye = moe.routed_outputs(host["x"], host, idx, tokens=every)
+    assert close(bwd.router_weight_rows(host["x"], lg, w.k, dout, Ye, every, ex), full["dW_router"][ex])
+    with pytest.raises(ValueError):
+        bwd.router_weight_rows(host["x"], lg, w.k, dout, Ye[:-1], every[:-1], ex)
