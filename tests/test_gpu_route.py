@@ -11,14 +11,20 @@ from tests._gpu import gate_tolerance, layer, need_gpu, say
 pytestmark = pytest.mark.gpu
 
 ROUTE_CASES = [
+    # the router GEMM's K ranges (planes the top-k adds in order): 4 for up to
+    # 128 output tiles of 128 x 128, 2 for up to 256, 1 beyond; logits per
+    # lane of the top-k from 1 (E <= 64) to 16 (E = 1000)
     synth.workload("tiny"),
     synth.Workload("ragged", T=333, D=320, I=64, E=24, k=5, I_shared=64, seed=11),
     synth.Workload("wide", T=130, D=256, I=64, E=384, k=8, I_shared=64, seed=12),
     synth.Workload("e1k", T=70, D=128, I=64, E=1000, k=16, I_shared=64, seed=13),
-    # the router GEMM's K ranges: 132 output tiles take 2 ranges, 258 take one
-    # (the small cases above take 4); the top-k adds the planes in order
+    synth.Workload("e100", T=1000, D=512, I=64, E=100, k=6, I_shared=64, seed=23),
+    synth.Workload("e512", T=700, D=256, I=64, E=512, k=16, I_shared=64, seed=24),
+    synth.Workload("d7168", T=2000, D=7168, I=64, E=256, k=8, I_shared=64, seed=25),
     synth.Workload("k2ranges", T=5632, D=128, I=64, E=384, k=8, I_shared=64, seed=17),
+    synth.Workload("k2ranges-e64", T=16512, D=128, I=64, E=64, k=6, I_shared=64, seed=19),
     synth.Workload("k1range", T=11008, D=128, I=64, E=384, k=8, I_shared=64, seed=18),
+    synth.Workload("k1range-e64", T=33024, D=128, I=64, E=64, k=6, I_shared=64, seed=20),
 ]
 
 
@@ -130,3 +136,24 @@ def test_route_nonfinite_sets_error_bit():
     rows = [t for t in range(w.T) if t != 3]
     assert np.array_equal(idx.cpu().numpy()[rows], ref.topk(l.numpy()[rows], w.k))
     assert 5 not in idx.cpu().numpy()[3]
+
+
+def test_route_from_x_nonfinite_sets_error_bit():
+    # an infinite entry of x makes its token's logits non-finite (the router
+    # GEMM's 4 K-range planes, summed by the top-k); the error bit is set and
+    # the other tokens' selections are the oracle's top-k of the GPU's logits
+    dev = need_gpu()
+    w = synth.Workload("inf-x", T=600, D=256, I=64, E=128, k=4, I_shared=64, seed=26)
+    inp = synth.make_inputs(w, with_weights=False)
+    x = inp["x"].clone()
+    x[257, 3] = float("inf")
+    say("route_from_x nonfinite", w)
+    m = layer(w, dev)
+    logits, idx, _ = m.route(x.to(dev), inp["w_router"].to(dev))
+    from mixture_experts_layer_counts_amd import _lib
+    assert m.device_error() & _lib.DEVERR_NONFINITE
+    lg = logits.cpu().numpy()
+    assert not np.all(np.isfinite(lg[257]))
+    rows = [t for t in range(w.T) if t != 257]
+    assert np.all(np.isfinite(lg[rows]))
+    assert np.array_equal(idx.cpu().numpy()[rows], ref.topk(lg[rows], w.k))
