@@ -1,5 +1,5 @@
-"""The whole layer (moe_route from x + moe_schedule + moe_forward) captured in
-a HIP graph and replayed.
+"""The whole layer (moe_route from x + moe_schedule + moe_forward), and the
+backward (moe_backward), each captured in a HIP graph and replayed.
 
 The library allocates nothing, reads no device data on the host and clears
 its scratch words with kernels, so a caller may capture a step and replay it.
@@ -61,3 +61,45 @@ def test_layer_graph_replay_bitwise(name, w, b, C):
         other(noise, inp_dev["w_router"], inp_dev)
         torch.cuda.synchronize()
     assert m.device_error() == 0
+
+
+def test_backward_graph_replay_bitwise():
+    # moe_backward is launches only (no allocation, no host read, no memset),
+    # so a caller may capture it too; each replay gives the eager gradients bit
+    # for bit, with other eager backward work between the replays
+    from mixture_experts_layer_counts_amd import MoEBackward, prepare_backward
+    dev = need_gpu()
+    w = synth.Workload("ragged", T=300, D=256, I=192, E=16, k=4, I_shared=128, seed=7, routing="gaussian")
+    say("graph_replay backward", w)
+    inp_dev = to_dev(synth.make_inputs(w), dev)
+    m = layer(w, dev)
+    r = m(inp_dev["x"], inp_dev["w_router"], inp_dev, logits=inp_dev["logits"])
+    y = m.routed_rows()
+    bw = prepare_backward(m.shape, inp_dev, inp_dev["w_router"])
+    b = MoEBackward(m.shape, device=dev)
+    dout = torch.randn((w.T, w.D), generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).to(dev)
+    grads = b(bw, inp_dev["x"], r["idx"], r["gate"], r, y, dout)
+    torch.cuda.synchronize()
+    want = {n: v.clone() for n, v in grads.items()}
+
+    other = MoEBackward(m.shape, device=dev)
+    noise = torch.randn_like(dout, dtype=torch.float32).to(torch.bfloat16)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        b(bw, inp_dev["x"], r["idx"], r["gate"], r, y, dout, grads)  # warm-up on the capturing stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b(bw, inp_dev["x"], r["idx"], r["gate"], r, y, dout, grads)
+    for rep in range(3):
+        for v in grads.values():
+            v.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in want:
+            assert torch.equal(grads[n], want[n]), f"replay {rep}: {n} differs from the eager backward"
+        other(bw, inp_dev["x"], r["idx"], r["gate"], r, y, noise)
+        torch.cuda.synchronize()
+    assert b.device_error() == 0 and other.device_error() == 0
