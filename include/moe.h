@@ -105,7 +105,10 @@ typedef struct {
                                   1: as one persistent kernel whose workgroups
                                   wait on device-side counters (MoK paper §3.2,
                                   "Maximally Deferred Synchronization", "Kernel
-                                  Fusion"); routed precision MOE_BF16 only */
+                                  Fusion"); up/gate runs up to H - 1 minibatches
+                                  ahead of down, H = C/b clamped to 2 .. 4 (H h
+                                  buffers of [b, I] in the workspace); routed
+                                  precision MOE_BF16 only */
   int32_t mem_workgroups;      /* pipeline == 1: workgroups of the persistent
                                   kernel that gather minibatches C/b and later
                                   (MoK paper §3.4, "Computation-Communication SM

@@ -535,16 +535,21 @@ hipError_t run(const GemmArgs& a, hipStream_t stream) {
 //         workgroups for m >= C/b (the first C/b are gathered before the
 //         kernel, by the whole chip); waits until U(m - C/b) has read the
 //         slots it overwrites;
-//   U(m)  up/gate + SwiGLU of minibatch m into h buffer m mod 2: waits for
-//         G(m) and for D(m - 2), the last reader of that h buffer;
+//   U(m)  up/gate + SwiGLU of minibatch m into h buffer m mod H: waits for
+//         G(m) and for D(m - H), the last reader of that h buffer;
 //   D(m)  down projection of minibatch m: each item waits for the up/gate
 //         items of its own row tile (all N blocks of that tile's h rows).
-// The GEMM workgroups take the U and D work items in the order U(0), then for
-// each m: U(m+1), D(m), so that a workgroup has up/gate work to do while the
-// last items of U(m) finish.  Every step waits only for steps earlier in that
-// order (and G(m) only for U(m - C/b), earlier still), and all workgroups are
-// resident at once (the grid is the chip's occupancy), so the step earliest in
-// the order that is not finished can always run: the kernel cannot deadlock.
+// H (2 to 4) follows the ring: C/b minibatches fit in it, so up/gate can run
+// up to C/b - 1 minibatches ahead of down.  The GEMM workgroups take the U and
+// D work items in the order U(0) .. U(H - 2), then for each m: U(m + H - 1),
+// D(m), so that several up/gate steps fill the chip while the down steps
+// trail them (a small minibatch's up/gate alone gives fewer work items than
+// there are CUs, each as long as the whole K loop).  U(m + H - 1) waits for
+// D(m - 1), the step just before it: every step waits only for steps earlier
+// in that order (and G(m) only for U(m - C/b), earlier still), and all
+// workgroups are resident at once (the grid is the chip's occupancy), so the
+// step earliest in the order that is not finished can always run: the kernel
+// cannot deadlock.
 // Each workgroup takes its items statically: the items of a step are cut into
 // 8 runs, one per XCD, as in the stream-ordered launches, and the GEMM
 // workgroups of an XCD deal its run among themselves.  A wait that spins past
@@ -670,13 +675,14 @@ __global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
     int lo, hi;
     my_items(n_items(m, nbu), lo, hi);
     if (lo >= hi) return;
-    // G(m) (memory workgroups, or before the kernel) and D(m - 2), the last reader of h buffer m mod 2
+    // G(m) (memory workgroups, or before the kernel) and D(m - n_h), the
+    // last reader of h buffer m mod n_h
     if (m >= ring_mb) wait_count(pa.gathered + m, pa.n_mem, pa.err);
-    if (m >= 2) wait_count(pa.down_done + (m - 2), n_items(m - 2, nbd), pa.err);
+    if (m >= pa.n_h) wait_count(pa.down_done + (m - pa.n_h), n_items(m - pa.n_h, nbd), pa.err);
     GemmArgs a = pa.up;
     a.tiles = pa.up.tiles + static_cast<int64_t>(m) * pa.up.max_tiles;
     a.tile_count = pa.up.tile_count + m;
-    a.C = pa.h + static_cast<int64_t>(m & 1) * pa.b * pa.up.N;
+    a.C = pa.h + static_cast<int64_t>(m % pa.n_h) * pa.b * pa.up.N;
     a.c_sub = static_cast<int64_t>(m) * pa.b;
     int* const tile_ctr = pa.upg_tile + static_cast<int64_t>(m) * pa.up.max_tiles;
     int done = 0;
@@ -696,7 +702,7 @@ __global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
     GemmArgs a = pa.down;
     a.tiles = pa.up.tiles + static_cast<int64_t>(m) * pa.up.max_tiles;
     a.tile_count = pa.up.tile_count + m;
-    a.A = pa.h + static_cast<int64_t>(m & 1) * pa.b * pa.up.N;
+    a.A = pa.h + static_cast<int64_t>(m % pa.n_h) * pa.b * pa.up.N;
     a.a_sub = static_cast<int64_t>(m) * pa.b;
     int* const tile_ctr = pa.upg_tile + static_cast<int64_t>(m) * pa.up.max_tiles;
     int done = 0;
@@ -709,9 +715,12 @@ __global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
     }
     signal_count(pa.down_done + m, done);
   };
-  if (pa.n_mb > 0) run_up(0);
+  // up/gate runs `ahead` minibatches in front of down: U(0) .. U(ahead - 1),
+  // then U(m + ahead), D(m) for each m
+  const int ahead = pa.n_h - 1;
+  for (int m = 0; m < ahead && m < pa.n_mb; ++m) run_up(m);
   for (int m = 0; m < pa.n_mb; ++m) {
-    if (m + 1 < pa.n_mb) run_up(m + 1);
+    if (m + ahead < pa.n_mb) run_up(m + ahead);
     run_down(m);
   }
 }
@@ -729,6 +738,7 @@ hipError_t run_pipeline(const PipeArgs& pa, hipStream_t stream) {
   const int64_t grid = resident / kXcds * kXcds;
   // GEMM workgroups on every XCD, and memory workgroups when some minibatch is gathered in the kernel
   if (pa.n_mem % kXcds || grid - pa.n_mem < kXcds) return hipErrorInvalidValue;
+  if (pa.n_h < 2 || pa.n_h > kMaxPipeH) return hipErrorInvalidValue;
   if (pa.n_mb > pa.C / pa.b && pa.n_mem <= 0) return hipErrorInvalidValue;
   kernel<<<static_cast<unsigned>(grid), 512, 0, stream>>>(pa);
   return hipGetLastError();

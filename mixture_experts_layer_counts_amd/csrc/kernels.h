@@ -138,11 +138,20 @@ struct PipeArgs {
   int L, k, D, n_mb, n_mem;
   int64_t b, C, max_rows;
   uint16_t* ring;
-  uint16_t* h;
+  uint16_t* h;    // n_h buffers of [b, I]: minibatch m writes buffer m mod n_h
+  int n_h;        // 2 .. kMaxPipeH; up/gate runs up to n_h - 1 minibatches ahead of down
   int *gathered, *upg, *down_done;
   int* upg_tile;  // [n_mb][up.max_tiles]: finished up/gate items of each row tile
   int* err;
 };
+constexpr int kMaxPipeH = 4;
+// h buffers of the persistent kernel for ring rows C and minibatch rows b:
+// C / b clamped to 2 .. kMaxPipeH (the ring bounds how far the gathers, and so
+// the up/gate steps, can run ahead).
+inline int pipeline_h_buffers(int64_t b, int64_t C) {
+  const int64_t q = b > 0 ? C / b : 2;
+  return static_cast<int>(q < 2 ? 2 : (q > kMaxPipeH ? kMaxPipeH : q));
+}
 // Workgroups the persistent kernel runs with for a tiling (all resident).
 int pipeline_workgroups(const RoutedTiling& tiling);
 hipError_t launch_pipeline(const PipeArgs& args, const RoutedTiling& tiling, hipStream_t stream);

@@ -139,8 +139,10 @@ Layout layout_of(const moe_shape* s) {
     L.h_s = take(s->minibatch_rows * (s->I / 32));
   } else {
     L.ring = take(sizeof(uint16_t) * s->ring_rows * s->D);
-    // the persistent kernel overlaps minibatch m+1's up/gate with m's down: two h buffers
-    L.h = take(sizeof(uint16_t) * s->minibatch_rows * s->I * (s->pipeline ? 2 : 1));
+    // the persistent kernel runs up/gate up to H - 1 minibatches ahead of
+    // down: H h buffers, H = C / b clamped to 2 .. 4
+    L.h = take(sizeof(uint16_t) * s->minibatch_rows * s->I *
+               (s->pipeline ? moe::pipeline_h_buffers(s->minibatch_rows, s->ring_rows) : 1));
   }
   L.pipe_counters = take(s->pipeline ? sizeof(int32_t) * (3 + L.max_tiles) * std::max<int64_t>(L.n_minibatches, 1)
                                      : 0);
@@ -677,6 +679,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     pa.max_rows = shape->max_rows;
     pa.ring = ring;
     pa.h = h;
+    pa.n_h = moe::pipeline_h_buffers(b, C);
     pa.gathered = counters;
     pa.upg = counters + L.n_minibatches;
     pa.down_done = counters + 2 * L.n_minibatches;

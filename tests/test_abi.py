@@ -214,9 +214,14 @@ def test_pipeline_shape_fields(lib):
     assert ws_bytes(lib, bad)[0] == -1
     assert ws_bytes(lib, shape_for(T=64, D=128, I=128, E=8, k=2, I_shared=128, precision="mxfp8",
                                    pipeline=True))[0] == -2
-    # it keeps two h buffers and per-minibatch counters in the workspace
+    # it keeps H = C/b (2 .. 4) h buffers and per-minibatch counters in the workspace
     plain = shape_for(T=64, D=128, I=64, E=8, k=2, minibatch_rows=32, ring_rows=64)
     assert ws_bytes(lib, ok)[1] >= ws_bytes(lib, plain)[1] + 32 * 64 * 2 + 3 * 4 * 4
+    for C, H in ((32, 2), (96, 3), (128, 4), (256, 4)):
+        deep = shape_for(T=64, D=128, I=64, E=8, k=2, minibatch_rows=32, ring_rows=C, pipeline=True,
+                         mem_workgroups=8)
+        flat = shape_for(T=64, D=128, I=64, E=8, k=2, minibatch_rows=32, ring_rows=C)
+        assert ws_bytes(lib, deep)[1] >= ws_bytes(lib, flat)[1] + (H - 1) * 32 * 64 * 2 + 3 * 4 * 4, C
 
 
 def test_backward_validates_before_any_launch(lib):

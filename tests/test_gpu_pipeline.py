@@ -23,17 +23,20 @@ pytestmark = pytest.mark.gpu
 CASES = [
     # name, workload, [(b, C, memory workgroups)]; tilings: 128-row tiles
     # (small b), 256-row (tiny minibatch counts) and 320-row (skewed320, all
-    # rows at once)
-    ("tiny", synth.workload("tiny", routing="gaussian"), [(16, 32, 8), (16, 16, 8), (32, 64, 16), (128, 128, 0)]),
+    # rows at once); rings of C/b = 3, 4 and 8 minibatches keep H = 3 and 4 h
+    # buffers, up/gate running 2 and 3 minibatches ahead of down
+    ("tiny", synth.workload("tiny", routing="gaussian"),
+     [(16, 32, 8), (16, 16, 8), (32, 64, 16), (128, 128, 0), (16, 48, 8), (16, 128, 8)]),
     ("ragged", synth.Workload("ragged", T=300, D=256, I=192, E=16, k=4, I_shared=128, seed=7, routing="gaussian"),
-     [(100, 300, 8), (100, 100, 24), (256, 512, 8), (1200, 1200, 0)]),
+     [(100, 300, 8), (100, 100, 24), (256, 512, 8), (1200, 1200, 0), (64, 192, 8), (100, 400, 16)]),
     ("mid", synth.workload("mid", routing="gaussian"),
-     [(512, 1024, 16), (512, 512, 32), (2048, 2048, 8), (4096, 8192, 16), (32768, 32768, 0)]),
+     [(512, 1024, 16), (512, 512, 32), (2048, 2048, 8), (4096, 8192, 16), (32768, 32768, 0), (512, 4096, 8),
+      (1024, 3072, 8)]),
     ("skewed320", synth.Workload("skewed320", T=1024, D=256, I=1024, E=24, k=6, I_shared=128, seed=9,
                                  routing="zipf"), [(6144, 6144, 0), (3072, 3072, 8)]),
     # 2048-row minibatches of ~256-row segments with I = 2048: 256-row tiles
     ("wideI", synth.Workload("wideI", T=2048, D=256, I=2048, E=32, k=4, I_shared=128, seed=19, routing="gaussian"),
-     [(2048, 4096, 8), (2048, 2048, 16)]),
+     [(2048, 4096, 8), (2048, 2048, 16), (1024, 4096, 8)]),
 ]
 
 
