@@ -114,7 +114,9 @@ typedef struct {
                                   (MoK paper §3.4, "Computation-Communication SM
                                   Tuning"); a multiple of 8, at least 8 when
                                   the ring holds fewer than all minibatches,
-                                  and leaving at least 8 for the GEMMs */
+                                  and leaving at least 8 for the GEMMs; unused
+                                  (every workgroup runs GEMM items) when the
+                                  ring holds all minibatches */
 } moe_shape;
 
 /* Expert weights, all K-contiguous (each output row is a contiguous K vector):

@@ -546,15 +546,18 @@ hipError_t run(const GemmArgs& a, hipStream_t stream) {
 // trail them (a small minibatch's up/gate alone gives fewer work items than
 // there are CUs, each as long as the whole K loop).  U(m + H - 1) waits for
 // D(m - 1), the step just before it: every step waits only for steps earlier
-// in that order (and G(m) only for U(m - C/b), earlier still), and all
-// workgroups are resident at once (the grid is the chip's occupancy), so the
-// step earliest in the order that is not finished can always run: the kernel
-// cannot deadlock.
-// Each workgroup takes its items statically: the items of a step are cut into
-// 8 runs, one per XCD, as in the stream-ordered launches, and the GEMM
-// workgroups of an XCD deal its run among themselves.  A wait that spins past
-// about a second (a workgroup that cannot be resident, for instance) sets
-// MOE_DEVERR_PIPELINE and stops waiting, so the kernel always ends.
+// in that order (and G(m) only for U(m - C/b), earlier still).
+// The items of a step are cut into 8 runs, one per XCD, as in the
+// stream-ordered launches, and an XCD's GEMM workgroups take the items of its
+// runs, in step order, from one queue (an atomic counter): a workgroup that
+// finishes early takes the next item (with a single minibatch they are dealt
+// round-robin instead, in the same order).  All workgroups are resident at once
+// (the grid is the chip's occupancy), so the kernel cannot deadlock: the
+// earliest unfinished item waits for nothing unfinished, and it is either
+// running or the next item of its XCD's queue, which every item taken before
+// it has finished and so left a workgroup free to take it.  A wait that spins
+// past about a second (a workgroup that cannot be resident, for instance)
+// sets MOE_DEVERR_PIPELINE and stops waiting, so the kernel always ends.
 //
 // Visibility: a finished step's writers drain their stores (s_waitcnt), pass a
 // barrier, and one thread adds to the counter with an agent-scope release,
@@ -648,21 +651,38 @@ __global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
     return;
   }
 
-  // ---- GEMM workgroup: the U and D items of its XCD's runs ----
+  // ---- GEMM workgroup: items of its XCD's runs, taken from the XCD's queue ----
+  // The items of a step are cut into 8 runs, one per XCD, as in the
+  // stream-ordered launches.  An XCD's runs of all steps, in step order, are
+  // numbered consecutively; a GEMM workgroup takes the next number from its
+  // XCD's queue head (one atomic), runs that item and takes another, so a
+  // workgroup whose items were short takes more of them (an up/gate item runs
+  // the whole K = D loop, a down item K = I).  Every workgroup of the XCD walks
+  // the same steps to map its number to (step, item).  Which workgroup runs an
+  // item does not change the item's arithmetic.
+  // With one minibatch there is nothing to even out between steps, and the
+  // numbers are dealt statically instead (the XCD's GEMM workgroup r takes
+  // r, r + nr, ...), which saves each item the queue's atomic round trip.
+  int* const head = pa.queue + xcd;
+  int* const slot = pa.queue + kXcds + blockIdx.x;
   const int r = rx - mem_per_xcd, nr = static_cast<int>(gridDim.x) / kXcds - mem_per_xcd;
-  // The items of the steps are dealt to the XCD's GEMM workgroups round-robin
-  // in step order, each step starting where the last one stopped (`cursor`),
-  // so that consecutive steps (U(m+1) and D(m)) land on different workgroups
-  // and run side by side; this workgroup takes positions j0, j0 + nr, ... of
-  // its XCD's run of the step's n items.
-  int cursor = 0;
-  auto my_items = [&](int n, int& lo, int& hi) __attribute__((always_inline)) {
+  const bool from_queue = pa.n_mb > 1;
+  int dealt = r - nr;
+  auto take = [&]() __attribute__((always_inline)) {
+    if (!from_queue) return dealt += nr;
+    __syncthreads();  // every wave has read the previous number
+    if (threadIdx.x == 0)
+      __hip_atomic_store(slot, __hip_atomic_fetch_add(head, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+  };
+  // this XCD's run of a step with n items: [run0, run0 + len)
+  auto xcd_run = [&](int n, int& run0) __attribute__((always_inline)) {
     const int chunk = (n + kXcds - 1) / kXcds;
-    const int run0 = xcd * chunk, run1 = min(n, (xcd + 1) * chunk);
-    const int len = run1 > run0 ? run1 - run0 : 0;
-    lo = run0 + (r - cursor + nr) % nr;
-    hi = run1;
-    cursor = (cursor + len) % nr;
+    run0 = xcd * chunk;
+    const int run1 = min(n, (xcd + 1) * chunk);
+    return run1 > run0 ? run1 - run0 : 0;
   };
   // row tile of item w of a step with nb N blocks (the decoding gemm_item uses)
   auto item_tile = [&](const int4* tiles, int w, int nb) __attribute__((always_inline)) {
@@ -671,10 +691,7 @@ __global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
     grouped_item(w - g.w * nb, g.x >> 10, nb, nblk, lt);
     return g.w + lt;
   };
-  auto run_up = [&](int m) __attribute__((always_inline)) {
-    int lo, hi;
-    my_items(n_items(m, nbu), lo, hi);
-    if (lo >= hi) return;
+  auto up_item = [&](int m, int w) __attribute__((always_inline)) {
     // G(m) (memory workgroups, or before the kernel) and D(m - n_h), the
     // last reader of h buffer m mod n_h
     if (m >= ring_mb) wait_count(pa.gathered + m, pa.n_mem, pa.err);
@@ -684,44 +701,57 @@ __global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
     a.tile_count = pa.up.tile_count + m;
     a.C = pa.h + static_cast<int64_t>(m % pa.n_h) * pa.b * pa.up.N;
     a.c_sub = static_cast<int64_t>(m) * pa.b;
-    int* const tile_ctr = pa.upg_tile + static_cast<int64_t>(m) * pa.up.max_tiles;
-    int done = 0;
-    for (int w = lo; w < hi; w += nr, ++done) {
-      const int wu = __builtin_amdgcn_readfirstlane(w);
-      gemm_item<BMU, BNU, WMU, WNU, kEpiSwiGLU, true, kStageK>(a, wu, nbu, 1, smem, wave);
-      // the tile's h columns of this item are written (the barrier inside
-      // also lets the next item refill the LDS)
-      signal_count(tile_ctr + item_tile(a.tiles, wu, nbu), 1);
+    gemm_item<BMU, BNU, WMU, WNU, kEpiSwiGLU, true, kStageK>(a, w, nbu, 1, smem, wave);
+    // the tile's h columns of this item are written: count it for the
+    // tile's down items (a release: they read those h rows) and for the step
+    // (relaxed: its waiters, the gathers, only need this item's loads of the
+    // ring rows to have landed, which the wait on the load counter gives)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int* const tile_ctr = pa.upg_tile + static_cast<int64_t>(m) * pa.up.max_tiles;
+      __hip_atomic_fetch_add(tile_ctr + item_tile(a.tiles, w, nbu), 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(pa.upg + m, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    signal_count(pa.upg + m, done);
   };
-  auto run_down = [&](int m) __attribute__((always_inline)) {
-    int lo, hi;
-    my_items(n_items(m, nbd), lo, hi);
-    if (lo >= hi) return;
+  auto down_item = [&](int m, int w) __attribute__((always_inline)) {
     GemmArgs a = pa.down;
     a.tiles = pa.up.tiles + static_cast<int64_t>(m) * pa.up.max_tiles;
     a.tile_count = pa.up.tile_count + m;
     a.A = pa.h + static_cast<int64_t>(m % pa.n_h) * pa.b * pa.up.N;
     a.a_sub = static_cast<int64_t>(m) * pa.b;
-    int* const tile_ctr = pa.upg_tile + static_cast<int64_t>(m) * pa.up.max_tiles;
-    int done = 0;
-    for (int w = lo; w < hi; w += nr, ++done) {
-      const int wd = __builtin_amdgcn_readfirstlane(w);
-      // every up/gate item of this item's row tile: its h rows (the barrier
-      // inside also lets this item refill the LDS)
-      wait_count(tile_ctr + item_tile(a.tiles, wd, nbd), nbu, pa.err);
-      gemm_item<BMD, BND, WMD, WND, kEpiBF16, true, kStageK>(a, wd, nbd, 1, smem, wave);
-    }
-    signal_count(pa.down_done + m, done);
+    // every up/gate item of this item's row tile: its h rows (the barrier
+    // inside also lets this item refill the LDS)
+    const int* const tile_ctr = pa.upg_tile + static_cast<int64_t>(m) * pa.up.max_tiles;
+    wait_count(const_cast<int*>(tile_ctr) + item_tile(a.tiles, w, nbd), nbu, pa.err);
+    gemm_item<BMD, BND, WMD, WND, kEpiBF16, true, kStageK>(a, w, nbd, 1, smem, wave);
+    // relaxed, and with no wait on this item's output stores: the waiter
+    // (up/gate of m + n_h) only needs this item's loads of the h rows it will
+    // overwrite to have landed, and every wave's K loop ends with its loads
+    // drained, before the barrier that opens the epilogue
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(pa.down_done + m, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   // up/gate runs `ahead` minibatches in front of down: U(0) .. U(ahead - 1),
   // then U(m + ahead), D(m) for each m
   const int ahead = pa.n_h - 1;
-  for (int m = 0; m < ahead && m < pa.n_mb; ++m) run_up(m);
+  int number = take(), base = 0;  // this workgroup's queue number; the XCD's items in the steps walked so far
+  // (one loop per item kind, so that each loop holds one GEMM's code)
+  auto step_up = [&](int m) __attribute__((always_inline)) {
+    int run0;
+    const int len = xcd_run(n_items(m, nbu), run0);
+    for (; number < base + len; number = take()) up_item(m, run0 + number - base);
+    base += len;
+  };
+  auto step_down = [&](int m) __attribute__((always_inline)) {
+    int run0;
+    const int len = xcd_run(n_items(m, nbd), run0);
+    for (; number < base + len; number = take()) down_item(m, run0 + number - base);
+    base += len;
+  };
+  for (int m = 0; m < ahead && m < pa.n_mb; ++m) step_up(m);
   for (int m = 0; m < pa.n_mb; ++m) {
-    if (m + ahead < pa.n_mb) run_up(m + ahead);
-    run_down(m);
+    if (m + ahead < pa.n_mb) step_up(m + ahead);
+    step_down(m);
   }
 }
 
@@ -738,7 +768,7 @@ hipError_t run_pipeline(const PipeArgs& pa, hipStream_t stream) {
   const int64_t grid = resident / kXcds * kXcds;
   // GEMM workgroups on every XCD, and memory workgroups when some minibatch is gathered in the kernel
   if (pa.n_mem % kXcds || grid - pa.n_mem < kXcds) return hipErrorInvalidValue;
-  if (pa.n_h < 2 || pa.n_h > kMaxPipeH) return hipErrorInvalidValue;
+  if (pa.n_h < 2 || pa.n_h > kMaxPipeH || grid > kPipeMaxGrid || !pa.queue) return hipErrorInvalidValue;
   if (pa.n_mb > pa.C / pa.b && pa.n_mem <= 0) return hipErrorInvalidValue;
   kernel<<<static_cast<unsigned>(grid), 512, 0, stream>>>(pa);
   return hipGetLastError();

@@ -142,8 +142,11 @@ struct PipeArgs {
   int n_h;        // 2 .. kMaxPipeH; up/gate runs up to n_h - 1 minibatches ahead of down
   int *gathered, *upg, *down_done;
   int* upg_tile;  // [n_mb][up.max_tiles]: finished up/gate items of each row tile
+  int* queue;     // [kPipeQueueInts]: 8 per-XCD item queue heads, then one word per workgroup; zero on entry
   int* err;
 };
+constexpr int kPipeMaxGrid = 1024;
+constexpr int kPipeQueueInts = 8 + kPipeMaxGrid;
 constexpr int kMaxPipeH = 4;
 // h buffers of the persistent kernel for ring rows C and minibatch rows b:
 // C / b clamped to 2 .. kMaxPipeH (the ring bounds how far the gathers, and so

@@ -32,7 +32,7 @@ struct Layout {
   int max_tiles;
   int routed_bm;      // tile height of the routed GEMMs' tile lists
   int bn_up, bn_down;  // output columns per work item of the routed bf16 GEMMs
-  size_t pipe_counters;  // pipeline == 1: (3 + max_tiles) * n_minibatches ints
+  size_t pipe_counters;  // pipeline == 1: (3 + max_tiles) * n_minibatches ints, then the work queues
   int64_t y_rows;
 };
 
@@ -144,7 +144,8 @@ Layout layout_of(const moe_shape* s) {
     L.h = take(sizeof(uint16_t) * s->minibatch_rows * s->I *
                (s->pipeline ? moe::pipeline_h_buffers(s->minibatch_rows, s->ring_rows) : 1));
   }
-  L.pipe_counters = take(s->pipeline ? sizeof(int32_t) * (3 + L.max_tiles) * std::max<int64_t>(L.n_minibatches, 1)
+  L.pipe_counters = take(s->pipeline ? sizeof(int32_t) * ((3 + L.max_tiles) * std::max<int64_t>(L.n_minibatches, 1) +
+                                                          moe::kPipeQueueInts)
                                      : 0);
   L.Y = take(sizeof(uint16_t) * L.y_rows * s->D);
   L.shared_out = take(sizeof(float) * s->T * s->D);
@@ -660,7 +661,8 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     // the persistent kernel gathers the rest while it runs the GEMMs
     const int64_t pre = std::min<int64_t>(C / b, L.n_minibatches);
     int32_t* counters = at<int32_t>(ws, L.pipe_counters);
-    MOE_TRY_HIP(moe::launch_clear_int(counters, static_cast<int>((3 + L.max_tiles) * L.n_minibatches), s));
+    const int64_t n_counters = (3 + L.max_tiles) * L.n_minibatches;
+    MOE_TRY_HIP(moe::launch_clear_int(counters, static_cast<int>(n_counters + moe::kPipeQueueInts), s));
     for (int64_t m = 0; m < pre; ++m) MOE_TRY_HIP(gather(m));
     moe::PipeArgs pa{};
     pa.up = up_args(0, h);
@@ -673,7 +675,9 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     pa.k = k;
     pa.D = D;
     pa.n_mb = static_cast<int>(L.n_minibatches);
-    pa.n_mem = shape->mem_workgroups;
+    // memory workgroups only when some minibatch is gathered inside the
+    // kernel; otherwise every workgroup runs GEMM items
+    pa.n_mem = L.n_minibatches > C / b ? shape->mem_workgroups : 0;
     pa.b = b;
     pa.C = C;
     pa.max_rows = shape->max_rows;
@@ -684,6 +688,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     pa.upg = counters + L.n_minibatches;
     pa.down_done = counters + 2 * L.n_minibatches;
     pa.upg_tile = counters + 3 * L.n_minibatches;
+    pa.queue = counters + n_counters;
     pa.err = at<int>(ws, L.err);
     {
       ProbeScope probe(MOE_K_PIPELINE, s);
