@@ -1,5 +1,5 @@
 /*
- * moe.h - C ABI of the MI355X (gfx950) MoE-layer forward library, libmoe.so.
+ * moe.h - C ABI of the MI355X (gfx950) MoE-layer library, libmoe.so.
  *
  * The library computes the forward pass of one DeepSeek-V3-style MoE layer on
  * one GPU's share of the work (MoK paper "Mixture-of-Kittens: MoE Megakernel
@@ -16,6 +16,8 @@
  *   moe_forward   shared expert, then per minibatch of b routed rows: gather
  *                 into the ring buffer, grouped up/gate GEMM with SwiGLU,
  *                 grouped down GEMM; then the fixed-order gate-weighted combine.
+ * and, for training on one GPU, the backward pass of such a forward
+ * (moe_backward_prepare once per weight set, then moe_backward).
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers, allocated and owned by the caller;
@@ -291,8 +293,8 @@ moe_status moe_backward_prepare(const moe_shape* shape, const moe_weights* weigh
                                 const moe_bwd_weights* bw, void* stream);
 
 /* Bytes of device workspace moe_backward needs (a separate allocation from
- * the forward's: about 140 bytes per routed row and hidden column at the
- * DeepSeek-V3 shape, 9 GB). */
+ * the forward's; 10.0 GB at the DeepSeek-V3 shape, mostly the routed rows'
+ * intermediates and their transposed copies). */
 moe_status moe_backward_workspace_bytes(const moe_shape* shape, size_t* bytes);
 
 /*
