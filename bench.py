@@ -21,6 +21,8 @@ when every expert is local) and its fraction of the dense MFMA peak of the
 routed precision, a roofline of the dominant kernel (up/gate + SwiGLU) timed
 with HIP events inside the timed region, a per-kernel breakdown with each
 kernel's algorithmic bytes and FLOP, and the CPU oracle timed on a sample.
+The bf16 workloads also time the persistent routed kernel at minibatches of
+512, 2048 and 8192 rows (a ring of four) under "granularity_sweep".
 """
 
 from __future__ import annotations
@@ -72,10 +74,12 @@ def parse():
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
     ap.add_argument("--backward", action="store_true",
                     help="also time moe_backward on the step's routes and a seeded output gradient (bf16, R = 1)")
-    ap.add_argument("--sweep", default="", metavar="B[:C[:M]],...",
-                    help="after the main run, time the step at these minibatch sizes b (ring C, default b; with "
-                         "--pipeline, M memory workgroups, default --mem-workgroups) and report them under "
-                         "'granularity_sweep'")
+    ap.add_argument("--sweep", default="", metavar="[p]B[:C[:M]],...",
+                    help="after the main run, time the step at these minibatch sizes b (ring C, default b; a 'p' "
+                         "prefix, or --pipeline, runs the persistent routed kernel with M memory workgroups, default "
+                         "--mem-workgroups) and report them under 'granularity_sweep'; by default the bf16 "
+                         "workloads sweep the persistent kernel at b = 512, 2048 and 8192 with C = 4b")
+    ap.add_argument("--no-granularity", action="store_true", help="skip the default granularity sweep")
     ap.add_argument("--graph", action="store_true",
                     help="in the sweep, also time the step captured once in a HIP graph and replayed "
                          "(launch overhead removed)")
@@ -167,10 +171,10 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
     x, wr, logits_in = inp["x"], inp["w_router"], inp.get("logits")
     out = torch.empty((w.T, w.D), dtype=torch.bfloat16, device=dev)
 
-    def make(b, C, mem=None):
+    def make(b, C, mem=None, pipeline=None):
         layer = MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
                                    precision=precision, shared_precision=args.shared_precision,
-                                   pipeline=args.pipeline,
+                                   pipeline=args.pipeline if pipeline is None else pipeline,
                                    mem_workgroups=args.mem_workgroups if mem is None else mem), device=dev)
 
         def step():
@@ -230,9 +234,10 @@ def setup_ep64(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
     x_local = x_pool[c * N:(c + 1) * N]
     out = torch.empty((N, w.D), dtype=torch.bfloat16, device=dev)
 
-    def make(b, C, mem=None):
+    def make(b, C, mem=None, pipeline=None):
         layer = MoELayer(shape_for(N, w.D, w.I, E_total, k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
-                                   precision=precision, R=R, rank=c, max_rows=P, pipeline=args.pipeline,
+                                   precision=precision, R=R, rank=c, max_rows=P,
+                                   pipeline=args.pipeline if pipeline is None else pipeline,
                                    mem_workgroups=args.mem_workgroups if mem is None else mem), device=dev)
 
         def step():
@@ -438,6 +443,9 @@ def main():
 
     if getattr(job, "weight_quantize", None):
         result["weight_quantize"] = job.weight_quantize  # ahead of time, not part of the step
+    if not args.sweep and not args.no_granularity and job.precision == "bf16" and job.P > 8192:
+        # the persistent routed kernel at small minibatches, a ring of four
+        args.sweep = "p512:2048,p2048:8192,p8192:32768"
     if args.sweep:
         result["granularity_sweep"] = sweep(job, args, torch)
 
@@ -561,11 +569,12 @@ def sweep(job, args, torch):
     out = []
     job.layer = None  # release the main workspace first
     for item in args.sweep.split(","):
-        parts = item.split(":")
+        persistent = args.pipeline or item.startswith("p")
+        parts = item.lstrip("p").split(":")
         b = min(int(parts[0]), job.P)
-        C = int(parts[1]) if len(parts) > 1 and parts[1] else b
+        C = min(int(parts[1]), -(-job.P // b) * b) if len(parts) > 1 and parts[1] else b
         mem = int(parts[2]) if len(parts) > 2 else args.mem_workgroups
-        layer, step = job.make(b, C, mem)
+        layer, step = job.make(b, C, mem, pipeline=persistent)
         for _ in range(2):
             step()
         torch.cuda.synchronize()
@@ -578,8 +587,9 @@ def sweep(job, args, torch):
         if layer.device_error():
             raise RuntimeError(f"device error word {layer.device_error():#x} at b={b} C={C}")
         e = {"minibatch_rows": b, "ring_rows": C, "minibatches": (job.P + b - 1) // b,
-             "ms_per_step": round(ms, 4), "tokens_per_s": round(job.T / (ms * 1e-3), 1)}
-        if args.pipeline:
+             "ms_per_step": round(ms, 4), "tokens_per_s": round(job.T / (ms * 1e-3), 1),
+             "persistent": persistent}
+        if persistent:
             e["mem_workgroups"] = mem
         if args.graph:
             # the same step captured once (the library allocates nothing and
@@ -604,7 +614,7 @@ def sweep(job, args, torch):
                 raise RuntimeError(f"device error word {layer.device_error():#x} at b={b} C={C} (graph)")
             del g
         out.append(e)
-        log(f"sweep b={b} C={C}" + (f" mem={mem}" if args.pipeline else "") + f": {ms:.3f} ms/step" +
+        log(f"sweep b={b} C={C}" + (f" persistent mem={mem}" if persistent else "") + f": {ms:.3f} ms/step" +
             (f", graph {e['graph_ms_per_step']:.3f}" if args.graph else ""))
         del layer, step
         torch.cuda.empty_cache()
