@@ -24,11 +24,13 @@
 // Work order (routed).  The 256 MI355X CUs sit in 8 XCDs, each with its own
 // L2, and workgroups are dealt to XCDs round-robin.  Work items are ordered
 // expert-major, then by group of row tiles, then by N block, then by row tile
-// in the group (grouped_item), and cut into 8 contiguous runs, one per XCD,
-// whose workgroups walk it side by side: so the row tiles of one (expert, N
-// block) (which share the same weight rows) and the N-block tiles of one
-// group (which share the same activation rows) run close together on one XCD
-// and meet in its L2, while every weight byte is fetched from HBM about once
+// in the group (grouped_item), and cut into 8 contiguous runs, one per XCD
+// (balanced by an estimate of each tile's cost when the tile list comes with
+// runs, else of equal item count), whose workgroups walk it side by side: so
+// the row tiles of one (expert, N block) (which share the same weight rows)
+// and the N-block tiles of one group (which share the same activation rows)
+// run close together on one XCD and meet in its L2, while every weight byte
+// is fetched from HBM about once
 // for each group of row tiles.  With BM = 256 an expert's rows at the
 // DeepSeek-V3 shape (about 256 per expert) mostly fit in one tile; 32-row
 // blocks past the end of a tile are not multiplied.
@@ -453,14 +455,19 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
 }
 
 // Work items are split into 8 contiguous runs, one per XCD (workgroups are
-// dealt to XCDs round-robin, so workgroup b sits on XCD b mod 8), and
-// workgroup b takes item b / 8 of its XCD's run.  The routed down projection
-// launches only as many workgroups as fit on the chip at once, and workgroup
-// b walks items b / 8, b / 8 + G, b / 8 + 2G, ... of its run (G = workgroups
-// per XCD), so the XCD's workgroups still move through the run side by side:
-// a workgroup that stays resident overlaps one item's output stores with the
-// next item's first loads, where a fresh workgroup would first wait for the
-// stores to drain and then for its loads.
+// dealt to XCDs round-robin, so workgroup b sits on XCD b mod 8): runs of
+// equal item count, or, for a routed list that comes with them, the list's
+// cost-balanced runs (tile_runs).  Workgroup b takes item b / 8 of its XCD's
+// run; the grid holds, per XCD, as many workgroups as the longest run may
+// have items (tile_run_cap tiles' worth for balanced runs).
+// The routed down projection instead launches only as many workgroups as fit
+// on the chip at once, and workgroup b walks items b / 8, b / 8 + G, b / 8 +
+// 2G, ... of its run (G = workgroups per XCD), so the XCD's workgroups still
+// move through the run side by side: a workgroup that stays resident overlaps
+// one item's output stores with the next item's first loads, where a fresh
+// workgroup would first wait for the stores to drain and then for its loads.
+// (A loop over items in the other kernels measured slower: it raises their
+// register pressure.)
 template <int BM, int BN, int WM, int WN, int EPI, bool ROUTED, int BK>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args) {
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
@@ -468,19 +475,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmArgs args)
   static_assert(LDS_BYTES <= kLdsBytes, "LDS rings");
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const int n_blocks = (args.N + BN - 1) / BN;
-  const int tcount = ROUTED ? *args.tile_count : (args.dense_rows + BM - 1) / BM;
+  const int xcd = static_cast<int>(blockIdx.x) % kXcds;
+  int run0, len;
+  if (ROUTED && args.tile_runs) {  // positions in 1/kTileRunFrac of a tile
+    run0 = static_cast<int>(static_cast<int64_t>(__builtin_amdgcn_readfirstlane(args.tile_runs[xcd])) * n_blocks /
+                            kTileRunFrac);
+    len = static_cast<int>(static_cast<int64_t>(__builtin_amdgcn_readfirstlane(args.tile_runs[xcd + 1])) * n_blocks /
+                           kTileRunFrac) -
+          run0;
+  } else {
+    const int tcount = ROUTED ? *args.tile_count : (args.dense_rows + BM - 1) / BM;
+    const int S = ROUTED ? 1 : args.k_splits;
+    const int W = tcount * n_blocks * S * (!ROUTED && args.k_groups ? args.n_groups : 1);
+    const int chunk = (W + kXcds - 1) / kXcds;
+    run0 = xcd * chunk;
+    len = W - run0 < chunk ? W - run0 : chunk;
+  }
   const int S = ROUTED ? 1 : args.k_splits;  // K ranges (dense only), each with its own output plane
-  const int W = tcount * n_blocks * S * (!ROUTED && args.k_groups ? args.n_groups : 1);
-  const int chunk = (W + kXcds - 1) / kXcds;
-  const int run0 = (static_cast<int>(blockIdx.x) % kXcds) * chunk;
   const int first = static_cast<int>(blockIdx.x) / kXcds;
+  const int per_xcd = static_cast<int>(gridDim.x) / kXcds;  // the grid is a multiple of kXcds
   const int wave0 = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   if constexpr (!(EPI == kEpiBF16 && ROUTED)) {
-    if (first < chunk && run0 + first < W)
-      gemm_item<BM, BN, WM, WN, EPI, ROUTED, BK>(args, run0 + first, n_blocks, S, smem, wave0);
+    if (first < len) gemm_item<BM, BN, WM, WN, EPI, ROUTED, BK>(args, run0 + first, n_blocks, S, smem, wave0);
   } else {
-    const int per_xcd = static_cast<int>(gridDim.x) / kXcds;  // the grid is a multiple of kXcds
-    for (int local = first; local < chunk && run0 + local < W; local += per_xcd) {
+    for (int local = first; local < len; local += per_xcd) {
       // the previous item's copy-out has read the LDS before this item's loads refill it
       if (local > first) __syncthreads();
       gemm_item<BM, BN, WM, WN, EPI, ROUTED, BK>(args, __builtin_amdgcn_readfirstlane(run0 + local), n_blocks, S,
@@ -500,8 +518,9 @@ hipError_t run(const GemmArgs& a, hipStream_t stream) {
   // Resident workgroups walk several items only for the routed down
   // projection, whose items end in large output stores (a 320 x 256 bf16
   // tile after 32 K stages); elsewhere one item per workgroup measured as
-  // fast or faster.
-  int64_t cap = work;
+  // fast or faster, and a list with balanced XCD runs gets room for runs of
+  // up to tile_run_cap tiles on every XCD.
+  int64_t cap = (ROUTED && a.tile_runs) ? int64_t(kXcds) * tile_run_cap(a.max_tiles) * n_blocks : work;
   if (EPI == kEpiBF16 && ROUTED) {
     static std::atomic<int64_t> resident_cache{0};
     int64_t resident = resident_cache.load(std::memory_order_relaxed);
@@ -677,9 +696,15 @@ __global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
     __syncthreads();
     return __builtin_amdgcn_readfirstlane(__hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
   };
-  // this XCD's run of a step with n items: [run0, run0 + len)
-  auto xcd_run = [&](int n, int& run0) __attribute__((always_inline)) {
-    const int chunk = (n + kXcds - 1) / kXcds;
+  // this XCD's run of minibatch m's step with nb N blocks: [run0, run0 + len)
+  auto xcd_run = [&](int m, int nb, int& run0) __attribute__((always_inline)) {
+    if (pa.up.tile_runs) {
+      const int32_t* tr = pa.up.tile_runs + static_cast<int64_t>(m) * kTileRunBounds;
+      run0 = static_cast<int>(static_cast<int64_t>(__builtin_amdgcn_readfirstlane(tr[xcd])) * nb / kTileRunFrac);
+      return static_cast<int>(static_cast<int64_t>(__builtin_amdgcn_readfirstlane(tr[xcd + 1])) * nb / kTileRunFrac) -
+             run0;
+    }
+    const int n = n_items(m, nb), chunk = (n + kXcds - 1) / kXcds;
     run0 = xcd * chunk;
     const int run1 = min(n, (xcd + 1) * chunk);
     return run1 > run0 ? run1 - run0 : 0;
@@ -738,13 +763,13 @@ __global__ __launch_bounds__(512) void pipeline_kernel(const PipeArgs pa) {
   // (one loop per item kind, so that each loop holds one GEMM's code)
   auto step_up = [&](int m) __attribute__((always_inline)) {
     int run0;
-    const int len = xcd_run(n_items(m, nbu), run0);
+    const int len = xcd_run(m, nbu, run0);
     for (; number < base + len; number = take()) up_item(m, run0 + number - base);
     base += len;
   };
   auto step_down = [&](int m) __attribute__((always_inline)) {
     int run0;
-    const int len = xcd_run(n_items(m, nbd), run0);
+    const int len = xcd_run(m, nbd, run0);
     for (; number < base + len; number = take()) down_item(m, run0 + number - base);
     base += len;
   };

@@ -484,27 +484,42 @@ __device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int 
   }
 }
 
-// Work items are cut into 8 contiguous runs, one per XCD, and workgroup b
-// takes item b / 8 of the run of XCD b mod 8.  The down projection launches
-// only as many workgroups as fit on the chip at once, and they walk their
-// XCD's run side by side (workgroup b takes items b / 8, b / 8 + G, ... with G
-// workgroups per XCD), so that one item's output stores drain under the next
-// item's first loads.
+// Work items are cut into 8 contiguous runs, one per XCD: runs of equal item
+// count, or the list's cost-balanced runs (tile_runs) when it comes with
+// them.  Workgroup b takes item b / 8 of the run of XCD b mod 8,
+// and the grid holds, per XCD, as many workgroups as the longest run may have
+// items.  The down projection instead launches only as many workgroups as fit
+// on the chip at once, and they walk their XCD's run side by side (workgroup
+// b takes items b / 8, b / 8 + G, ... with G workgroups per XCD), so that one
+// item's output stores drain under the next item's first loads.  (A loop over
+// items in the up/gate kernel measured 5% slower: it raises its register
+// pressure.)
 template <int BN, int EPI>
 __global__ __launch_bounds__(64 * kNW) void gemm_mx_kernel(const MxGemmArgs args) {
   constexpr int NB = (EPI == kEpiSwiGLU) ? 2 : 1;
   __shared__ __attribute__((aligned(1024))) char smem[kNSA * kMxBM * kRB + kNSB * NB * BN * kRB];
   const int n_blocks = (args.N + BN - 1) / BN;
-  const int W = *args.tile_count * n_blocks;
-  const int chunk = (W + kXcds - 1) / kXcds;
-  const int run0 = (static_cast<int>(blockIdx.x) % kXcds) * chunk;
+  const int xcd = static_cast<int>(blockIdx.x) % kXcds;
+  int run0, len;
+  if (args.tile_runs) {  // positions in 1/kTileRunFrac of a tile
+    run0 = static_cast<int>(static_cast<int64_t>(__builtin_amdgcn_readfirstlane(args.tile_runs[xcd])) * n_blocks /
+                            kTileRunFrac);
+    len = static_cast<int>(static_cast<int64_t>(__builtin_amdgcn_readfirstlane(args.tile_runs[xcd + 1])) * n_blocks /
+                           kTileRunFrac) -
+          run0;
+  } else {
+    const int W = *args.tile_count * n_blocks;
+    const int chunk = (W + kXcds - 1) / kXcds;
+    run0 = xcd * chunk;
+    len = W - run0 < chunk ? W - run0 : chunk;
+  }
   const int first = static_cast<int>(blockIdx.x) / kXcds;
+  const int per_xcd = static_cast<int>(gridDim.x) / kXcds;  // the grid is a multiple of kXcds
   const int wave0 = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   if constexpr (EPI != kEpiBF16) {
-    if (first < chunk && run0 + first < W) gemm_mx_item<BN, EPI>(args, run0 + first, n_blocks, smem, wave0);
+    if (first < len) gemm_mx_item<BN, EPI>(args, run0 + first, n_blocks, smem, wave0);
   } else {
-    const int per_xcd = static_cast<int>(gridDim.x) / kXcds;  // the grid is a multiple of kXcds
-    for (int local = first; local < chunk && run0 + local < W; local += per_xcd) {
+    for (int local = first; local < len; local += per_xcd) {
       // the previous item's copy-out has read the LDS before this item's loads refill it
       if (local > first) __syncthreads();
       gemm_mx_item<BN, EPI>(args, __builtin_amdgcn_readfirstlane(run0 + local), n_blocks, smem, wave0);
@@ -521,8 +536,9 @@ hipError_t run_mx(const MxGemmArgs& a, hipStream_t stream) {
   auto kernel = gemm_mx_kernel<BN, EPI>;
   // resident workgroups walk several items only for the down projection,
   // whose items end in large output stores; the up/gate items measured faster
-  // one per workgroup
-  int64_t cap = work;
+  // one per workgroup, with room for balanced runs of up to tile_run_cap
+  // tiles on every XCD
+  int64_t cap = a.tile_runs ? int64_t(kXcds) * tile_run_cap(a.max_tiles) * n_blocks : work;
   if (EPI == kEpiBF16) {
     static std::atomic<int64_t> resident_cache{0};
     int64_t resident = resident_cache.load(std::memory_order_relaxed);

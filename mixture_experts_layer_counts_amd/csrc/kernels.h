@@ -26,8 +26,23 @@ hipError_t launch_schedule(const int32_t* routes, int R, int NK, int c, int L, i
                            int32_t* counts, int32_t* offsets, int32_t* sched_src, int32_t* route_dst,
                            const SchedScratch& s, int* err, hipStream_t stream);
 
+// XCD runs of a tile list: the GEMM kernels cut a list's work items (in
+// their work order, n_blocks per row tile) into one contiguous run per XCD.
+// The boundaries are positions counted in 1/kTileRunFrac of a tile: with N
+// blocks of nb items per tile, run x holds items [floor(runs[x] nb /
+// kTileRunFrac), floor(runs[x + 1] nb / kTileRunFrac)); runs[0] = 0 and
+// runs[8] = kTileRunFrac times the tile count.
+constexpr int kTileRunBounds = 9;
+constexpr int kTileRunFrac = 64;
+// Most tiles one run may span, for lists of at most max_tiles tiles: twice
+// the equal share of the largest list.  The up/gate GEMMs launch this many
+// tiles' items per XCD, one workgroup each.
+__host__ __device__ inline int tile_run_cap(int max_tiles) { return (max_tiles + 3) / 4; }
+// `runs` (kTileRunBounds words per minibatch, each run spanning at most
+// tile_run_cap(max_tiles) tiles) may be NULL: the kernels then cut the items
+// into runs of equal count.
 hipError_t launch_build_tiles(const int32_t* offsets, int L, int64_t b, int64_t max_rows, int BM, int n_minibatches,
-                              int max_tiles, int4* tiles, int32_t* tile_count, hipStream_t stream);
+                              int max_tiles, int4* tiles, int32_t* tile_count, int32_t* runs, hipStream_t stream);
 
 // Tile list of a dense GEMM run through the routed kernels: rows 0 .. rows-1 as
 // one segment of expert 0, cut into ceil(rows / BM) tiles of equal height
@@ -61,6 +76,7 @@ struct GemmArgs {
   int64_t c_sub;
   const int4* tiles;         // routed: {expert, p0, rows, 0}; NULL: dense rows 0..dense_rows-1
   const int32_t* tile_count;  // routed: number of valid tiles
+  const int32_t* tile_runs;   // routed, or NULL: the list's XCD runs (kTileRunBounds tile indices)
   int tile_rows;              // routed: the height the tile lists were built with (gemm_routed_tiling)
   int tile_cols;              // routed: output columns per work item (gemm_routed_tiling's bn_up or bn_down)
   int dense_rows;
@@ -101,6 +117,7 @@ struct MxGemmArgs {
   int64_t c_sub;
   const int4* tiles;
   const int32_t* tile_count;
+  const int32_t* tile_runs;  // or NULL: the list's XCD runs (kTileRunBounds tile indices)
   int max_tiles;
 };
 hipError_t launch_gemm_mx(const MxGemmArgs& args, int epilogue, hipStream_t stream);
@@ -122,11 +139,10 @@ int gemm_tiles_bound(int64_t rows, int groups, int bm);
 
 // The routed minibatch loop as one persistent kernel (gather, up/gate +
 // SwiGLU, down for every minibatch, with device-side counters between them).
-// `up` and `down` are minibatch 0's GEMM arguments (tiles, tile_count of
-// minibatch 0; the kernel steps them by minibatch); h holds two buffers of
-// b * I bf16 (minibatch m uses buffer m mod 2).  gathered / upg / down_done
-// count finished work per minibatch, upg_tile per row tile; all must be zero
-// at launch.  Minibatches
+// `up` and `down` are minibatch 0's GEMM arguments (tiles, tile_count and
+// tile_runs of minibatch 0; the kernel steps them by minibatch); h holds n_h
+// buffers of b * I bf16.  gathered / upg / down_done count finished work per
+// minibatch, upg_tile per row tile; all must be zero at launch.  Minibatches
 // below C / b are gathered before the launch; n_mem workgroups (a multiple of
 // 8) gather the others.
 struct PipeArgs {

@@ -25,7 +25,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t err, ord_local, chunk_cnt, M, tiles, tile_count, ring, ring_s, h, h_s, Y, h_shared, shared_out, router_parts,
+  size_t err, ord_local, chunk_cnt, M, tiles, tile_count, tile_runs, ring, ring_s, h, h_s, Y, h_shared, shared_out, router_parts,
       xs_q, xs_s, hs_s, shared_tiles, shared_tile_count, total;
   int router_splits;
   int64_t n_minibatches;
@@ -132,6 +132,7 @@ Layout layout_of(const moe_shape* s) {
   L.M = take(sizeof(int32_t) * R * Lx);
   L.tiles = take(sizeof(int4) * L.n_minibatches * L.max_tiles);
   L.tile_count = take(sizeof(int32_t) * std::max<int64_t>(L.n_minibatches, 1));
+  L.tile_runs = take(sizeof(int32_t) * moe::kTileRunBounds * std::max<int64_t>(L.n_minibatches, 1));
   if (s->precision == MOE_MXFP8) {  // E4M3 bytes + one E8M0 byte per 32 along K
     L.ring = take(s->ring_rows * s->D);
     L.ring_s = take(s->ring_rows * (s->D / 32));
@@ -329,6 +330,7 @@ hipError_t routed_minibatch_mx(const moe_shape* shape, const moe_weights* w, con
   uint8_t* h_s = at<uint8_t>(ws, L.h_s);
   const int4* tiles = at<int4>(ws, L.tiles) + m * L.max_tiles;
   const int32_t* tile_count = at<int32_t>(ws, L.tile_count) + m;
+  const int32_t* tile_runs = at<int32_t>(ws, L.tile_runs) + m * moe::kTileRunBounds;
   {
     ProbeScope probe(MOE_K_GATHER, s);
     const hipError_t e =
@@ -358,6 +360,7 @@ hipError_t routed_minibatch_mx(const moe_shape* shape, const moe_weights* w, con
   u.c_sub = p_begin;
   u.tiles = tiles;
   u.tile_count = tile_count;
+  u.tile_runs = tile_runs;
   u.max_tiles = L.max_tiles;
   {
     ProbeScope probe(MOE_K_UP_GATE, s);
@@ -382,6 +385,7 @@ hipError_t routed_minibatch_mx(const moe_shape* shape, const moe_weights* w, con
   d.c_sub = 0;
   d.tiles = tiles;
   d.tile_count = tile_count;
+  d.tile_runs = tile_runs;
   d.max_tiles = L.max_tiles;
   ProbeScope probe(MOE_K_DOWN, s);
   return moe::launch_gemm_mx(d, moe::kEpiBF16, s);
@@ -544,14 +548,16 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
   float* sh_out = at<float>(ws, L.shared_out);
   int4* tiles = at<int4>(ws, L.tiles);
   int32_t* tile_count = at<int32_t>(ws, L.tile_count);
+  int32_t* tile_runs = at<int32_t>(ws, L.tile_runs);
   const int bm = L.routed_bm;
 
-  // 1. tile lists of every minibatch, from the device-side expert offsets
+  // 1. tile lists of every minibatch (and their XCD runs), from the
+  // device-side expert offsets
   {
     ProbeScope probe(MOE_K_TILES, s);
     MOE_TRY_HIP(moe::launch_build_tiles(expert_offsets, Lx, b, shape->max_rows, bm,
                                         static_cast<int>(L.n_minibatches), L.max_tiles,
-                                        tiles, tile_count, s));
+                                        tiles, tile_count, tile_runs, s));
   }
 
   // 2. shared expert on this rank's tokens (MoK paper §3.4, "Shared Expert":
@@ -619,6 +625,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     u.c_sub = m * b;
     u.tiles = tiles + m * L.max_tiles;
     u.tile_count = tile_count + m;
+    u.tile_runs = tile_runs + m * moe::kTileRunBounds;
     u.max_tiles = L.max_tiles;
     u.tile_rows = L.routed_bm;
     u.tile_cols = L.bn_up;
@@ -642,6 +649,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     d.c_sub = 0;
     d.tiles = tiles + m * L.max_tiles;
     d.tile_count = tile_count + m;
+    d.tile_runs = tile_runs + m * moe::kTileRunBounds;
     d.max_tiles = L.max_tiles;
     d.tile_rows = L.routed_bm;
     d.tile_cols = L.bn_down;
@@ -812,7 +820,7 @@ namespace {
 int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
 
 struct BwdLayout {
-  size_t tiles, tile_count, padded, k_groups, seg_off, seg_pad, seg_kg, ring, dy, act, dh, h, da, dx_ring, dyT, hT, daT,
+  size_t tiles, tile_count, tile_runs, padded, k_groups, seg_off, seg_pad, seg_kg, ring, dy, act, dh, h, da, dx_ring, dyT, hT, daT,
       xT, dg, dl, dlT, act_s, dh_s, h_s, da_s, dx_s, doutT, h_sT, da_sT, x_T, dx_r, total;
   int64_t P, Ppad, Tpad, Ep;
   moe::RoutedTiling tiling;
@@ -854,6 +862,7 @@ BwdLayout bwd_layout_of(const moe_shape* s) {
   };
   L.tiles = take(sizeof(int4) * L.max_tiles);
   L.tile_count = take(sizeof(int32_t));
+  L.tile_runs = take(sizeof(int32_t) * moe::kTileRunBounds);
   L.padded = take(sizeof(int32_t) * (Lx + 1));
   L.k_groups = take(sizeof(int2) * Lx);
   L.seg_off = take(sizeof(int32_t) * 2);
@@ -989,6 +998,7 @@ moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const
   if (T == 0) return MOE_OK;
   int4* tiles = at<int4>(ws, L.tiles);
   int32_t* tile_count = at<int32_t>(ws, L.tile_count);
+  int32_t* tile_runs = at<int32_t>(ws, L.tile_runs);
   uint16_t* ring = at<uint16_t>(ws, L.ring);
   uint16_t* dy = at<uint16_t>(ws, L.dy);
   uint16_t* act = at<uint16_t>(ws, L.act);
@@ -1000,7 +1010,8 @@ moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const
   const uint16_t* dob = static_cast<const uint16_t*>(dout);
 
   // ---- routed experts: the forward's rows again, in schedule order ----
-  MOE_TRY_HIP(moe::launch_build_tiles(expert_offsets, Lx, P, P, L.tiling.bm, 1, L.max_tiles, tiles, tile_count, s));
+  MOE_TRY_HIP(moe::launch_build_tiles(expert_offsets, Lx, P, P, L.tiling.bm, 1, L.max_tiles, tiles, tile_count,
+                                      tile_runs, s));
   MOE_TRY_HIP(moe::launch_gather_src(xb, T, D, k, route_dst, P, P, ring, dev_error, s));
   MOE_TRY_HIP(moe::launch_dy_gather(dob, topk_gate, sched_src, P, T, D, k, dy, dev_error, s));
   auto routed = [&](const void* A, int64_t lda, const void* B, int64_t b_stride, int N, int K, void* C, int64_t ldc) {
@@ -1019,6 +1030,7 @@ moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const
     a.ldc = ldc;
     a.tiles = tiles;
     a.tile_count = tile_count;
+    a.tile_runs = tile_runs;
     a.max_tiles = L.max_tiles;
     a.tile_rows = L.tiling.bm;
     a.tile_cols = 256;

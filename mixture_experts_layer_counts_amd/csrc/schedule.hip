@@ -17,6 +17,7 @@
 //           staged in LDS); writes the table row and its inverse.
 
 #include "common.h"
+#include "gemm_common.h"
 #include "kernels.h"
 
 namespace moe {
@@ -229,9 +230,32 @@ int sched_chunks(int NK) { return NK > 0 ? (NK + kSchedChunk - 1) / kSchedChunk 
 // L2 instead of re-fetching them from HBM.  Entry = {expert | (n << 10), first
 // position, rows, index of this expert's first tile}; the GEMM kernels order
 // their work by it.
+//
+// XCD runs.  The GEMM kernels cut a list's work items (N blocks of each row
+// tile) into 8 contiguous runs, one per XCD.  Equal item counts are equal work
+// only while the tiles have nearly equal heights; under skewed routing a list
+// holds the full tiles of a few large experts and many short tiles of small
+// ones, and the XCDs that get the large experts' tiles would run longest.  So
+// the runs are cut by cost: a tile of r rows is taken to cost ceil(r / 32) +
+// BM / 32 units (its 32-row MFMA blocks, plus the weight slab and the tile of
+// activation rows it streams whatever its height), and boundary j (j = 1 ..
+// 7) is the position where the running cost reaches j / 8 of the list's
+// total, placed inside its expert's tiles in proportion to cost, in
+// 1/kTileRunFrac of a tile.  (Cutting only at tile-group starts measured
+// slower on lists of a few large experts: too coarse with about a dozen tiles
+// per XCD.)  The boundaries rise with j, so the runs partition the items;
+// which XCD runs an item does not change its result.  Then each run is held
+// to at most `cap` tiles (tile_run_cap), the most its XCD's workgroups cover
+// in the up/gate launch: boundary j is clamped, in order, into [runs[j - 1],
+// runs[j - 1] + cap] and no lower than count - (8 - j) cap, so that the runs
+// after it can still hold the rest (8 cap >= count makes the range
+// non-empty).  Balanced runs stay far inside the cap: a tile costs between 1
+// and 2 times BM / 32 units, so a run of one eighth of the cost holds at most
+// about a quarter of the tiles.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int L, int64_t b,
                                                            int64_t max_rows, int BM, int max_tiles,
-                                                           int4* __restrict__ tiles, int32_t* __restrict__ tile_count) {
+                                                           int4* __restrict__ tiles, int32_t* __restrict__ tile_count,
+                                                           int32_t* __restrict__ runs) {
   const int m = blockIdx.x, l = threadIdx.x;
   // rows past max_rows were never placed (the schedule flagged the overflow)
   const int64_t P = offsets[L] < max_rows ? offsets[L] : max_rows;
@@ -259,7 +283,48 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
       out[start + i] = make_int4(l | (n << 10), static_cast<int>(p0), static_cast<int>(rows), start);
     }
   }
-  if (l == 0) tile_count[m] = total < max_tiles ? total : max_tiles;
+  const int count = total < max_tiles ? total : max_tiles;
+  if (l == 0) tile_count[m] = count;
+  if (!runs) return;  // uniform: every thread of the block returns here
+
+  // cost units of this expert's tiles: all but the last are h rows high
+  int cost = 0;
+  if (n > 0) {
+    const int64_t len = s_hi - s_lo;
+    const int64_t h = ((len + n - 1) / n + 31) / 32 * 32;
+    const int last = static_cast<int>((len - (n - 1) * h + 31) / 32);
+    cost = (n - 1) * static_cast<int>(h / 32 + BM / 32) + last + BM / 32;
+  }
+  int total_cost = 0;
+  const int before = block_exclusive_scan_1024(cost, &total_cost);
+  const int count_pos = count * kTileRunFrac;
+  __shared__ int bound[kTileRunBounds];  // boundary j, written by the expert whose cost range holds j / 8 of it
+  if (cost > 0) {
+    for (int j = 1; j < kXcds; ++j) {
+      const int target = static_cast<int>(static_cast<int64_t>(total_cost) * j / kXcds);
+      if (target < before || target >= before + cost) continue;  // another expert's
+      const int64_t into = static_cast<int64_t>(target - before) * n * kTileRunFrac;
+      const int64_t pos = static_cast<int64_t>(start) * kTileRunFrac + (into + cost / 2) / cost;
+      bound[j] = pos < count_pos ? static_cast<int>(pos) : count_pos;
+    }
+  }
+  __syncthreads();
+  if (l == 0) {
+    const int64_t cap = static_cast<int64_t>(tile_run_cap(max_tiles)) * kTileRunFrac;
+    int32_t* r = runs + static_cast<int64_t>(m) * kTileRunBounds;
+    int64_t prev = 0;
+    r[0] = 0;
+    for (int j = 1; j < kXcds; ++j) {
+      int64_t v = total_cost > 0 ? bound[j] : 0;  // no tiles: every run is empty
+      const int64_t lo = count_pos - (kXcds - j) * cap;
+      v = v < lo ? lo : v;
+      v = v < prev ? prev : v;
+      v = v > prev + cap ? prev + cap : v;
+      r[j] = static_cast<int32_t>(v);  // <= count_pos
+      prev = v;
+    }
+    r[kXcds] = count_pos;
+  }
 }
 
 // Dense tile list: one segment [0, rows) of expert 0, split as the routed
@@ -286,9 +351,13 @@ hipError_t launch_dense_tiles(int64_t rows, int BM, int4* tiles, int32_t* tile_c
 }
 
 hipError_t launch_build_tiles(const int32_t* offsets, int L, int64_t b, int64_t max_rows, int BM, int n_minibatches,
-                              int max_tiles, int4* tiles, int32_t* tile_count, hipStream_t stream) {
+                              int max_tiles, int4* tiles, int32_t* tile_count, int32_t* runs, hipStream_t stream) {
+  static_assert(kTileRunBounds == kXcds + 1, "one run per XCD");
   if (n_minibatches <= 0) return hipSuccess;
-  build_tiles_kernel<<<n_minibatches, 1024, 0, stream>>>(offsets, L, b, max_rows, BM, max_tiles, tiles, tile_count);
+  // run positions (kTileRunFrac per tile) are int32
+  if (runs && static_cast<int64_t>(max_tiles) * kTileRunFrac >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  build_tiles_kernel<<<n_minibatches, 1024, 0, stream>>>(offsets, L, b, max_rows, BM, max_tiles, tiles, tile_count,
+                                                         runs);
   return hipGetLastError();
 }
 
