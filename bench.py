@@ -97,10 +97,11 @@ def src_digest(*names):
     return h.hexdigest()[:16]
 
 
-# sources an expert GEMM kernel is compiled from: stored counter readings
-# apply only while none of them has changed
-GEMM_SOURCES = {False: ("gemm.hip", "gemm_common.h", "common.h", "kernels.h"),
-                True: ("gemm_mx.hip", "gemm_common.h", "common.h", "kernels.h", "mx.h")}
+# sources an expert GEMM kernel is compiled from, and the tile-list builder
+# that sets its work order: stored counter readings apply only while none of
+# them has changed
+GEMM_SOURCES = {False: ("gemm.hip", "gemm_common.h", "common.h", "kernels.h", "schedule.hip"),
+                True: ("gemm_mx.hip", "gemm_common.h", "common.h", "kernels.h", "mx.h", "schedule.hip")}
 
 
 def gemm_digest(mx):
@@ -190,7 +191,7 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
     layer, step = make(b, C)
     return Job(name=w.name, w=w, R=1, c=0, T=w.T, E_route=w.E, P=P, b=b, C=C, precision=precision, layer=layer,
                inp=inp, step=step, make=make, routed_from_x=logits_in is None, weight_quantize=wq,
-               shared_precision=args.shared_precision,
+               shared_precision=args.shared_precision, routing=args.routing,
                config={"workload": f"{w.name}: T={w.T} D={w.D} I={w.I} E={w.E} top-{w.k} + 1 shared "
                                    f"(I={w.I_shared})", "minibatch_rows": b, "ring_rows": C,
                        "shared_precision": args.shared_precision,
@@ -249,7 +250,7 @@ def setup_ep64(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
 
     layer, step = make(b, C)
     return Job(name="ep64", w=w, R=R, T=N, E_route=E_total, P=P, b=b, C=C, precision=precision, layer=layer,
-               inp=inp, step=step, make=make, routed_from_x=True, A=A, c=c, L=L, wr=wr, router=router,
+               inp=inp, step=step, make=make, routed_from_x=True, A=A, c=c, L=L, wr=wr, router=router, routing="x",
                config={"workload": f"ep64: one rank of 64 (4 local experts D={w.D} I={w.I}, {P} routed rows, "
                                    f"Zipf(1.2) counts {counts}; shared expert on {N} tokens)",
                        "minibatch_rows": b, "ring_rows": C, "routing": "router projection from x (local tokens); "
@@ -396,12 +397,15 @@ def main():
         achieved, peak, unit = alg_bytes / t_dom / 1e9, PEAK_HBM / 1e9, "GB/s"
     else:
         achieved, peak, unit = alg_flops / t_dom / 1e12, peak_mma / 1e12, "TFLOP/s"
+    # counters taken on the same workload, routing, minibatch, precision and
+    # GEMM sources
     traffic = None
-    tr_path = os.path.join(ROOT, "profiles", f"traffic_{dominant}_{job.name}.json")
+    suffix = "" if job.routing == "x" else "_" + job.routing
+    tr_path = os.path.join(ROOT, "profiles", f"traffic_{dominant}_{job.name}{suffix}.json")
     if os.path.exists(tr_path):
         tr = json.load(open(tr_path))
         if tr.get("src_digest") == gemm_digest(mx) and tr.get("minibatch_rows") == job.b and \
-                tr.get("precision", "bf16") == job.precision:
+                tr.get("precision", "bf16") == job.precision and tr.get("routing", "x") == job.routing:
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic,
