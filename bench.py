@@ -83,6 +83,10 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="in the sweep, also time the step captured once in a HIP graph and replayed "
                          "(launch overhead removed)")
+    ap.add_argument("--floor", action="store_true",
+                    help="instead of the layer, measure the expert GEMMs' load floor: stream probes of the routed "
+                         "up/gate K loop without arithmetic (moe_stream_probe), and hipBLASLt (torch.bmm) on the "
+                         "uniform stand-in of the expert GEMMs; prints one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy a MIB-MiB buffer 3 times with a plain device copy (a known-size "
                          "reference for hardware byte counters)")
@@ -291,6 +295,116 @@ def kernel_model(job, offsets, sched_src):
     return m
 
 
+def time_launches(torch, fn, reps=5, warm=2):
+    """Mean ms of fn() over reps launches on the current stream (HIP events), after warm untimed ones."""
+    for _ in range(warm):
+        fn()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / reps
+
+
+def run_floor(torch, _lib):
+    """The load floor of the routed expert GEMMs, and a library reference point.
+
+    Stream probes (moe_stream_probe): the routed up/gate's K-loop loads, with
+    the GEMM's LDS rings and slot protocol and no arithmetic, at the bf16
+    DeepSeek-V3 work (4,096 items of 320 activation and 256 weight rows,
+    K = 7,168 bf16) and the MXFP8 layer's (6,144 items of 256 + 256 rows,
+    K = 7,168 bytes); each stream alone and both together; then the weight
+    stream alone at 1 to 4 stages in flight.  16 consecutive items share their
+    activation rows, as the 16 N blocks of one row tile do.  Reference:
+    hipBLASLt (torch.bmm) on the uniform stand-in of the expert GEMMs, 256
+    experts of 256 rows each, the weights a contiguous right operand.  Also
+    torch's own kernels on the access patterns of the gather and the combine
+    (pure reads, pure writes, copy, k rows in and 1 out, 1 in and k out), for
+    the rates such mixed streams reach on the device.
+    """
+    lib = _lib.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {"mode": "floor", "device": torch.cuda.get_device_name(0), "probes": [], "hipblaslt": []}
+
+    def probe(name, items, row_bytes, a_rows, b_rows, slots_a, slots_b, share=16):
+        blocks = (items + share - 1) // share
+        act = torch.empty(max(blocks * a_rows * row_bytes, 1), dtype=torch.uint8, device="cuda")
+        wts = torch.empty(max(items * b_rows * row_bytes, 1), dtype=torch.uint8, device="cuda")
+        a = _lib.MoeStreamProbeArgs(act.data_ptr(), wts.data_ptr(), row_bytes, items, share, a_rows, b_rows,
+                                    slots_a, slots_b)
+
+        def launch():
+            _lib.check("moe_stream_probe", lib.moe_stream_probe(ctypes.byref(a), ctypes.c_void_p(stream)))
+
+        ms = time_launches(torch, launch)
+        w_bytes, a_bytes = items * b_rows * row_bytes, blocks * a_rows * row_bytes
+        lds_bytes = items * (a_rows + b_rows) * row_bytes
+        rec = {"probe": name, "items": items, "row_bytes": row_bytes, "a_rows": a_rows, "b_rows": b_rows,
+               "slots": [slots_a, slots_b], "ms": round(ms, 4),
+               "weight_GB": round(w_bytes / 1e9, 3), "act_unique_GB": round(a_bytes / 1e9, 3),
+               "lds_fill_GB": round(lds_bytes / 1e9, 3),
+               "weight_TB_per_s": round(w_bytes / ms / 1e9, 3) if w_bytes else None,
+               "lds_fill_TB_per_s": round(lds_bytes / ms / 1e9, 3)}
+        log("floor", json.dumps(rec))
+        out["probes"].append(rec)
+        del act, wts
+        torch.cuda.empty_cache()
+
+    # bf16 up/gate at the DeepSeek-V3 shape: 256 experts x 16 N blocks, 320-row tiles
+    for a_rows, b_rows, tag in ((320, 256, "bf16 up/gate: both streams"), (320, 0, "bf16 up/gate: activation rows"),
+                                (0, 256, "bf16 up/gate: weight rows")):
+        probe(tag, 4096, 7168 * 2, a_rows, b_rows, 2, 2)
+    # MXFP8 up/gate: 384 experts x 16 N blocks, 256-row tiles, weight ring one slot deeper
+    for a_rows, b_rows, tag in ((256, 256, "mxfp8 up/gate: both streams"), (256, 0, "mxfp8 up/gate: activation rows"),
+                                (0, 256, "mxfp8 up/gate: weight rows")):
+        probe(tag, 6144, 7168, a_rows, b_rows, 2, 3)
+    for n in (2, 3, 4, 5):
+        probe(f"weight rows, {n - 1} stage(s) of 32 KB in flight per workgroup", 6144, 7168, 0, 256, n, n)
+
+    # hipBLASLt on the uniform stand-in (fresh N(0,1) bf16 operands)
+    for name, K, N in (("up/gate (gate and up as one 2I-wide operand)", 7168, 4096), ("down", 2048, 7168)):
+        a = torch.randn(256, 256, K, device="cuda", dtype=torch.bfloat16)
+        w = torch.randn(256, K, N, device="cuda", dtype=torch.bfloat16)
+        c = torch.empty(256, 256, N, device="cuda", dtype=torch.bfloat16)
+        ms = time_launches(torch, lambda: torch.bmm(a, w, out=c))
+        flops = 2.0 * 256 * 256 * K * N
+        rec = {"gemm": name, "experts": 256, "rows": 256, "K": K, "N": N, "ms": round(ms, 4),
+               "TFLOP_per_s": round(flops / ms / 1e9, 1), "weight_TB_per_s": round(256 * K * N * 2 / ms / 1e9, 3)}
+        log("floor", json.dumps(rec))
+        out["hipblaslt"].append(rec)
+        del a, w, c
+        torch.cuda.empty_cache()
+    # library kernels with the access patterns of the gather and the combine,
+    # at the DeepSeek-V3 shape (T = 8192 tokens, k = 8, D = 7168, bf16)
+    out["streams"] = []
+    T, k, D = 8192, 8, 7168
+    x = torch.randn(T * k, D, device="cuda", dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    xs = x[:T]
+    z = torch.empty(T, D, device="cuda", dtype=torch.bfloat16)
+    r32 = torch.empty((), device="cuda", dtype=torch.float32)
+    row = T * D * 2
+    for name, fn, nbytes in (
+            ("pure reads (torch.sum over T*k rows)",
+             lambda: torch.sum(x, dim=(0, 1), dtype=torch.float32, out=r32), k * row),
+            ("pure writes (fill_ of T*k rows)", lambda: y.fill_(1.0), k * row),
+            ("copy (T*k rows)", lambda: y.copy_(x), 2 * k * row),
+            ("k rows in, 1 out (sum over k, the combine's pattern)",
+             lambda: torch.sum(x.view(T, k, D), dim=1, out=z), (k + 1) * row),
+            ("1 row in, k out (broadcast copy, the gather's pattern)",
+             lambda: y.view(T, k, D).copy_(xs.unsqueeze(1).expand(T, k, D)), (k + 1) * row)):
+        ms = time_launches(torch, fn)
+        rec = {"pattern": name, "ms": round(ms, 4), "GB": round(nbytes / 1e9, 3),
+               "TB_per_s": round(nbytes / ms / 1e9, 3)}
+        log("floor", json.dumps(rec))
+        out["streams"].append(rec)
+    del x, y, z
+    torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -301,6 +415,11 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.floor:
+        from mixture_experts_layer_counts_amd import _lib
+        run_floor(torch, _lib)
+        return
 
     import synth
     from mixture_experts_layer_counts_amd import MoELayer, _lib, quantize_mxfp8, shape_for

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef enum {
   MOE_OK = 0,
@@ -387,6 +387,37 @@ typedef enum {
 
 moe_status moe_probe_begin(int32_t kernel_id, int32_t max_launches);
 moe_status moe_probe_end(double* total_ms, int32_t* launches);
+
+/*
+ * Measurement, not part of the layer: the operand stream of the routed
+ * expert GEMMs' K loop with the arithmetic taken out, to locate the floor of
+ * their load pipeline on the device.  `items` workgroups (8 waves each, cut
+ * into 8 contiguous per-XCD runs as the GEMMs cut their work items) each walk
+ * row_bytes / 128 stages; at each stage a workgroup moves 128 bytes of each
+ * of a_rows activation-like rows and b_rows weight-like rows into LDS rings of
+ * slots_a and slots_b stages with direct buffer->LDS loads, one barrier per
+ * stage, refilling a slot right after the barrier that frees it (the GEMMs'
+ * protocol).  Item i reads activation block i / a_share of `act` and weight
+ * block i of `wts`:
+ *   act  [ceil(items / a_share)][a_rows][row_bytes]  device, caller-owned
+ *   wts  [items][b_rows][row_bytes]                  device, caller-owned
+ * Nothing is written to device memory.  Supported (a_rows, b_rows, slots_a,
+ * slots_b): (320, 256, 2, 2) and (320, 0, 2, 2), the bf16 up/gate stage;
+ * (256, 256, 2, 3) and (256, 0, 2, 3), the MXFP8 up/gate stage; (0, 256, n, n)
+ * for n = 2 .. 5 and (0, 256, 2, 3).  Other combinations: MOE_ERR_UNSUPPORTED;
+ * row_bytes not a positive multiple of 128, items or a_share < 1, or a NULL
+ * buffer that a nonzero row count needs: MOE_ERR_INVALID_ARG.  One launch on
+ * `stream`; no synchronisation.
+ */
+typedef struct {
+  const void* act;
+  const void* wts;
+  int64_t row_bytes;
+  int32_t items, a_share;
+  int32_t a_rows, b_rows;
+  int32_t slots_a, slots_b;
+} moe_stream_probe_args;
+moe_status moe_stream_probe(const moe_stream_probe_args* args, void* stream);
 
 /* Static string for a status code. */
 const char* moe_status_str(moe_status status);

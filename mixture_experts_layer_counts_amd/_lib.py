@@ -48,6 +48,12 @@ class MoeGrads(ctypes.Structure):
                                               "dw_router")]
 
 
+class MoeStreamProbeArgs(ctypes.Structure):
+    _fields_ = [("act", ctypes.c_void_p), ("wts", ctypes.c_void_p), ("row_bytes", ctypes.c_int64),
+                ("items", ctypes.c_int32), ("a_share", ctypes.c_int32), ("a_rows", ctypes.c_int32),
+                ("b_rows", ctypes.c_int32), ("slots_a", ctypes.c_int32), ("slots_b", ctypes.c_int32)]
+
+
 class MoeError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
@@ -78,6 +84,7 @@ _SIGS = {
                                     _P, _P, ctypes.POINTER(MoeGrads), _P, _P, ctypes.c_size_t, _P]),
     "moe_probe_begin": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32]),
     "moe_probe_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
+    "moe_stream_probe": (ctypes.c_int, [ctypes.POINTER(MoeStreamProbeArgs), _P]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_abi_version": (ctypes.c_int32, []),
 }

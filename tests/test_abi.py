@@ -255,3 +255,25 @@ def test_backward_validates_before_any_launch(lib):
     assert call(weights=_lib.MoeBwdWeights()) == -1               # weights not prepared
     w = _lib.MoeWeights()
     assert lib.moe_backward_prepare(ctypes.byref(s), ctypes.byref(w), fake, ctypes.byref(bw), None) == -1
+
+
+def test_stream_probe_validates_before_any_launch(lib):
+    # the measurement probe answers unsupported or invalid arguments on the host
+    def call(**kw):
+        f = dict(act=4096, wts=4096, row_bytes=7168, items=64, a_share=16, a_rows=256, b_rows=256, slots_a=2,
+                 slots_b=3)
+        f.update(kw)
+        a = _lib.MoeStreamProbeArgs(f["act"], f["wts"], f["row_bytes"], f["items"], f["a_share"], f["a_rows"],
+                                    f["b_rows"], f["slots_a"], f["slots_b"])
+        return lib.moe_stream_probe(ctypes.byref(a), None)
+
+    assert lib.moe_stream_probe(None, None) == -1
+    assert call(row_bytes=7000) == -1          # not a multiple of 128
+    assert call(items=0) == -1
+    assert call(a_share=0) == -1
+    assert call(act=None) == -1                # activation rows asked, no buffer
+    assert call(wts=None) == -1
+    assert call(slots_b=2) == -2               # the MXFP8 stage runs 2 + 3 slots
+    assert call(a_rows=128) == -2
+    assert call(a_rows=0, b_rows=256, slots_a=6, slots_b=6) == -2
+    assert call(row_bytes=128 << 20) == -2     # one item's rows past 2^31 bytes
