@@ -316,7 +316,9 @@ def run_floor(torch, _lib):
     DeepSeek-V3 work (4,096 items of 320 activation and 256 weight rows,
     K = 7,168 bf16) and the MXFP8 layer's (6,144 items of 256 + 256 rows,
     K = 7,168 bytes); each stream alone and both together; then the weight
-    stream alone at 1 to 4 stages in flight.  16 consecutive items share their
+    stream alone at 1 to 4 stages in flight; then the down projections'
+    stages (K = I = 2,048; 28 N blocks share a row tile), both streams and
+    weight rows alone.  16 consecutive items share their
     activation rows, as the 16 N blocks of one row tile do.  Reference:
     hipBLASLt (torch.bmm) on the uniform stand-in of the expert GEMMs, 256
     experts of 256 rows each, the weights a contiguous right operand.  Also
@@ -362,6 +364,11 @@ def run_floor(torch, _lib):
         probe(tag, 6144, 7168, a_rows, b_rows, 2, 3)
     for n in (2, 3, 4, 5):
         probe(f"weight rows, {n - 1} stage(s) of 32 KB in flight per workgroup", 6144, 7168, 0, 256, n, n)
+    # down projections: h rows against W_down, K = I = 2048, 28 N blocks of 256 share a row tile
+    probe("bf16 down: both streams", 256 * 28, 2048 * 2, 320, 256, 2, 2, share=28)
+    probe("bf16 down: weight rows", 256 * 28, 2048 * 2, 0, 256, 2, 2, share=28)
+    probe("mxfp8 down: both streams", 384 * 28, 2048, 256, 256, 2, 3, share=28)
+    probe("mxfp8 down: weight rows", 384 * 28, 2048, 0, 256, 2, 3, share=28)
 
     # hipBLASLt on the uniform stand-in (fresh N(0,1) bf16 operands)
     for name, K, N in (("up/gate (gate and up as one 2I-wide operand)", 7168, 4096), ("down", 2048, 7168)):
