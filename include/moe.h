@@ -59,7 +59,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* null pointer, inconsistent sizes, bad tunable */
-  MOE_ERR_UNSUPPORTED = -2, /* valid request this build does not implement */
+  MOE_ERR_UNSUPPORTED = -2, /* valid request the library does not implement */
   MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_workspace_bytes() */
   MOE_ERR_HIP = -4          /* a HIP launch or runtime call failed */
 } moe_status;

@@ -7,14 +7,16 @@ mode (minibatches of 2,048 rows cycling a 4,096-row ring).
 * the full path from x, over all tokens:
   - router logits within the fp32 summation bound of the fp64 logits;
   - the selection equal to the oracle's top-k of the GPU's own fp32 logits
-    (the spec condition: identical fp32 logits give identical
-    indices), and the gates within the fp32 gate bound of the oracle's;
+    (identical fp32 logits must give identical indices), and the gates
+    within the fp32 gate bound of the oracle's;
   - the schedule tables equal to the oracle's for that selection;
   - bf16 output = RNE(out32);
 * the layer output against the oracle, fed the same fp32 logits, on a sample
   of over 512 tokens that together route to every one of the 256 experts and
   include the first and last row of every expert's region;
 * ring mode: bitwise equal to the single-minibatch run;
+* the persistent routed kernel at b = 512, 2,048 and 8,192 (rings of four
+  minibatches): bitwise equal to the single-minibatch run;
 * the backward (moe_backward after the forward from x, seeded N(0,1) bf16
   output gradient) against the backward oracle's sampled pieces: dx of 16
   seeded tokens, every weight gradient of four experts (the first, the last,
@@ -152,6 +154,25 @@ def test_dsv3_ring_mode_bitwise_equal(dsv3, dsv3_run, b, C):
     torch.cuda.synchronize()
     assert m.device_error() == 0
     assert np.array_equal(r["idx"].cpu().numpy(), dsv3_run["idx"])
+    assert np.array_equal(r["out32"].cpu().numpy().view(np.int32), dsv3_run["out32"].view(np.int32))
+    assert np.array_equal(r["out"].cpu().view(torch.int16).numpy(), dsv3_run["out"])
+    del m, r
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("b,C", [(512, 2048), (2048, 8192), (8192, 32768)])
+def test_dsv3_persistent_kernel_bitwise_equal(dsv3, dsv3_run, b, C):
+    # the persistent routed kernel at the minibatch sizes the benchmark's
+    # granularity sweep times (a ring of four minibatches, 16 gathering
+    # workgroups) gives the bits of the single-minibatch stream-ordered run
+    from mixture_experts_layer_counts_amd import MoELayer, shape_for
+    w, inp, dev = dsv3
+    m = MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
+                           pipeline=True, mem_workgroups=16), device=dev)
+    say("dsv3 persistent kernel from x, b =", b, "C =", C)
+    r = m(inp["x"], inp["w_router"], inp)
+    torch.cuda.synchronize()
+    assert m.device_error() == 0
     assert np.array_equal(r["out32"].cpu().numpy().view(np.int32), dsv3_run["out32"].view(np.int32))
     assert np.array_equal(r["out"].cpu().view(torch.int16).numpy(), dsv3_run["out"])
     del m, r
