@@ -1,5 +1,6 @@
-"""The whole layer (moe_route from x + moe_schedule + moe_forward), and the
-backward (moe_backward), each captured in a HIP graph and replayed.
+"""The whole layer (moe_route from x + moe_schedule + moe_forward), also with
+the persistent routed kernel, and the backward (moe_backward), each captured
+in a HIP graph and replayed.
 
 The library allocates nothing, reads no device data on the host and clears
 its scratch words with kernels, so a caller may capture a step and replay it.
@@ -19,18 +20,31 @@ CASES = [
     # one minibatch (source-side gather; the down projection's resident
     # workgroups walk several items each), and several minibatches through a
     # ring smaller than the routed rows
-    ("ragged-one", synth.Workload("ragged", T=300, D=256, I=192, E=16, k=4, I_shared=128, seed=7), None, None),
-    ("ragged-ring", synth.Workload("ragged", T=300, D=256, I=192, E=16, k=4, I_shared=128, seed=7), 256, 512),
-    ("mid-one", synth.workload("mid", T=1024), None, None),
+    ("ragged-one", synth.Workload("ragged", T=300, D=256, I=192, E=16, k=4, I_shared=128, seed=7), None, None, False),
+    ("ragged-ring", synth.Workload("ragged", T=300, D=256, I=192, E=16, k=4, I_shared=128, seed=7), 256, 512,
+     False),
+    ("mid-one", synth.workload("mid", T=1024), None, None, False),
+    # the persistent routed kernel: its counters and queues are cleared by a
+    # fill kernel in the captured sequence, and its memory workgroups gather
+    # the minibatches past the ring
+    ("mid-persistent", synth.workload("mid", T=1024), 512, 2048, True),
 ]
 
 
-@pytest.mark.parametrize("name,w,b,C", CASES, ids=[c[0] for c in CASES])
-def test_layer_graph_replay_bitwise(name, w, b, C):
+def make_layer(w, dev, b, C, pipeline):
+    if not pipeline:
+        return layer(w, dev, b, C)
+    from mixture_experts_layer_counts_amd import MoELayer, shape_for
+    return MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
+                              pipeline=True, mem_workgroups=16), device=dev)
+
+
+@pytest.mark.parametrize("name,w,b,C,pipeline", CASES, ids=[c[0] for c in CASES])
+def test_layer_graph_replay_bitwise(name, w, b, C, pipeline):
     dev = need_gpu()
-    say("graph_replay", name, w, b, C)
+    say("graph_replay", name, w, b, C, "persistent" if pipeline else "")
     inp_dev = to_dev(synth.make_inputs(w), dev)
-    m = layer(w, dev, b, C)
+    m = make_layer(w, dev, b, C, pipeline)
     keys = ("logits", "idx", "gate", "offsets", "sched", "route_dst", "out", "out32")
 
     eager = m(inp_dev["x"], inp_dev["w_router"], inp_dev)
@@ -38,7 +52,7 @@ def test_layer_graph_replay_bitwise(name, w, b, C):
     want = {k: eager[k].clone() for k in keys}
 
     # a second layer object supplies eager work between the replays
-    other = layer(w, dev, b, C)
+    other = make_layer(w, dev, b, C, pipeline)
     noise = torch.randn_like(inp_dev["x"], dtype=torch.float32).to(torch.bfloat16)
 
     g = torch.cuda.CUDAGraph()
