@@ -44,6 +44,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "gemm_common.h"
@@ -175,12 +176,12 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
   constexpr int NRD = FML + NB * FN;  // fragment reads per 16-wide sub-step
   // one fragment read under each MFMA; in the sub-step after the barrier
   // also the stage's loads (A, then B), one under each MFMA
-  auto interleave = [&](int ks) __attribute__((always_inline)) {
+  auto interleave = [&](int ks, bool loads) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NMF; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (ks == KS && i < AI + BI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (loads && ks == KS && i < AI + BI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   };
 
@@ -208,13 +209,14 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
   frag_a_t af[2];
   frag_b_t bf[2];
   if constexpr (FML > 0) read_frags(0, 0, af[0], bf[0]);
-  for (int kt = 0; kt < nk; ++kt) {
+  auto step = [&](int kt, auto loads) __attribute__((always_inline)) {
+    constexpr bool kLoads = decltype(loads)::value;
     if constexpr (FML > 0) {
 #pragma unroll
       for (int ks = 0; ks + 1 < KS; ++ks) {
         read_frags(kt, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
         mfmas(af[ks & 1], bf[ks & 1]);
-        interleave(ks);
+        interleave(ks, kLoads);
       }
     }
     // A(kt+1) and B(kt+1) have landed and this wave's reads of stage kt are
@@ -222,14 +224,29 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
     asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_STAGE, 0)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue_a(kt + NSA);
-    issue_b(kt + NSB);
+    if constexpr (kLoads) {
+      issue_a(kt + NSA);
+      issue_b(kt + NSB);
+    }
     if constexpr (FML > 0) {
-      // past the last stage this reads the repeated stage, and is not used
+      // past the last stage this reads a slot whose data is not used
       read_frags(kt + 1, 0, af[KS & 1], bf[KS & 1]);
       mfmas(af[(KS - 1) & 1], bf[(KS - 1) & 1]);
-      interleave(KS);
+      interleave(KS, kLoads);
     }
+  };
+  // With both rings two slots deep, every wait in the loop drains the load
+  // counter (VM_STAGE == 0), so the last NSA steps need not refetch the last
+  // stage to keep the counts uniform: they issue nothing (2 of the 34 stage
+  // loads of a routed down item).  Deeper rings count their waits, and keep
+  // the refetches.
+  constexpr bool kDropTail = VM_STAGE == 0 && NSB == NSA;
+  int kt = 0;
+  if constexpr (kDropTail) {
+    for (; kt < nk - NSA; ++kt) step(kt, std::true_type{});
+    for (; kt < nk; ++kt) step(kt, std::false_type{});
+  } else {
+    for (; kt < nk; ++kt) step(kt, std::true_type{});
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still target LDS when the workgroup ends
 }
