@@ -127,8 +127,9 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
   const int frag_row = lane & 31, frag_c = lane >> 5;
 
-  // past the last stage the loads repeat it (into a free slot), so that every
-  // step issues the same number of loads
+  // a stage past the last (in the prologue of a K range shorter than the
+  // rings) loads the last stage again, into a free slot, so that the
+  // prologue issues the same number of loads
   auto issue_a = [&](int kt) __attribute__((always_inline)) {
     const int ko = (kt < nk ? kt : nk - 1) * RB;
     char* sa = sa0 + (kt % NSA) * ASLOT;
@@ -220,13 +221,19 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
       }
     }
     // A(kt+1) and B(kt+1) have landed and this wave's reads of stage kt are
-    // done, before any wave refills a slot
-    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_STAGE, 0)) : "memory");
+    // done, before any wave refills a slot (in the tail, where fewer loads
+    // are in flight than VM_STAGE counts on, by draining the counter)
+    if constexpr (kLoads)
+      asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(VM_STAGE, 0)) : "memory");
+    else
+      asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(0, 0)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if constexpr (kLoads) {
       issue_a(kt + NSA);
       issue_b(kt + NSB);
+    } else if constexpr (NSB > NSA) {
+      if (kt + NSA < nk) issue_a(kt + NSA);  // a stage still to come (uniform branch)
     }
     if constexpr (FML > 0) {
       // past the last stage this reads a slot whose data is not used
@@ -235,19 +242,16 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
       interleave(KS, kLoads);
     }
   };
-  // With both rings two slots deep, every wait in the loop drains the load
-  // counter (VM_STAGE == 0), so the last NSA steps need not refetch the last
-  // stage to keep the counts uniform: they issue nothing (2 of the 34 stage
-  // loads of a routed down item).  Deeper rings count their waits, and keep
-  // the refetches.
-  constexpr bool kDropTail = VM_STAGE == 0 && NSB == NSA;
+  // The last NSB steps issue no refetch of the last stage (the loads past it
+  // only kept the count of loads per step uniform for the counted waits):
+  // they load only the activation stages still to come, and wait by
+  // draining the counter.  With both rings two slots deep every wait drains
+  // it anyway.  The routed down item (K = 2048, 32 stages) thereby loses 2
+  // of its 34 stage loads; a weight-gradient item (K = an expert's rows,
+  // about 4 stages) 5 of its 13.
   int kt = 0;
-  if constexpr (kDropTail) {
-    for (; kt < nk - NSA; ++kt) step(kt, std::true_type{});
-    for (; kt < nk; ++kt) step(kt, std::false_type{});
-  } else {
-    for (; kt < nk; ++kt) step(kt, std::true_type{});
-  }
+  for (; kt < nk - NSB; ++kt) step(kt, std::true_type{});
+  for (; kt < nk; ++kt) step(kt, std::false_type{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still target LDS when the workgroup ends
 }
 

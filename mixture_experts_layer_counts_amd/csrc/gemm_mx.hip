@@ -36,6 +36,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 #include "gemm_common.h"
@@ -101,8 +102,9 @@ __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const ui
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
   const int frag_row = lane & 31, frag_h = lane >> 5;
 
-  // past the last stage the loads repeat it (into a free slot), so that every
-  // step issues the same number of loads
+  // a stage past the last (in the prologue of a K range shorter than the
+  // rings) loads the last stage again, into a free slot, so that the
+  // prologue issues the same number of loads
   auto issue_a = [&](int kt, MxScales<FML, NB, FN>& sc) __attribute__((always_inline)) {
     const int kc = kt < nk ? kt : nk - 1;
     char* sa = sa0 + (kt % kNSA) * ASLOT;
@@ -211,27 +213,66 @@ __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const ui
   asm volatile("" ::: "memory");
   Frags f[2];
   if constexpr (FML > 0) read_frags(0, 0, f[0]);
-  for (int kt = 0; kt < nk; ++kt) {
-    issue_a(kt + 1, sc_next);
+  // One step per stage.  In the down projection (one B operand) the last two
+  // steps do not refetch the last stage (those loads only kept the per-step
+  // load count uniform for the counted wait): step nk-2 issues A(nk-1) but
+  // no B, step nk-1 nothing, and both wait by draining the counter.  An item
+  // (K = 2048, 16 stages) thereby loses 3 of its 35 stage loads: 7% off the
+  // step's time.  The up/gate (56 stages) keeps the uniform steps: the extra
+  // code of the tail cost it 3-5%, more than its 3 refetches of 59.
+  auto step = [&](int kt, auto load_a, auto load_b) __attribute__((always_inline)) {
+    constexpr bool kA = decltype(load_a)::value, kB = decltype(load_b)::value;
+    if constexpr (kA) issue_a(kt + 1, sc_next);
     if constexpr (FML > 0) {
       read_frags(kt, 1, f[1]);
       mfmas(f[0], sc_cur, 0);
-      interleave(0, true);
+      interleave(0, kA);
     }
-    issue_b(kt + 2);
+    if constexpr (kB) issue_b(kt + 2);
     // A(kt+1), its scales and B(kt+1) have landed (B(kt+2) may still be in
     // flight) and this wave's reads of stage kt are done
-    asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI, 0)) : "memory");
+    if constexpr (kB)
+      asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI, 0)) : "memory");
+    else
+      asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(0, 0)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if constexpr (FML > 0) {
-      // stage kt+1's first fragments (past the last stage: the repeated
-      // stage, never used)
+      // stage kt+1's first fragments (past the last stage: a slot whose
+      // data is never used)
       read_frags(kt + 1, 0, f[0]);
       mfmas(f[1], sc_cur, 1);
       interleave(1, false);
     }
-    sc_cur = sc_next;
+    if constexpr (kA) sc_cur = sc_next;
+  };
+  if constexpr (NB == 1) {
+    int kt = 0;
+    for (; kt < nk - 2; ++kt) step(kt, std::true_type{}, std::true_type{});
+    if (kt == nk - 2) step(kt++, std::true_type{}, std::false_type{});
+    step(kt, std::false_type{}, std::false_type{});  // kt == nk - 1
+  } else {
+    // the same steps, written out: the compiler places its own waits on the
+    // scale words differently when this loop goes through the step above,
+    // and that measured 4-5% slower
+    for (int kt = 0; kt < nk; ++kt) {
+      issue_a(kt + 1, sc_next);
+      if constexpr (FML > 0) {
+        read_frags(kt, 1, f[1]);
+        mfmas(f[0], sc_cur, 0);
+        interleave(0, true);
+      }
+      issue_b(kt + 2);
+      asm volatile("s_waitcnt %0" ::"n"(waitcnt_imm(BI, 0)) : "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if constexpr (FML > 0) {
+        read_frags(kt + 1, 0, f[0]);
+        mfmas(f[1], sc_cur, 1);
+        interleave(1, false);
+      }
+      sc_cur = sc_next;
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may still target LDS when the workgroup ends
 }
