@@ -362,6 +362,7 @@ def run_floor(torch, _lib):
     for a_rows, b_rows, tag in ((256, 256, "mxfp8 up/gate: both streams"), (256, 0, "mxfp8 up/gate: activation rows"),
                                 (0, 256, "mxfp8 up/gate: weight rows")):
         probe(tag, 6144, 7168, a_rows, b_rows, 2, 3)
+    probe("mxfp8 up/gate: both streams, two weight slots", 6144, 7168, 256, 256, 2, 2)
     for n in (2, 3, 4, 5):
         probe(f"weight rows, {n - 1} stage(s) of 32 KB in flight per workgroup", 6144, 7168, 0, 256, n, n)
     # down projections: h rows against W_down, K = I = 2048, 28 N blocks of 256 share a row tile
@@ -369,6 +370,7 @@ def run_floor(torch, _lib):
     probe("bf16 down: weight rows", 256 * 28, 2048 * 2, 0, 256, 2, 2, share=28)
     probe("mxfp8 down: both streams", 384 * 28, 2048, 256, 256, 2, 3, share=28)
     probe("mxfp8 down: weight rows", 384 * 28, 2048, 0, 256, 2, 3, share=28)
+    probe("mxfp8 down: both streams, two weight slots", 384 * 28, 2048, 256, 256, 2, 2, share=28)
 
     # hipBLASLt on the uniform stand-in (fresh N(0,1) bf16 operands)
     for name, K, N in (("up/gate (gate and up as one 2I-wide operand)", 7168, 4096), ("down", 2048, 7168)):

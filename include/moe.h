@@ -403,7 +403,8 @@ moe_status moe_probe_end(double* total_ms, int32_t* launches);
  *   wts  [items][b_rows][row_bytes]                  device, caller-owned
  * Nothing is written to device memory.  Supported (a_rows, b_rows, slots_a,
  * slots_b): (320, 256, 2, 2) and (320, 0, 2, 2), the bf16 up/gate stage;
- * (256, 256, 2, 3) and (256, 0, 2, 3), the MXFP8 up/gate stage; (0, 256, n, n)
+ * (256, 256, 2, 3) and (256, 0, 2, 3), the MXFP8 up/gate stage, and (256, 256,
+ * 2, 2), the same with two weight slots; (0, 256, n, n)
  * for n = 2 .. 5 and (0, 256, 2, 3).  Other combinations: MOE_ERR_UNSUPPORTED;
  * row_bytes not a positive multiple of 128, items or a_share < 1, or a NULL
  * buffer that a nonzero row count needs: MOE_ERR_INVALID_ARG.  One launch on

@@ -453,11 +453,14 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
       const char* src_l = smem + row_b * CS + ch * 16;
       char* dst = cbase + (crow * args.ldc + col) * ESZ;
       if (vec_ok && col + EPC <= args.N) {
-        // the routed down projection's rows are next read by the combine,
-        // long after they leave the caches: non-temporal stores (measured
-        // 3% faster for that kernel)
+        // bf16 outputs take non-temporal stores: most are read long after
+        // they leave the caches (the routed down projection's rows by the
+        // combine, the weight gradients by the optimiser).  Measured 3%
+        // faster for the routed down projection and 1.5% for the weight
+        // gradients, and no slower for the shared expert's activations in
+        // the backward, which the SwiGLU backward reads next
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src_l);
-        if constexpr (EPI == kEpiBF16 && ROUTED)
+        if constexpr (EPI == kEpiBF16)
           __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
         else
           *reinterpret_cast<u32x4_t*>(dst) = v;

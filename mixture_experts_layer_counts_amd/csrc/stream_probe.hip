@@ -121,6 +121,8 @@ extern "C" moe_status moe_stream_probe(const moe_stream_probe_args* a, void* str
   // the MXFP8 routed up/gate's stage (256 + 256 rows, 2 + 3 slots)
   else if (A == 256 && B == 256 && NA == 2 && NB == 3) e = launch<4, 4, 2, 3>(p, s);
   else if (A == 256 && B == 0 && NA == 2 && NB == 3) e = launch<4, 0, 2, 3>(p, s);
+  // the same stage with both rings two slots deep (one stage in flight each)
+  else if (A == 256 && B == 256 && NA == 2 && NB == 2) e = launch<4, 4, 2, 2>(p, s);
   // weight rows alone, at ring depths of 2 to 5 slots (1 to 4 stages in flight)
   else if (A == 0 && B == 256 && NA == NB && NB == 2) e = launch<0, 4, 2, 2>(p, s);
   else if (A == 0 && B == 256 && NA == 2 && NB == 3) e = launch<0, 4, 2, 3>(p, s);

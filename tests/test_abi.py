@@ -273,7 +273,7 @@ def test_stream_probe_validates_before_any_launch(lib):
     assert call(a_share=0) == -1
     assert call(act=None) == -1                # activation rows asked, no buffer
     assert call(wts=None) == -1
-    assert call(slots_b=2) == -2               # the MXFP8 stage runs 2 + 3 slots
+    assert call(slots_b=4) == -2               # the MXFP8 stage runs 2 + 3 or 2 + 2 slots
     assert call(a_rows=128) == -2
     assert call(a_rows=0, b_rows=256, slots_a=6, slots_b=6) == -2
     assert call(row_bytes=128 << 20) == -2     # one item's rows past 2^31 bytes

@@ -12,7 +12,7 @@ from tests._gpu import need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = [(320, 256, 2, 2), (320, 0, 2, 2), (256, 256, 2, 3), (256, 0, 2, 3), (0, 256, 2, 3)] + \
+CONFIGS = [(320, 256, 2, 2), (320, 0, 2, 2), (256, 256, 2, 3), (256, 0, 2, 3), (256, 256, 2, 2), (0, 256, 2, 3)] + \
           [(0, 256, n, n) for n in (2, 3, 4, 5)]
 
 
