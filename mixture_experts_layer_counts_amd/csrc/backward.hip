@@ -212,9 +212,12 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(const uint16_t* __re
   for (int j = 0; j < 2; ++j) {
     const int v = threadIdx.x + 256 * j;
     const int c = v >> 3, r = (v & 7) * 8;  // output row (source column), first of 8 output columns
+    // the transposed operands (up to 1 GB each) are read back by the
+    // weight-gradient GEMMs only after the other transposes: non-temporal
+    // stores (measured 0.2% off the backward)
     if (w0 + c < W)
-      *reinterpret_cast<u32x4_t*>(out + static_cast<int64_t>(w0 + c) * ld_out + q0 + r) =
-          *reinterpret_cast<const u32x4_t*>(tile + c * kStride + r);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(tile + c * kStride + r),
+                                  reinterpret_cast<u32x4_t*>(out + static_cast<int64_t>(w0 + c) * ld_out + q0 + r));
   }
 }
 
@@ -259,9 +262,11 @@ __global__ __launch_bounds__(256) void dx_assemble_kernel(const float* __restric
       if (c == 0) raise_error(err, kErrExpertRange);
       continue;
     }
-    acc += *reinterpret_cast<const f32x4_t*>(dx_ring + static_cast<int64_t>(p) * D + c);
+    // each dx_ring row is read once, here: non-temporal loads, and a
+    // non-temporal store of dx (measured 0.2% off the backward)
+    acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(dx_ring + static_cast<int64_t>(p) * D + c));
   }
-  *reinterpret_cast<f32x4_t*>(dx + o) = acc;
+  __builtin_nontemporal_store(acc, reinterpret_cast<f32x4_t*>(dx + o));
 }
 
 // One segment of `rows` rows (the shared expert's and the router's weight

@@ -453,14 +453,18 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
       const char* src_l = smem + row_b * CS + ch * 16;
       char* dst = cbase + (crow * args.ldc + col) * ESZ;
       if (vec_ok && col + EPC <= args.N) {
-        // bf16 outputs take non-temporal stores: most are read long after
-        // they leave the caches (the routed down projection's rows by the
-        // combine, the weight gradients by the optimiser).  Measured 3%
-        // faster for the routed down projection and 1.5% for the weight
-        // gradients, and no slower for the shared expert's activations in
-        // the backward, which the SwiGLU backward reads next
+        // bf16 outputs and routed fp32 outputs take non-temporal stores:
+        // most are read long after they leave the caches (the routed down
+        // projection's rows by the combine, the weight gradients by the
+        // optimiser), and the backward's routed fp32 rows (dh, dx_ring, 0.5
+        // and 1.9 GB at the DeepSeek-V3 shape) do not fit the MALL anyway.
+        // Measured: the routed down projection 3% faster, the weight
+        // gradients 1.5%, the data-gradient GEMMs 2.7%, and no slower for
+        // the shared expert's activations in the backward.  The dense fp32
+        // outputs (the shared expert's, the router's logits) are read next
+        // and keep plain stores.
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src_l);
-        if constexpr (EPI == kEpiBF16)
+        if constexpr (EPI == kEpiBF16 || (EPI == kEpiF32 && ROUTED))
           __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
         else
           *reinterpret_cast<u32x4_t*>(dst) = v;
