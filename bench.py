@@ -62,6 +62,9 @@ def parse():
                     help="shared-expert precision (bf16 as the pages keep it; mxfp8 is an option)")
     ap.add_argument("--minibatch", type=int, default=0, help="rows per minibatch b (0: all routed rows)")
     ap.add_argument("--ring", type=int, default=0, help="ring rows C (0: b)")
+    ap.add_argument("--weights", default="tiled", choices=["tiled", "row-major"],
+                    help="layout of the routed bf16 weights: K-tiled (prepared once with tile_bf16, outside the "
+                         "timed region) or row-major; --backward always runs row-major")
     ap.add_argument("--pipeline", action="store_true",
                     help="run the routed minibatch loop as one persistent kernel (bf16 routed experts)")
     ap.add_argument("--mem-workgroups", type=int, default=16,
@@ -144,6 +147,12 @@ def time_weight_quantize(torch, inp, quantize_mxfp8, pack_mxfp8_scales):
             "GB_per_s": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / PEAK_HBM, 4)}
 
 
+def tile_weights(args, precision):
+    """Whether the routed weights run K-tiled: bf16 only, and never for the
+    backward, which prepares its own copies from row-major weights."""
+    return precision == "bf16" and args.weights == "tiled" and not args.backward
+
+
 def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
     """All experts on one GPU (R = 1)."""
     w = synth.workload(args.workload, routing=args.routing)
@@ -164,6 +173,10 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
             q, sc = quantize_mxfp8(inp["w_" + n])
             weights["q_" + n], weights["s_" + n] = q, pack_mxfp8_scales(sc)
         wq = time_weight_quantize(torch, inp, quantize_mxfp8, pack_mxfp8_scales)
+    tiled = tile_weights(args, precision)
+    if tiled:  # routed bf16 weights K-tiled ahead of time, outside the timed region
+        from mixture_experts_layer_counts_amd import tile_bf16
+        weights = dict(inp, **{n: tile_bf16(inp[n]) for n in ("w_gate", "w_up", "w_down")})
     if args.shared_precision == "mxfp8":  # the shared weights too, ahead of time
         from mixture_experts_layer_counts_amd import pack_mxfp8_scales
         weights = dict(weights)
@@ -180,7 +193,8 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
         layer = MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
                                    precision=precision, shared_precision=args.shared_precision,
                                    pipeline=args.pipeline if pipeline is None else pipeline,
-                                   mem_workgroups=args.mem_workgroups if mem is None else mem), device=dev)
+                                   mem_workgroups=args.mem_workgroups if mem is None else mem,
+                                   weights_tiled=tiled), device=dev)
 
         def step():
             if logits_in is not None:
@@ -199,6 +213,7 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
                config={"workload": f"{w.name}: T={w.T} D={w.D} I={w.I} E={w.E} top-{w.k} + 1 shared "
                                    f"(I={w.I_shared})", "minibatch_rows": b, "ring_rows": C,
                        "shared_precision": args.shared_precision,
+                       "routed_weights": "K-tiled" if tiled else "row-major",
                        "routing": "router projection from x" if logits_in is None else f"given {args.routing} logits"})
 
 
@@ -228,6 +243,10 @@ def setup_ep64(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
         for n in ("gate", "up", "down"):
             q, sc = quantize_mxfp8(inp["w_" + n])
             weights["q_" + n], weights["s_" + n] = q, pack_mxfp8_scales(sc)
+    tiled = tile_weights(args, precision)
+    if tiled:  # routed bf16 weights K-tiled ahead of time, outside the timed region
+        from mixture_experts_layer_counts_amd import tile_bf16
+        weights = dict(inp, **{n: tile_bf16(inp[n]) for n in ("w_gate", "w_up", "w_down")})
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
     dev = torch.device("cuda", 0)
@@ -243,7 +262,8 @@ def setup_ep64(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
         layer = MoELayer(shape_for(N, w.D, w.I, E_total, k, I_shared=w.I_shared, minibatch_rows=b, ring_rows=C,
                                    precision=precision, R=R, rank=c, max_rows=P,
                                    pipeline=args.pipeline if pipeline is None else pipeline,
-                                   mem_workgroups=args.mem_workgroups if mem is None else mem), device=dev)
+                                   mem_workgroups=args.mem_workgroups if mem is None else mem,
+                                   weights_tiled=tiled), device=dev)
 
         def step():
             _, _, gate = router.route(x_local, wr)
@@ -257,8 +277,8 @@ def setup_ep64(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
                inp=inp, step=step, make=make, routed_from_x=True, A=A, c=c, L=L, wr=wr, router=router, routing="x",
                config={"workload": f"ep64: one rank of 64 (4 local experts D={w.D} I={w.I}, {P} routed rows, "
                                    f"Zipf(1.2) counts {counts}; shared expert on {N} tokens)",
-                       "minibatch_rows": b, "ring_rows": C, "routing": "router projection from x (local tokens); "
-                                                                       "routes of all ranks synthetic"})
+                       "minibatch_rows": b, "ring_rows": C, "routed_weights": "K-tiled" if tiled else "row-major",
+                       "routing": "router projection from x (local tokens); routes of all ranks synthetic"})
 
 
 def kernel_model(job, offsets, sched_src):
@@ -525,15 +545,16 @@ def main():
         achieved, peak, unit = alg_bytes / t_dom / 1e9, PEAK_HBM / 1e9, "GB/s"
     else:
         achieved, peak, unit = alg_flops / t_dom / 1e12, peak_mma / 1e12, "TFLOP/s"
-    # counters taken on the same workload, routing, minibatch, precision and
-    # GEMM sources
+    # counters taken on the same workload, routing, minibatch, precision,
+    # routed-weight layout and GEMM sources
     traffic = None
     suffix = "" if job.routing == "x" else "_" + job.routing
     tr_path = os.path.join(ROOT, "profiles", f"traffic_{dominant}_{job.name}{suffix}.json")
     if os.path.exists(tr_path):
         tr = json.load(open(tr_path))
         if tr.get("src_digest") == gemm_digest(mx) and tr.get("minibatch_rows") == job.b and \
-                tr.get("precision", "bf16") == job.precision and tr.get("routing", "x") == job.routing:
+                tr.get("precision", "bf16") == job.precision and tr.get("routing", "x") == job.routing and \
+                tr.get("routed_weights", "row-major") == job.config.get("routed_weights", "row-major"):
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 typedef enum {
   MOE_OK = 0,
@@ -119,10 +119,21 @@ typedef struct {
                                   and leaving at least 8 for the GEMMs; unused
                                   (every workgroup runs GEMM items) when the
                                   ring holds all minibatches */
+  int32_t weights_tiled;       /* 0: the routed weights w_gate, w_up, w_down
+                                  row-major as described under moe_weights;
+                                  1: K-tiled, as moe_tile_bf16 writes them:
+                                  each expert's [N, K] matrix as [K/64, N, 64]
+                                  (planes of 64 K columns, each holding all N
+                                  rows), so that one K stage of the expert
+                                  GEMMs reads one contiguous plane.  Values
+                                  and results are the same either way.
+                                  precision MOE_BF16 only */
 } moe_shape;
 
 /* Expert weights, all K-contiguous (each output row is a contiguous K vector):
- *   routed  w_gate, w_up [L, I, D]; w_down [L, D, I]   (bf16, or e4m3 for MXFP8)
+ *   routed  w_gate, w_up [L, I, D]; w_down [L, D, I]   (bf16, or e4m3 for MXFP8;
+ *           with moe_shape.weights_tiled, bf16 [L, D/64, I, 64] and
+ *           [L, I/64, D, 64])
  *           s_gate, s_up [L, D/128, I, 4]; s_down [L, I/128, D, 4]   (E8M0,
  *           MXFP8 only): stage-major scales, as moe_mxfp8_pack_scales writes
  *           them from the row-major [L, N, K/32] of moe_quantize_mxfp8
@@ -288,7 +299,9 @@ typedef struct {
 
 /* Fill `bw` from the forward's weights and the router weights (transposes and
  * copies on `stream`, run once per weight set).  MOE_ERR_UNSUPPORTED unless
- * num_src_ranks == 1 and both precisions are MOE_BF16. */
+ * num_src_ranks == 1, both precisions are MOE_BF16 and the routed weights are
+ * row-major (weights_tiled == 0); the same holds for moe_backward and
+ * moe_backward_workspace_bytes. */
 moe_status moe_backward_prepare(const moe_shape* shape, const moe_weights* weights, const void* w_router,
                                 const moe_bwd_weights* bw, void* stream);
 
@@ -329,6 +342,17 @@ moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const
  */
 moe_status moe_routed_rows(const moe_shape* shape, const void* ws, size_t ws_bytes, const void** rows,
                            int64_t* n_rows);
+
+/*
+ * K-tiling of bf16 matrices (the routed weights' moe_shape.weights_tiled
+ * layout; the weights are prepared once, ahead of the layer, as in MoK paper
+ * §3.4, "MXFP8 Support").  src [groups, rows, K] row-major -> dst [groups,
+ * K/64, rows, 64]: element (g, r, k) lands at ((g*(K/64) + k/64)*rows + r)*64
+ * + k%64.  K must be a positive multiple of 64, both pointers 16-byte aligned
+ * and the buffers distinct (MOE_ERR_INVALID_ARG otherwise).  Byte moves only
+ * (bit-exact).  Device memory, caller-owned; one launch on `stream`.
+ */
+moe_status moe_tile_bf16(const void* src, int64_t groups, int64_t rows, int64_t K, void* dst, void* stream);
 
 /*
  * MX quantisation along rows (MoK paper §3.4, "MXFP8 Support": weights are

@@ -5,4 +5,5 @@ into the C calls moe_route, moe_schedule and moe_forward; every step of the
 layer runs in the library's kernels.
 """
 
-from .api import MoEBackward, MoELayer, pack_mxfp8_scales, prepare_backward, quantize_mxfp8, shape_for  # noqa: F401
+from .api import (MoEBackward, MoELayer, pack_mxfp8_scales, prepare_backward, quantize_mxfp8, shape_for,  # noqa: F401
+                  tile_bf16)

@@ -29,7 +29,7 @@ class MoeShape(ctypes.Structure):
         "T", "D", "I", "I_shared", "E_total", "k", "num_src_ranks", "rank", "experts_per_rank",
         "tokens_per_src_rank", "max_rows", "minibatch_rows", "ring_rows")] + [
         ("precision", ctypes.c_int32), ("shared_precision", ctypes.c_int32), ("pipeline", ctypes.c_int32),
-        ("mem_workgroups", ctypes.c_int32)]
+        ("mem_workgroups", ctypes.c_int32), ("weights_tiled", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -75,6 +75,7 @@ _SIGS = {
                                        ctypes.POINTER(ctypes.c_int64)]),
     "moe_quantize_mxfp8": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]),
     "moe_mxfp8_pack_scales": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P]),
+    "moe_tile_bf16": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P]),
     "moe_get_device_error": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_size_t, _P,
                                             ctypes.POINTER(ctypes.c_int32)]),
     "moe_backward_prepare": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights), _P,

@@ -39,12 +39,14 @@ def _need(t: torch.Tensor, name: str, dtype, shape, device: torch.device) -> Non
 def shape_for(T: int, D: int, I: int, E: int, k: int, I_shared: Optional[int] = None,
               minibatch_rows: Optional[int] = None, ring_rows: Optional[int] = None,
               precision: str = "bf16", R: int = 1, rank: int = 0, max_rows: Optional[int] = None,
-              shared_precision: str = "bf16", pipeline: bool = False, mem_workgroups: int = 0) -> _lib.MoeShape:
+              shared_precision: str = "bf16", pipeline: bool = False, mem_workgroups: int = 0,
+              weights_tiled: bool = False) -> _lib.MoeShape:
     """A moe_shape for one GPU (R = 1) or for rank ``rank`` of R source ranks.
     ``precision`` is that of the routed experts, ``shared_precision`` that of
     the shared expert (bf16 unless MXFP8 is asked for).  ``pipeline`` runs the
     routed minibatch loop as one persistent kernel, ``mem_workgroups`` of
-    whose workgroups gather the minibatches the ring does not hold at once."""
+    whose workgroups gather the minibatches the ring does not hold at once.
+    ``weights_tiled``: the routed bf16 weights come K-tiled (``tile_bf16``)."""
     L = E // R
     max_rows = T * k if max_rows is None else max_rows
     b = minibatch_rows or max(max_rows, 1)
@@ -56,6 +58,7 @@ def shape_for(T: int, D: int, I: int, E: int, k: int, I_shared: Optional[int] = 
     s.precision = {"bf16": _lib.MOE_BF16, "mxfp8": _lib.MOE_MXFP8}[precision]
     s.shared_precision = {"bf16": _lib.MOE_BF16, "mxfp8": _lib.MOE_MXFP8}[shared_precision]
     s.pipeline, s.mem_workgroups = int(bool(pipeline)), mem_workgroups
+    s.weights_tiled = int(bool(weights_tiled))
     return s
 
 
@@ -132,8 +135,9 @@ class MoELayer:
         _need(gate, "gate", torch.float32, (s.T, s.k), dev)
         w = _lib.MoeWeights()
         if s.precision == _lib.MOE_BF16:
-            for n, shp in (("w_gate", (L, I, D)), ("w_up", (L, I, D)), ("w_down", (L, D, I))):
-                _need(weights[n], n, torch.bfloat16, shp, dev)
+            for n, (N, K) in (("w_gate", (I, D)), ("w_up", (I, D)), ("w_down", (D, I))):
+                # row-major [L, N, K], or K-tiled [L, K/64, N, 64] (tile_bf16)
+                _need(weights[n], n, torch.bfloat16, (L, K // 64, N, 64) if s.weights_tiled else (L, N, K), dev)
                 setattr(w, n, _ptr(weights[n]))
         else:
             for n, qn, sn, shp in (("w_gate", "q_gate", "s_gate", (L, I, D)), ("w_up", "q_up", "s_up", (L, I, D)),
@@ -301,6 +305,20 @@ def quantize_mxfp8(src: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     sc = torch.empty(src.shape[:-1] + (K // 32,), dtype=torch.uint8, device=src.device)
     _lib.check("moe_quantize_mxfp8", lib.moe_quantize_mxfp8(_ptr(src), rows, K, _ptr(q), _ptr(sc), _stream()))
     return q, sc
+
+
+def tile_bf16(w: torch.Tensor) -> torch.Tensor:
+    """Row-major bf16 matrices [G, N, K] -> the K-tiled [G, K/64, N, 64]
+    that ``forward`` reads with ``weights_tiled`` (moe_tile_bf16)."""
+    lib = _lib.load()
+    if w.dtype != torch.bfloat16 or not w.is_contiguous() or w.device.type != "cuda" or w.dim() != 3:
+        raise ValueError("w must be a contiguous bf16 [G, N, K] device tensor")
+    G, N, K = w.shape
+    if K % 64:
+        raise ValueError("K must be a multiple of 64")
+    out = torch.empty((G, K // 64, N, 64), dtype=torch.bfloat16, device=w.device)
+    _lib.check("moe_tile_bf16", lib.moe_tile_bf16(_ptr(w), G, N, K, _ptr(out), _stream()))
+    return out
 
 
 def pack_mxfp8_scales(scale: torch.Tensor) -> torch.Tensor:

@@ -11,6 +11,8 @@
 // atomics, a fixed order): out32[t] = (sum over s in slot order of
 // fma(g[t,s], y[t,s], .)) + shared[t], in fp32; out = bf16(out32).
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -148,6 +150,31 @@ hipError_t launch_combine(const uint16_t* Y, const float* shared_out, const floa
   if (T <= 0) return hipSuccess;
   combine_kernel<<<T, 256, 0, stream>>>(Y, shared_out, gate, route_dst, route_base, D, k, by_route_dst ? 1 : 0,
                                         out, out32);
+  return hipGetLastError();
+}
+
+// K-tiling of bf16 matrices [groups][rows][K] -> [groups][K/64][rows][64]:
+// one 16-byte chunk (eight elements) per thread and step; eight consecutive
+// threads read 128 contiguous bytes of a row and write one whole 128-byte
+// line of a plane.
+__global__ __launch_bounds__(256) void tile_bf16_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t K,
+                                                        int64_t chunks, uint16_t* __restrict__ dst) {
+  const int64_t per_row = K / 8, per_group = rows * per_row;
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < chunks;
+       q += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t g = q / per_group, rem = q - g * per_group;
+    const int64_t r = rem / per_row, c = rem - r * per_row;
+    const int64_t to = ((g * (K / kTileK) + c / 8) * rows + r) * kTileK + (c % 8) * 8;
+    *reinterpret_cast<uint4*>(dst + to) = *reinterpret_cast<const uint4*>(src + q * 8);
+  }
+}
+
+hipError_t launch_tile_bf16(const uint16_t* src, int64_t groups, int64_t rows, int64_t K, uint16_t* dst,
+                            hipStream_t stream) {
+  if (groups <= 0 || rows <= 0 || K <= 0 || K % kTileK) return hipErrorInvalidValue;
+  const int64_t chunks = groups * rows * (K / 8);
+  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 65536);
+  tile_bf16_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(src, rows, K, chunks, dst);
   return hipGetLastError();
 }
 

@@ -59,6 +59,12 @@ enum GemmEpilogue : int {
   kEpiF32 = 2,     // C = A B0^T in fp32
 };
 
+// K-tiled layout of a bf16 matrix [R][K]: element (r, k) at
+// ((k / kTileK) * R + r) * kTileK + k % kTileK (moe_tile_bf16).
+constexpr int kTileK = 64;
+hipError_t launch_tile_bf16(const uint16_t* src, int64_t groups, int64_t rows, int64_t K, uint16_t* dst,
+                            hipStream_t stream);
+
 struct GemmArgs {
   const uint16_t* A;  // bf16; tile position p reads row (p - a_sub) mod a_mod
   int64_t a_bytes;    // extent of A in bytes (< 2^31)
@@ -68,6 +74,9 @@ struct GemmArgs {
   const uint16_t* B0;  // bf16 [experts][N][K]
   const uint16_t* B1;  // second operand of the SwiGLU epilogue (same layout)
   int64_t b_expert_stride;
+  // 0: each expert's B row-major [N][K] (row stride ldb); N (routed only):
+  // K-tiled [K/kTileK][N][kTileK], so that one K stage's rows are one plane
+  int64_t b_plane;
   int N;
   int K;
   void* C;  // output row = c_idx ? c_idx[p] : p - c_sub

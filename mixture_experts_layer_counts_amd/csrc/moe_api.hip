@@ -75,8 +75,10 @@ bool valid_shape(const moe_shape* s, moe_status* why) {
   if (s->precision != MOE_BF16 && s->precision != MOE_MXFP8) return false;
   if (s->pipeline != 0 && s->pipeline != 1) return false;
   if (s->pipeline && (s->mem_workgroups < 0 || s->mem_workgroups % 8)) return false;
+  if (s->weights_tiled != 0 && s->weights_tiled != 1) return false;
   *why = MOE_ERR_UNSUPPORTED;
   if (s->pipeline && s->precision != MOE_BF16) return false;
+  if (s->weights_tiled && s->precision != MOE_BF16) return false;
   if (s->D % 64 || s->I % 64 || s->I_shared % 64) return false;
   if (s->k > 16 || s->E_total > 1024 || s->experts_per_rank > 1024) return false;
   if (s->num_src_ranks * s->T * s->k >= (int64_t(1) << 31)) return false;
@@ -617,6 +619,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     u.B0 = static_cast<const uint16_t*>(w->w_gate);
     u.B1 = static_cast<const uint16_t*>(w->w_up);
     u.b_expert_stride = static_cast<int64_t>(I) * D;
+    u.b_plane = shape->weights_tiled ? I : 0;
     u.N = I;
     u.K = D;
     u.C = hbuf;
@@ -641,6 +644,7 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* w, const void*
     d.a_mod = INT64_MAX;
     d.B0 = static_cast<const uint16_t*>(w->w_down);
     d.b_expert_stride = static_cast<int64_t>(D) * I;
+    d.b_plane = shape->weights_tiled ? D : 0;
     d.N = D;
     d.K = I;
     d.C = Y;
@@ -738,6 +742,15 @@ moe_status moe_routed_rows(const moe_shape* shape, const void* ws, size_t ws_byt
   return MOE_OK;
 }
 
+moe_status moe_tile_bf16(const void* src, int64_t groups, int64_t rows, int64_t K, void* dst, void* stream) {
+  if (groups < 0 || rows < 0 || K <= 0 || K % moe::kTileK != 0) return MOE_ERR_INVALID_ARG;
+  if (groups == 0 || rows == 0) return MOE_OK;
+  if (!src || !dst || src == dst) return MOE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_tile_bf16(static_cast<const uint16_t*>(src), groups, rows, K,
+                                          static_cast<uint16_t*>(dst), static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* scale, void* stream) {
   if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;
@@ -832,7 +845,8 @@ struct BwdLayout {
 bool valid_bwd_shape(const moe_shape* s, moe_status* why) {
   if (!valid_shape(s, why)) return false;
   *why = MOE_ERR_UNSUPPORTED;
-  if (s->num_src_ranks != 1 || s->precision != MOE_BF16 || s->shared_precision != MOE_BF16) return false;
+  if (s->num_src_ranks != 1 || s->precision != MOE_BF16 || s->shared_precision != MOE_BF16 || s->weights_tiled)
+    return false;
   constexpr int64_t kLimit = int64_t(1) << 31;
   const int64_t P = s->T * s->k, Ppad = pad64(P) + 64 * s->experts_per_rank, Tpad = pad64(s->T);
   const int64_t Ep = pad64(s->E_total);

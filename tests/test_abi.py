@@ -149,6 +149,29 @@ def test_pack_scales_validates_before_launching(lib):
     assert lib.moe_mxfp8_pack_scales(a, 0, 8, 128, b, None) == 0      # nothing to move: no launch
 
 
+def test_tile_bf16_validates_before_launching(lib):
+    a, b = ctypes.c_void_p(4096), ctypes.c_void_p(8192)  # never dereferenced
+    assert lib.moe_tile_bf16(a, 2, 8, 96, b, None) == -1             # K not a multiple of 64
+    assert lib.moe_tile_bf16(a, 2, 8, 128, a, None) == -1            # in place
+    assert lib.moe_tile_bf16(ctypes.c_void_p(4104), 2, 8, 128, b, None) == -1  # misaligned
+    assert lib.moe_tile_bf16(None, 2, 8, 128, b, None) == -1
+    assert lib.moe_tile_bf16(a, 2, -1, 128, b, None) == -1
+    assert lib.moe_tile_bf16(a, 0, 8, 128, b, None) == 0             # nothing to move: no launch
+
+
+def test_tiled_weights_flag(lib):
+    # the K-tiled routed weights are a bf16 layout; the backward prepares its
+    # own copies from row-major weights
+    assert ws_bytes(lib, shape_for(T=64, D=128, I=128, E=8, k=2, weights_tiled=True))[0] == 0
+    bad = shape_for(T=64, D=128, I=128, E=8, k=2)
+    bad.weights_tiled = 2
+    assert ws_bytes(lib, bad)[0] == -1
+    assert ws_bytes(lib, shape_for(T=64, D=128, I=128, E=8, k=2, precision="mxfp8", weights_tiled=True))[0] == -2
+    n = ctypes.c_size_t()
+    s = shape_for(T=64, D=128, I=128, E=8, k=2, weights_tiled=True)
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == -2
+
+
 # Each case breaks exactly one buffer-resource limit of the GEMM operands
 # (fewer than 2^31 bytes each) while every other operand stays small; the
 # second set of sizes is the same shape brought just under that limit.
