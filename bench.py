@@ -63,8 +63,8 @@ def parse():
     ap.add_argument("--minibatch", type=int, default=0, help="rows per minibatch b (0: all routed rows)")
     ap.add_argument("--ring", type=int, default=0, help="ring rows C (0: b)")
     ap.add_argument("--weights", default="tiled", choices=["tiled", "row-major"],
-                    help="layout of the routed bf16 weights: K-tiled (prepared once with tile_bf16, outside the "
-                         "timed region) or row-major; --backward always runs row-major")
+                    help="layout of the routed weights: K-tiled (prepared once with tile_bf16 / tile_mxfp8, "
+                         "outside the timed region) or row-major; --backward always runs row-major")
     ap.add_argument("--pipeline", action="store_true",
                     help="run the routed minibatch loop as one persistent kernel (bf16 routed experts)")
     ap.add_argument("--mem-workgroups", type=int, default=16,
@@ -148,9 +148,17 @@ def time_weight_quantize(torch, inp, quantize_mxfp8, pack_mxfp8_scales):
 
 
 def tile_weights(args, precision):
-    """Whether the routed weights run K-tiled: bf16 only, and never for the
-    backward, which prepares its own copies from row-major weights."""
-    return precision == "bf16" and args.weights == "tiled" and not args.backward
+    """Whether the routed weights run K-tiled: never for the backward, which
+    prepares its own copies from row-major weights."""
+    return args.weights == "tiled" and not args.backward
+
+
+def tile_routed(weights, precision):
+    """The routed weights K-tiled: bf16 w_* by tile_bf16, E4M3 q_* by tile_mxfp8."""
+    from mixture_experts_layer_counts_amd import tile_bf16, tile_mxfp8
+    if precision == "bf16":
+        return dict(weights, **{n: tile_bf16(weights[n]) for n in ("w_gate", "w_up", "w_down")})
+    return dict(weights, **{n: tile_mxfp8(weights[n]) for n in ("q_gate", "q_up", "q_down")})
 
 
 def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
@@ -174,9 +182,8 @@ def setup_single(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
             weights["q_" + n], weights["s_" + n] = q, pack_mxfp8_scales(sc)
         wq = time_weight_quantize(torch, inp, quantize_mxfp8, pack_mxfp8_scales)
     tiled = tile_weights(args, precision)
-    if tiled:  # routed bf16 weights K-tiled ahead of time, outside the timed region
-        from mixture_experts_layer_counts_amd import tile_bf16
-        weights = dict(inp, **{n: tile_bf16(inp[n]) for n in ("w_gate", "w_up", "w_down")})
+    if tiled:  # routed weights K-tiled ahead of time, outside the timed region
+        weights = tile_routed(weights, precision)
     if args.shared_precision == "mxfp8":  # the shared weights too, ahead of time
         from mixture_experts_layer_counts_amd import pack_mxfp8_scales
         weights = dict(weights)
@@ -244,9 +251,8 @@ def setup_ep64(args, torch, synth, MoELayer, shape_for, quantize_mxfp8):
             q, sc = quantize_mxfp8(inp["w_" + n])
             weights["q_" + n], weights["s_" + n] = q, pack_mxfp8_scales(sc)
     tiled = tile_weights(args, precision)
-    if tiled:  # routed bf16 weights K-tiled ahead of time, outside the timed region
-        from mixture_experts_layer_counts_amd import tile_bf16
-        weights = dict(inp, **{n: tile_bf16(inp[n]) for n in ("w_gate", "w_up", "w_down")})
+    if tiled:  # routed weights K-tiled ahead of time, outside the timed region
+        weights = tile_routed(weights, precision)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
     dev = torch.device("cuda", 0)

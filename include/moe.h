@@ -123,17 +123,20 @@ typedef struct {
                                   row-major as described under moe_weights;
                                   1: K-tiled, as moe_tile_bf16 writes them:
                                   each expert's [N, K] matrix as [K/64, N, 64]
-                                  (planes of 64 K columns, each holding all N
-                                  rows), so that one K stage of the expert
-                                  GEMMs reads one contiguous plane.  Values
-                                  and results are the same either way.
-                                  precision MOE_BF16 only */
+                                  in bf16 (planes of 64 K columns, each
+                                  holding all N rows), or its E4M3 bytes as
+                                  [K/128, N, 128] in MXFP8 (moe_tile_bf16 on
+                                  the bytes taken as 2-byte units; the scales
+                                  stay as described under moe_weights), so
+                                  that one K stage of the expert GEMMs reads
+                                  one contiguous plane.  Values and results
+                                  are the same either way */
 } moe_shape;
 
 /* Expert weights, all K-contiguous (each output row is a contiguous K vector):
  *   routed  w_gate, w_up [L, I, D]; w_down [L, D, I]   (bf16, or e4m3 for MXFP8;
  *           with moe_shape.weights_tiled, bf16 [L, D/64, I, 64] and
- *           [L, I/64, D, 64])
+ *           [L, I/64, D, 64], e4m3 [L, D/128, I, 128] and [L, I/128, D, 128])
  *           s_gate, s_up [L, D/128, I, 4]; s_down [L, I/128, D, 4]   (E8M0,
  *           MXFP8 only): stage-major scales, as moe_mxfp8_pack_scales writes
  *           them from the row-major [L, N, K/32] of moe_quantize_mxfp8

@@ -6,4 +6,4 @@ layer runs in the library's kernels.
 """
 
 from .api import (MoEBackward, MoELayer, pack_mxfp8_scales, prepare_backward, quantize_mxfp8, shape_for,  # noqa: F401
-                  tile_bf16)
+                  tile_bf16, tile_mxfp8)

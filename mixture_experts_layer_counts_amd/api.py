@@ -142,7 +142,9 @@ class MoELayer:
         else:
             for n, qn, sn, shp in (("w_gate", "q_gate", "s_gate", (L, I, D)), ("w_up", "q_up", "s_up", (L, I, D)),
                                    ("w_down", "q_down", "s_down", (L, D, I))):
-                _need(weights[qn], qn, torch.uint8, shp, dev)
+                # row-major [L, N, K] bytes, or K-tiled [L, K/128, N, 128] (tile_mxfp8)
+                _need(weights[qn], qn, torch.uint8,
+                      (L, shp[2] // 128, shp[1], 128) if s.weights_tiled else shp, dev)
                 _need(weights[sn], sn, torch.uint8, (L, shp[2] // 128, shp[1], 4), dev)
                 setattr(w, n, _ptr(weights[qn]))
                 setattr(w, sn, _ptr(weights[sn]))
@@ -319,6 +321,16 @@ def tile_bf16(w: torch.Tensor) -> torch.Tensor:
     out = torch.empty((G, K // 64, N, 64), dtype=torch.bfloat16, device=w.device)
     _lib.check("moe_tile_bf16", lib.moe_tile_bf16(_ptr(w), G, N, K, _ptr(out), _stream()))
     return out
+
+
+def tile_mxfp8(q: torch.Tensor) -> torch.Tensor:
+    """Row-major E4M3 bytes [G, N, K] -> the K-tiled [G, K/128, N, 128] that
+    ``forward`` reads with ``weights_tiled`` (moe_tile_bf16 on the bytes taken
+    as 2-byte units)."""
+    if q.dtype != torch.uint8 or not q.is_contiguous() or q.dim() != 3 or q.shape[2] % 128:
+        raise ValueError("q must be contiguous uint8 [G, N, K] with K a multiple of 128")
+    G, N, K = q.shape
+    return tile_bf16(q.view(torch.bfloat16)).view(torch.uint8).view(G, K // 128, N, 128)
 
 
 def pack_mxfp8_scales(scale: torch.Tensor) -> torch.Tensor:

@@ -88,7 +88,8 @@ struct MxScales {  // one stage's scale words (4 K blocks) of this lane's fragme
 // and wave: AI + BI 1 KB direct loads and FML + NB*FN 4-byte scale loads.
 template <int BN, int NB, int FML, int FM, int FN, int AI, int BI>
 __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const uint32_t (&a_off)[AI],
-                                          const uint32_t (&b_off)[BI], const MxScaleOff<FM, NB, FN>& so, int nk,
+                                          const uint32_t (&b_off)[BI], int b_stage, const MxScaleOff<FM, NB, FN>& so,
+                                          int nk,
                                           int a_rows, int as_stage, int bs_stage, int tid, int wm, int wn,
                                           f32x16_t (&acc)[NB][FM][FN]) {
   constexpr int BM = kMxBM, BROWS = NB * BN;
@@ -127,7 +128,7 @@ __device__ __forceinline__ void k_loop_mx(char* smem, const MxSrc& src, const ui
 #pragma unroll
     for (int j = 0; j < BI; ++j) {
       const int g = wave * BI + j;
-      dma16((NB == 2 && g * ROWS_PER_LD >= BN) ? src.b1 : src.b0, sb + g * 1024, b_off[j], kc * kRB);
+      dma16((NB == 2 && g * ROWS_PER_LD >= BN) ? src.b1 : src.b0, sb + g * 1024, b_off[j], kc * b_stage);
     }
   };
 
@@ -317,6 +318,10 @@ __device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int 
     const int64_t arow = (p - args.a_sub) % args.a_mod;
     a_off[j] = static_cast<uint32_t>(arow * K + c * 16);
   }
+  // weights K-tiled: a stage's weight rows sit in one plane of N rows, kRB
+  // bytes apart, and the next stage's plane follows
+  const bool b_tiled = args.b_plane > 0;
+  const int b_stage = b_tiled ? static_cast<int>(args.b_plane * kRB) : kRB;
   uint32_t b_off[BI];
 #pragma unroll
   for (int j = 0; j < BI; ++j) {
@@ -325,7 +330,7 @@ __device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int 
     const int half = row / BN;
     int n = n0 + (row - half * BN);
     n = n < args.N ? n : args.N - 1;
-    b_off[j] = static_cast<uint32_t>(static_cast<int64_t>(n) * K + c * 16);
+    b_off[j] = b_tiled ? static_cast<uint32_t>(n * kRB + c * 16) : static_cast<uint32_t>(static_cast<int64_t>(n) * K + c * 16);
   }
   // ---- scale words of this lane's fragment rows in stage 0 (rows past the
   // tile or N are clamped; their products only reach dropped outputs); stage
@@ -382,7 +387,7 @@ __device__ __forceinline__ void gemm_mx_item(const MxGemmArgs& args, int w, int 
 #define MOE_CASE(n)                                                                                         \
   case n:                                                                                                   \
     if constexpr (n <= FM)                                                                                  \
-      k_loop_mx<BN, NB, n, FM, FN, AI, BI>(smem, src, a_off, b_off, so, nk, nrows, as_stage, bs_stage, tid, \
+      k_loop_mx<BN, NB, n, FM, FN, AI, BI>(smem, src, a_off, b_off, b_stage, so, nk, nrows, as_stage, bs_stage, tid, \
                                             wm, wn, acc);                                                \
     break;
     MOE_CASE(0)
@@ -605,6 +610,7 @@ hipError_t launch_gemm_mx(const MxGemmArgs& a, int epilogue, hipStream_t stream)
   // buffer resources address at most 2^31 bytes per operand here
   if (a.a_rows * a.K >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   if (static_cast<int64_t>(a.N) * a.K >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (a.b_plane != 0 && a.b_plane != a.N) return hipErrorInvalidValue;  // K-tiled weights: planes of all N rows
   // 16-byte output stores: the base and the row strides keep 16-byte alignment
   if (reinterpret_cast<uintptr_t>(a.C) % 16 != 0) return hipErrorInvalidValue;
   switch (epilogue) {

@@ -116,6 +116,7 @@ struct MxGemmArgs {
   const uint8_t* B1;  // up (SwiGLU)
   const uint8_t* Bs0;
   const uint8_t* Bs1;
+  int64_t b_plane;  // 0: each expert's B row-major [N][K]; N: K-tiled [K/128][N][128] (one plane per K stage)
   int N;
   int K;
   void* C;      // SwiGLU: E4M3 [.][ldc], scales to Cs [ldc/128][cs_rows][4]; BF16: bf16 [.][ldc]; F32: fp32 [.][ldc]

@@ -78,7 +78,6 @@ bool valid_shape(const moe_shape* s, moe_status* why) {
   if (s->weights_tiled != 0 && s->weights_tiled != 1) return false;
   *why = MOE_ERR_UNSUPPORTED;
   if (s->pipeline && s->precision != MOE_BF16) return false;
-  if (s->weights_tiled && s->precision != MOE_BF16) return false;
   if (s->D % 64 || s->I % 64 || s->I_shared % 64) return false;
   if (s->k > 16 || s->E_total > 1024 || s->experts_per_rank > 1024) return false;
   if (s->num_src_ranks * s->T * s->k >= (int64_t(1) << 31)) return false;
@@ -353,6 +352,7 @@ hipError_t routed_minibatch_mx(const moe_shape* shape, const moe_weights* w, con
   u.B1 = static_cast<const uint8_t*>(w->w_up);
   u.Bs0 = w->s_gate;
   u.Bs1 = w->s_up;
+  u.b_plane = shape->weights_tiled ? I : 0;
   u.N = I;
   u.K = D;
   u.C = h_q;
@@ -379,6 +379,7 @@ hipError_t routed_minibatch_mx(const moe_shape* shape, const moe_weights* w, con
   d.B1 = nullptr;
   d.Bs0 = w->s_down;
   d.Bs1 = nullptr;
+  d.b_plane = shape->weights_tiled ? D : 0;
   d.N = D;
   d.K = I;
   d.C = at<uint16_t>(ws, L.Y);

@@ -160,13 +160,13 @@ def test_tile_bf16_validates_before_launching(lib):
 
 
 def test_tiled_weights_flag(lib):
-    # the K-tiled routed weights are a bf16 layout; the backward prepares its
+    # the routed weights K-tiled (bf16 or E4M3); the backward prepares its
     # own copies from row-major weights
     assert ws_bytes(lib, shape_for(T=64, D=128, I=128, E=8, k=2, weights_tiled=True))[0] == 0
     bad = shape_for(T=64, D=128, I=128, E=8, k=2)
     bad.weights_tiled = 2
     assert ws_bytes(lib, bad)[0] == -1
-    assert ws_bytes(lib, shape_for(T=64, D=128, I=128, E=8, k=2, precision="mxfp8", weights_tiled=True))[0] == -2
+    assert ws_bytes(lib, shape_for(T=64, D=128, I=128, E=8, k=2, precision="mxfp8", weights_tiled=True))[0] == 0
     n = ctypes.c_size_t()
     s = shape_for(T=64, D=128, I=128, E=8, k=2, weights_tiled=True)
     assert lib.moe_backward_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == -2

@@ -1,8 +1,8 @@
-"""The routed bf16 weights in the K-tiled layout (moe_shape.weights_tiled):
+"""The routed weights in the K-tiled layout (moe_shape.weights_tiled):
 moe_tile_bf16 moves every element to ((g*(K/64) + k/64)*N + n)*64 + k%64, and
 the layer gives bitwise the same output as with row-major weights, through
-the C ABI, at several shapes, minibatch and ring sizes, stream-ordered and
-persistent."""
+the C ABI: bf16 at several shapes, minibatch and ring sizes, stream-ordered
+and persistent; MXFP8 with the E4M3 bytes tiled in 128-byte planes."""
 
 import pytest
 import torch
@@ -57,3 +57,30 @@ def test_tiled_weights_bitwise_equal(w, bcs):
             assert m.device_error() == 0
             outs.append(r["out32"].cpu())
         assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+
+
+MX_CASES = [
+    synth.Workload("tiny-mx", T=64, D=128, I=128, E=8, k=2, I_shared=64, seed=55, routing="gaussian"),
+    synth.Workload("ragged-mx", T=300, D=384, I=256, E=16, k=4, I_shared=128, seed=56, routing="zipf"),
+    synth.Workload("wide-mx", T=1024, D=7168, I=2048, E=12, k=8, I_shared=2048, seed=57, routing="gaussian"),
+]
+
+
+@pytest.mark.parametrize("w", MX_CASES, ids=[w.name for w in MX_CASES])
+def test_tiled_mx_weights_bitwise_equal(w):
+    dev = need_gpu()
+    from mixture_experts_layer_counts_amd import MoELayer, shape_for, tile_mxfp8
+    from tests._gpu import mx_weights_dev
+    inp_dev = to_dev(synth.make_inputs(w), dev)
+    wq = mx_weights_dev(inp_dev)
+    tiled = dict(wq, **{n: tile_mxfp8(wq[n]) for n in ("q_gate", "q_up", "q_down")})
+    say("tiled MX weights", w.name)
+    outs = []
+    for wt, weights in ((False, wq), (True, tiled)):
+        m = MoELayer(shape_for(w.T, w.D, w.I, w.E, w.k, I_shared=w.I_shared, precision="mxfp8", weights_tiled=wt),
+                     device=dev)
+        r = m(inp_dev["x"], inp_dev["w_router"], weights, logits=inp_dev["logits"])
+        torch.cuda.synchronize()
+        assert m.device_error() == 0
+        outs.append(r["out32"].cpu())
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
