@@ -279,8 +279,10 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const
 
 /* The weights rearranged for the backward (caller-allocated device memory,
  * filled once per weight set by moe_backward_prepare; bf16):
- *   w_gu [L, 2I, D]: W_gate and W_up of each expert stacked (the replay's
- *     operand); w_gu_t [L, D, 2I]: [W_gate^T | W_up^T]; w_down_t [L, I, D];
+ *   w_gu: W_gate and W_up of each expert stacked ([2I, D], the replay's
+ *     operand); w_gu_t: [W_gate^T | W_up^T] ([D, 2I]); w_down_t: W_down^T
+ *     ([I, D]); each expert's matrix K-tiled as under moe_shape.weights_tiled
+ *     ([D/64, 2I, 64], [2I/64, D, 64], [D/64, I, 64]; sizes unchanged);
  *   ws_gu [2I_s, D], ws_gu_t [D, 2I_s], ws_down_t [I_s, D]: the shared expert;
  *   w_router_t [D, Ep]: W_r^T with Ep = E_total rounded up to 64 (zero past
  *     E_total). */

@@ -222,10 +222,12 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(const uint16_t* __re
 }
 
 // Batched transpose: out[b][c][col0 + r] = in[b][r][c] for in [B][R][Cn]
-// (bf16), out rows of stride ld_out, batch strides in_b / out_b.
+// (bf16), out rows of stride ld_out, batch strides in_b / out_b; with
+// plane_rows > 0 the output is K-tiled instead: element (row, col) of batch b
+// at ((col / 64) * plane_rows + row) * 64 + col % 64.
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ in, int R, int Cn, int64_t in_b,
                                                         uint16_t* __restrict__ out, int64_t ld_out, int64_t out_b,
-                                                        int col0) {
+                                                        int col0, int64_t plane_rows) {
   __shared__ uint16_t tile[64][66];
   const int b = blockIdx.z;
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
@@ -238,7 +240,9 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
   __syncthreads();
   for (int v = threadIdx.x; v < 64 * 64; v += 256) {
     const int c = v / 64, r = v % 64;
-    if (r0 + r < R && c0 + c < Cn) dst[static_cast<int64_t>(c0 + c) * ld_out + col0 + r0 + r] = tile[c][r];
+    if (r0 + r >= R || c0 + c >= Cn) continue;
+    const int64_t row = c0 + c, col = col0 + r0 + r;
+    dst[plane_rows > 0 ? ((col / kTileK) * plane_rows + row) * kTileK + col % kTileK : row * ld_out + col] = tile[c][r];
   }
 }
 
@@ -341,10 +345,11 @@ hipError_t launch_seg_transpose(const uint16_t* src, int64_t lda, int W, const i
 }
 
 hipError_t launch_transpose(const uint16_t* in, int B, int R, int Cn, uint16_t* out, int64_t ld_out, int64_t out_b,
-                            int col0, hipStream_t s) {
+                            int col0, hipStream_t s, int64_t plane_rows) {
   if (B <= 0 || R <= 0 || Cn <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((R + 63) / 64), static_cast<unsigned>((Cn + 63) / 64), static_cast<unsigned>(B));
-  transpose_kernel<<<grid, 256, 0, s>>>(in, R, Cn, static_cast<int64_t>(R) * Cn, out, ld_out, out_b, col0);
+  transpose_kernel<<<grid, 256, 0, s>>>(in, R, Cn, static_cast<int64_t>(R) * Cn, out, ld_out, out_b, col0,
+                                        plane_rows);
   return hipGetLastError();
 }
 

@@ -158,23 +158,28 @@ hipError_t launch_combine(const uint16_t* Y, const float* shared_out, const floa
 // threads read 128 contiguous bytes of a row and write one whole 128-byte
 // line of a plane.
 __global__ __launch_bounds__(256) void tile_bf16_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t K,
-                                                        int64_t chunks, uint16_t* __restrict__ dst) {
+                                                        int64_t chunks, uint16_t* __restrict__ dst,
+                                                        int64_t plane_rows, int64_t row0, int64_t group_stride) {
   const int64_t per_row = K / 8, per_group = rows * per_row;
   for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < chunks;
        q += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t g = q / per_group, rem = q - g * per_group;
     const int64_t r = rem / per_row, c = rem - r * per_row;
-    const int64_t to = ((g * (K / kTileK) + c / 8) * rows + r) * kTileK + (c % 8) * 8;
+    const int64_t to = g * group_stride + ((c / 8) * plane_rows + row0 + r) * kTileK + (c % 8) * 8;
     *reinterpret_cast<uint4*>(dst + to) = *reinterpret_cast<const uint4*>(src + q * 8);
   }
 }
 
 hipError_t launch_tile_bf16(const uint16_t* src, int64_t groups, int64_t rows, int64_t K, uint16_t* dst,
-                            hipStream_t stream) {
+                            hipStream_t stream, int64_t plane_rows, int64_t row0, int64_t group_stride) {
   if (groups <= 0 || rows <= 0 || K <= 0 || K % kTileK) return hipErrorInvalidValue;
+  if (plane_rows == 0) plane_rows = rows;
+  if (group_stride == 0) group_stride = plane_rows * K;
+  if (row0 < 0 || row0 + rows > plane_rows || group_stride < plane_rows * K) return hipErrorInvalidValue;
   const int64_t chunks = groups * rows * (K / 8);
   const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 65536);
-  tile_bf16_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(src, rows, K, chunks, dst);
+  tile_bf16_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(src, rows, K, chunks, dst, plane_rows, row0,
+                                                                      group_stride);
   return hipGetLastError();
 }
 

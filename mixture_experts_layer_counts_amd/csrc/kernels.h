@@ -62,8 +62,10 @@ enum GemmEpilogue : int {
 // K-tiled layout of a bf16 matrix [R][K]: element (r, k) at
 // ((k / kTileK) * R + r) * kTileK + k % kTileK (moe_tile_bf16).
 constexpr int kTileK = 64;
+// dst group g (group_stride elements apart; 0: rows * K) takes src group g
+// as rows row0 .. row0 + rows - 1 of its planes of plane_rows rows (0: rows).
 hipError_t launch_tile_bf16(const uint16_t* src, int64_t groups, int64_t rows, int64_t K, uint16_t* dst,
-                            hipStream_t stream);
+                            hipStream_t stream, int64_t plane_rows = 0, int64_t row0 = 0, int64_t group_stride = 0);
 
 struct GemmArgs {
   const uint16_t* A;  // bf16; tile position p reads row (p - a_sub) mod a_mod
@@ -208,9 +210,10 @@ hipError_t launch_seg_transpose(const uint16_t* src, int64_t lda, int W, const i
                                 hipStream_t s);
 // offsets {0, rows}, padded {0, ceil64(rows)}, k_groups[0] = {0, ceil(rows / 64)} for one dense segment
 hipError_t launch_single_segment(int rows, int32_t* offsets, int32_t* padded, int2* k_groups, hipStream_t s);
-// out[b][c][col0 + r] = in[b][r][c], in [B][R][Cn] contiguous, out rows ld_out, batches out_b apart
+// out[b][c][col0 + r] = in[b][r][c], in [B][R][Cn] contiguous, out rows ld_out, batches out_b apart; with
+// plane_rows > 0 each batch of the output is K-tiled with planes of plane_rows rows
 hipError_t launch_transpose(const uint16_t* in, int B, int R, int Cn, uint16_t* out, int64_t ld_out, int64_t out_b,
-                            int col0, hipStream_t s);
+                            int col0, hipStream_t s, int64_t plane_rows = 0);
 // dx[t] = dx_shared[t] + dx_router[t] + sum_s dx_ring[route_dst[t k + s]] (fp32, in that order)
 hipError_t launch_dx_assemble(const float* dx_shared, const float* dx_router, const float* dx_ring,
                               const int32_t* route_dst, int T, int D, int k, int64_t P, float* dx, int* err,

@@ -957,19 +957,22 @@ moe_status moe_backward_prepare(const moe_shape* shape, const moe_weights* w, co
   const int L = static_cast<int>(shape->experts_per_rank), D = static_cast<int>(shape->D);
   const int I = static_cast<int>(shape->I), Is = static_cast<int>(shape->I_shared), E = static_cast<int>(shape->E_total);
   const int64_t Ep = pad64(E);
-  const size_t slab = static_cast<size_t>(I) * D * 2;  // bytes of one expert's gate (or up) matrix
-  auto* gu = static_cast<char*>(bw->w_gu);
-  // w_gu: gate rows then up rows of each expert
-  MOE_TRY_HIP(hipMemcpy2DAsync(gu, 2 * slab, w->w_gate, slab, slab, L, hipMemcpyDeviceToDevice, s));
-  MOE_TRY_HIP(hipMemcpy2DAsync(gu + slab, 2 * slab, w->w_up, slab, slab, L, hipMemcpyDeviceToDevice, s));
+  // the routed copies are K-tiled (the backward's routed GEMMs read one
+  // plane per K stage, as the forward's do with K-tiled weights):
+  // w_gu: gate rows then up rows of each expert, [L, D/64, 2I, 64]
   const uint16_t* wg = static_cast<const uint16_t*>(w->w_gate);
   const uint16_t* wu = static_cast<const uint16_t*>(w->w_up);
   const uint16_t* wd = static_cast<const uint16_t*>(w->w_down);
+  auto* gu = static_cast<uint16_t*>(bw->w_gu);
+  const int64_t gu_stride = static_cast<int64_t>(2) * I * D;
+  MOE_TRY_HIP(moe::launch_tile_bf16(wg, L, I, D, gu, s, 2 * I, 0, gu_stride));
+  MOE_TRY_HIP(moe::launch_tile_bf16(wu, L, I, D, gu, s, 2 * I, I, gu_stride));
+  // w_gu_t: [W_gate^T | W_up^T], [L, 2I/64, D, 64]; w_down_t: [L, D/64, I, 64]
   auto* gut = static_cast<uint16_t*>(bw->w_gu_t);
-  MOE_TRY_HIP(moe::launch_transpose(wg, L, I, D, gut, 2 * I, static_cast<int64_t>(D) * 2 * I, 0, s));
-  MOE_TRY_HIP(moe::launch_transpose(wu, L, I, D, gut, 2 * I, static_cast<int64_t>(D) * 2 * I, I, s));
+  MOE_TRY_HIP(moe::launch_transpose(wg, L, I, D, gut, 2 * I, static_cast<int64_t>(D) * 2 * I, 0, s, D));
+  MOE_TRY_HIP(moe::launch_transpose(wu, L, I, D, gut, 2 * I, static_cast<int64_t>(D) * 2 * I, I, s, D));
   MOE_TRY_HIP(moe::launch_transpose(wd, L, D, I, static_cast<uint16_t*>(bw->w_down_t), D,
-                                    static_cast<int64_t>(I) * D, 0, s));
+                                    static_cast<int64_t>(I) * D, 0, s, I));
   const size_t sslab = static_cast<size_t>(Is) * D * 2;
   MOE_TRY_HIP(hipMemcpyAsync(bw->ws_gu, w->ws_gate, sslab, hipMemcpyDeviceToDevice, s));
   MOE_TRY_HIP(hipMemcpyAsync(static_cast<char*>(bw->ws_gu) + sslab, w->ws_up, sslab, hipMemcpyDeviceToDevice, s));
@@ -1039,6 +1042,7 @@ moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const
     a.a_mod = INT64_MAX;
     a.B0 = static_cast<const uint16_t*>(B);
     a.b_expert_stride = b_stride;
+    a.b_plane = N;  // the prepared routed weights are K-tiled
     a.N = N;
     a.K = K;
     a.C = C;
