@@ -179,7 +179,7 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __rest
 __global__ __launch_bounds__(256) void seg_transpose_kernel(const uint16_t* __restrict__ src, int64_t lda, int W,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ padded, int L,
-                                                            uint16_t* __restrict__ out, int64_t ld_out) {
+                                                            uint16_t* __restrict__ out, int64_t ld_out, bool tiled) {
   constexpr int kStride = 72;  // LDS row stride in elements (144 bytes: 16-byte aligned rows, spread banks)
   __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kStride];
   const int64_t q0 = static_cast<int64_t>(blockIdx.x) * 64;  // output column chunk
@@ -215,9 +215,12 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(const uint16_t* __re
     // the transposed operands (up to 1 GB each) are read back by the
     // weight-gradient GEMMs only after the other transposes: non-temporal
     // stores (measured 0.2% off the backward)
+    // row-major [W][ld_out], or K-tiled: output column chunk q0 is one plane
+    // of W rows, so the block's 64 x 64 tile is 8 KB of contiguous output
+    const int64_t to = tiled ? ((q0 / kTileK) * W + w0 + c) * kTileK + r : static_cast<int64_t>(w0 + c) * ld_out + q0 + r;
     if (w0 + c < W)
       __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(tile + c * kStride + r),
-                                  reinterpret_cast<u32x4_t*>(out + static_cast<int64_t>(w0 + c) * ld_out + q0 + r));
+                                  reinterpret_cast<u32x4_t*>(out + to));
   }
 }
 
@@ -334,13 +337,13 @@ hipError_t launch_pad_offsets(const int32_t* offsets, int L, int32_t* padded, in
 
 hipError_t launch_seg_transpose(const uint16_t* src, int64_t lda, int W, const int32_t* offsets,
                                 const int32_t* padded, int L, int64_t max_cols, uint16_t* out, int64_t ld_out,
-                                hipStream_t s) {
+                                hipStream_t s, bool tiled) {
   if (max_cols <= 0 || W <= 0) return hipSuccess;
   if (W % 8 || lda % 8 || ld_out % 64 || reinterpret_cast<uintptr_t>(src) % 16 ||
       reinterpret_cast<uintptr_t>(out) % 16)
     return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>((max_cols + 63) / 64), static_cast<unsigned>((W + 63) / 64));
-  seg_transpose_kernel<<<grid, 256, 0, s>>>(src, lda, W, offsets, padded, L, out, ld_out);
+  seg_transpose_kernel<<<grid, 256, 0, s>>>(src, lda, W, offsets, padded, L, out, ld_out, tiled);
   return hipGetLastError();
 }
 

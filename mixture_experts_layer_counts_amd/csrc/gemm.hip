@@ -109,8 +109,8 @@ __device__ __forceinline__ int tile_row(int wm, int fm) {
 // read.  FML = 32-row MFMA blocks of this wave that hold tile rows.
 template <int BM, int BN, int WM, int WN, int NB, int FML, int FM, int FN, int BK, int AI, int BI>
 __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uint32_t (&a_off)[AI],
-                                       const uint32_t (&b_off)[BI], int nk, int a_rows, int b_stage, int tid,
-                                       int wm, int wn, f32x16_t (&acc)[NB][FM][FN]) {
+                                       const uint32_t (&b_off)[BI], int nk, int a_rows, int a_stage, int b_stage,
+                                       int tid, int wm, int wn, f32x16_t (&acc)[NB][FM][FN]) {
   constexpr int RB = BK * 2;  // bytes of one row of a stage
   constexpr int BROWS = NB * BN;
   constexpr int NSA = ring_a_slots(BK), NSB = ring_b_slots(BK, BM * RB, BROWS * RB);  // ring slots
@@ -130,8 +130,10 @@ __device__ __forceinline__ void k_loop(char* smem, const TileSrc& src, const uin
   // a stage past the last (in the prologue of a K range shorter than the
   // rings) loads the last stage again, into a free slot, so that the
   // prologue issues the same number of loads
+  // a_stage, b_stage: bytes from one K stage of a row to the next (RB
+  // row-major, a whole plane K-tiled)
   auto issue_a = [&](int kt) __attribute__((always_inline)) {
-    const int ko = (kt < nk ? kt : nk - 1) * RB;
+    const int ko = (kt < nk ? kt : nk - 1) * a_stage;
     char* sa = sa0 + (kt % NSA) * ASLOT;
     // A row groups past the tile are not fetched (their rows only feed dropped
     // outputs); a reload of the group's first row keeps the per-wave load
@@ -324,6 +326,11 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
   // and rows past N onto row N-1: their products only reach output rows and
   // columns that are dropped.
   constexpr int CH = RB / 16;
+  // K-tiled operands (BK is the tiling's plane width): a stage's rows sit in
+  // one plane, RB bytes apart, and the next stage's plane follows
+  static_assert(BK == kTileK, "K stages are the tiling's planes");
+  const bool a_tiled = args.a_plane > 0;
+  const int a_stage = a_tiled ? static_cast<int>(args.a_plane * RB) : RB;
   uint32_t a_off[AI];
 #pragma unroll
   for (int j = 0; j < AI; ++j) {
@@ -331,12 +338,10 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
     const int c = (lane % CH) ^ ((row / (256 / RB)) & (CH - 1));
     const int64_t p = p0 + (row < nrows ? row : nrows - 1);
     const int64_t arow = (p - args.a_sub) % args.a_mod;
-    a_off[j] = static_cast<uint32_t>((arow * args.lda + k0 + c * 8) * 2);
+    a_off[j] = a_tiled ? static_cast<uint32_t>(((k0 / BK) * args.a_plane + arow) * RB + c * 16)
+                       : static_cast<uint32_t>((arow * args.lda + k0 + c * 8) * 2);
   }
-  // weights K-tiled (routed only; BK is the tiling's plane width): a stage's
-  // weight rows sit in one plane of N rows, RB bytes apart
-  const bool b_tiled = ROUTED && args.b_plane > 0;
-  static_assert(!ROUTED || BK == kTileK, "routed K stages are the tiling's planes");
+  const bool b_tiled = args.b_plane > 0;
   const int b_stage = b_tiled ? static_cast<int>(args.b_plane * RB) : RB;
   uint32_t b_off[BI];
 #pragma unroll
@@ -346,7 +351,7 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
     const int half = row / BN;
     int n = n0 + (row - half * BN);
     n = n < args.N ? n : args.N - 1;
-    b_off[j] = b_tiled ? static_cast<uint32_t>(n * RB + c * 16)
+    b_off[j] = b_tiled ? static_cast<uint32_t>(((k0 / BK) * args.b_plane + n) * RB + c * 16)
                        : static_cast<uint32_t>((static_cast<int64_t>(n) * ldb + k0 + c * 8) * 2);
   }
   constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
@@ -378,8 +383,8 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& args, int w, int n_blo
 #define MOE_CASE(n)                                                                       \
   case n:                                                                                 \
     if constexpr (n <= FM)                                                                \
-      k_loop<BM, BN, WM, WN, NB, n, FM, FN, BK, AI, BI>(smem, src, a_off, b_off, nk, nrows, b_stage, tid, wm, wn, \
-                                                        acc);                                                   \
+      k_loop<BM, BN, WM, WN, NB, n, FM, FN, BK, AI, BI>(smem, src, a_off, b_off, nk, nrows, a_stage, b_stage, tid, wm, \
+                                                        wn, acc);                                               \
     break;
     MOE_CASE(0)
     MOE_CASE(1)
@@ -926,8 +931,12 @@ hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t stream) {
   if (!a.k_groups && a.K % (kStageK * a.k_splits) != 0) return hipErrorInvalidValue;
   const int64_t ldb = a.ldb ? a.ldb : a.K;
   if (ldb % 8 != 0) return hipErrorInvalidValue;  // 16-byte aligned B rows
-  // K-tiled weights: routed, planes of all N rows, K in whole planes
-  if (a.b_plane != 0 && (!routed || a.b_plane != a.N || ldb != a.K || a.K % kTileK)) return hipErrorInvalidValue;
+  // K-tiled weights: planes of all N rows, K in whole planes (routed), or
+  // grouped K over a K extent ldb; K-tiled A: grouped K only
+  if (a.b_plane != 0 && (a.b_plane != a.N || (routed ? (ldb != a.K || a.K % kTileK) : (!a.k_groups || ldb % kTileK))))
+    return hipErrorInvalidValue;
+  if (a.a_plane < 0 || (a.a_plane > 0 && (!a.k_groups || a.lda % kTileK || a.a_plane < a.dense_rows)))
+    return hipErrorInvalidValue;
   // buffer resources address at most 2^31 bytes per operand here
   if (a.a_bytes <= 0 || a.a_bytes >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   if (static_cast<int64_t>(a.N) * ldb * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;

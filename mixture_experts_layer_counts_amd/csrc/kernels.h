@@ -73,11 +73,15 @@ struct GemmArgs {
   int64_t lda;
   int64_t a_sub;
   int64_t a_mod;
+  // 0: A row-major (lda); > 0 (grouped K only): A K-tiled with planes of
+  // a_plane rows, A pointing at the first of its rows in a plane
+  int64_t a_plane;
   const uint16_t* B0;  // bf16 [experts][N][K]
   const uint16_t* B1;  // second operand of the SwiGLU epilogue (same layout)
   int64_t b_expert_stride;
-  // 0: each expert's B row-major [N][K] (row stride ldb); N (routed only):
-  // K-tiled [K/kTileK][N][kTileK], so that one K stage's rows are one plane
+  // 0: each expert's B row-major [N][K] (row stride ldb); N (routed, or
+  // grouped K with ldb the K extent): K-tiled [K/kTileK][N][kTileK], so
+  // that one K stage's rows are one plane
   int64_t b_plane;
   int N;
   int K;
@@ -207,7 +211,7 @@ hipError_t launch_pad_offsets(const int32_t* offsets, int L, int32_t* padded, in
 // out [W][ld_out]: column padded[e] + i = row offsets[e] + i of src [.][lda] (zero past the segment)
 hipError_t launch_seg_transpose(const uint16_t* src, int64_t lda, int W, const int32_t* offsets,
                                 const int32_t* padded, int L, int64_t max_cols, uint16_t* out, int64_t ld_out,
-                                hipStream_t s);
+                                hipStream_t s, bool tiled = false);
 // offsets {0, rows}, padded {0, ceil64(rows)}, k_groups[0] = {0, ceil(rows / 64)} for one dense segment
 hipError_t launch_single_segment(int rows, int32_t* offsets, int32_t* padded, int2* k_groups, hipStream_t s);
 // out[b][c][col0 + r] = in[b][r][c], in [B][R][Cn] contiguous, out rows ld_out, batches out_b apart; with

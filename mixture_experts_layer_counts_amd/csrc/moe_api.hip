@@ -1077,20 +1077,27 @@ moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const
     uint16_t* daT = at<uint16_t>(ws, L.daT);
     uint16_t* xT = at<uint16_t>(ws, L.xT);
     MOE_TRY_HIP(moe::launch_pad_offsets(expert_offsets, Lx, padded, kg, s));
-    MOE_TRY_HIP(moe::launch_seg_transpose(dy, D, D, expert_offsets, padded, Lx, Ppad, dyT, Ppad, s));
-    MOE_TRY_HIP(moe::launch_seg_transpose(h, I, I, expert_offsets, padded, Lx, Ppad, hT, Ppad, s));
-    MOE_TRY_HIP(moe::launch_seg_transpose(da, 2 * I, 2 * I, expert_offsets, padded, Lx, Ppad, daT, Ppad, s));
-    MOE_TRY_HIP(moe::launch_seg_transpose(ring, D, D, expert_offsets, padded, Lx, Ppad, xT, Ppad, s));
-    auto grouped = [&](const uint16_t* A, int64_t M, const uint16_t* B, int N, void* C, int64_t ldc, int64_t gs) {
-      moe::GemmArgs a = dense_args(A, Ppad, M, B, Ppad, N, 0, C, ldc);
+    // the transposed operands are K-tiled (planes of 64 rows of the segment
+    // axis), so each K stage of the grouped GEMMs reads contiguous planes
+    MOE_TRY_HIP(moe::launch_seg_transpose(dy, D, D, expert_offsets, padded, Lx, Ppad, dyT, Ppad, s, true));
+    MOE_TRY_HIP(moe::launch_seg_transpose(h, I, I, expert_offsets, padded, Lx, Ppad, hT, Ppad, s, true));
+    MOE_TRY_HIP(moe::launch_seg_transpose(da, 2 * I, 2 * I, expert_offsets, padded, Lx, Ppad, daT, Ppad, s, true));
+    MOE_TRY_HIP(moe::launch_seg_transpose(ring, D, D, expert_offsets, padded, Lx, Ppad, xT, Ppad, s, true));
+    // A: M rows starting at row a0 of planes of a_rows rows; B: planes of N rows
+    auto grouped = [&](const uint16_t* A, int64_t M, int64_t a_rows, int64_t a0, const uint16_t* B, int N, void* C,
+                       int64_t ldc, int64_t gs) {
+      moe::GemmArgs a = dense_args(A + a0 * moe::kTileK, Ppad, M, B, Ppad, N, 0, C, ldc);
+      a.a_plane = a_rows;
+      a.a_bytes = (a_rows * Ppad - a0 * moe::kTileK) * 2;
+      a.b_plane = N;
       a.k_groups = kg;
       a.n_groups = Lx;
       a.c_group_stride = gs;
       return a;
     };
-    MOE_TRY_HIP(moe::launch_gemm(grouped(dyT, D, hT, I, g->dw_down, I, int64_t(D) * I), moe::kEpiBF16, s));
-    MOE_TRY_HIP(moe::launch_gemm(grouped(daT, I, xT, D, g->dw_gate, D, int64_t(I) * D), moe::kEpiBF16, s));
-    MOE_TRY_HIP(moe::launch_gemm(grouped(daT + I * Ppad, I, xT, D, g->dw_up, D, int64_t(I) * D), moe::kEpiBF16, s));
+    MOE_TRY_HIP(moe::launch_gemm(grouped(dyT, D, D, 0, hT, I, g->dw_down, I, int64_t(D) * I), moe::kEpiBF16, s));
+    MOE_TRY_HIP(moe::launch_gemm(grouped(daT, I, 2 * I, 0, xT, D, g->dw_gate, D, int64_t(I) * D), moe::kEpiBF16, s));
+    MOE_TRY_HIP(moe::launch_gemm(grouped(daT, I, 2 * I, I, xT, D, g->dw_up, D, int64_t(I) * D), moe::kEpiBF16, s));
   }
 
   // ---- the shared expert, on every token with dy = dout ----
@@ -1111,19 +1118,23 @@ moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const
   uint16_t* da_sT = at<uint16_t>(ws, L.da_sT);
   uint16_t* x_T = at<uint16_t>(ws, L.x_T);
   MOE_TRY_HIP(moe::launch_single_segment(T, seg_off, seg_pad, seg_kg, s));
-  MOE_TRY_HIP(moe::launch_seg_transpose(dob, D, D, seg_off, seg_pad, 1, Tpad, doutT, Tpad, s));
-  MOE_TRY_HIP(moe::launch_seg_transpose(h_s, Is, Is, seg_off, seg_pad, 1, Tpad, h_sT, Tpad, s));
-  MOE_TRY_HIP(moe::launch_seg_transpose(da_s, 2 * Is, 2 * Is, seg_off, seg_pad, 1, Tpad, da_sT, Tpad, s));
-  MOE_TRY_HIP(moe::launch_seg_transpose(xb, D, D, seg_off, seg_pad, 1, Tpad, x_T, Tpad, s));
-  auto one_group = [&](const uint16_t* A, int64_t M, const uint16_t* B, int N, void* C, int64_t ldc) {
-    moe::GemmArgs a = dense_args(A, Tpad, M, B, Tpad, N, 0, C, ldc);
+  MOE_TRY_HIP(moe::launch_seg_transpose(dob, D, D, seg_off, seg_pad, 1, Tpad, doutT, Tpad, s, true));
+  MOE_TRY_HIP(moe::launch_seg_transpose(h_s, Is, Is, seg_off, seg_pad, 1, Tpad, h_sT, Tpad, s, true));
+  MOE_TRY_HIP(moe::launch_seg_transpose(da_s, 2 * Is, 2 * Is, seg_off, seg_pad, 1, Tpad, da_sT, Tpad, s, true));
+  MOE_TRY_HIP(moe::launch_seg_transpose(xb, D, D, seg_off, seg_pad, 1, Tpad, x_T, Tpad, s, true));
+  auto one_group = [&](const uint16_t* A, int64_t M, int64_t a_rows, int64_t a0, const uint16_t* B, int N, void* C,
+                       int64_t ldc) {
+    moe::GemmArgs a = dense_args(A + a0 * moe::kTileK, Tpad, M, B, Tpad, N, 0, C, ldc);
+    a.a_plane = a_rows;
+    a.a_bytes = (a_rows * Tpad - a0 * moe::kTileK) * 2;
+    a.b_plane = N;
     a.k_groups = seg_kg;
     a.n_groups = 1;
     return a;
   };
-  MOE_TRY_HIP(moe::launch_gemm(one_group(doutT, D, h_sT, Is, g->dws_down, Is), moe::kEpiBF16, s));
-  MOE_TRY_HIP(moe::launch_gemm(one_group(da_sT, Is, x_T, D, g->dws_gate, D), moe::kEpiBF16, s));
-  MOE_TRY_HIP(moe::launch_gemm(one_group(da_sT + Is * Tpad, Is, x_T, D, g->dws_up, D), moe::kEpiBF16, s));
+  MOE_TRY_HIP(moe::launch_gemm(one_group(doutT, D, D, 0, h_sT, Is, g->dws_down, Is), moe::kEpiBF16, s));
+  MOE_TRY_HIP(moe::launch_gemm(one_group(da_sT, Is, 2 * Is, 0, x_T, D, g->dws_gate, D), moe::kEpiBF16, s));
+  MOE_TRY_HIP(moe::launch_gemm(one_group(da_sT, Is, 2 * Is, Is, x_T, D, g->dws_up, D), moe::kEpiBF16, s));
 
   // ---- router: gate gradients, the selected logits' gradient, its two products ----
   float* dg = at<float>(ws, L.dg);
@@ -1134,8 +1145,8 @@ moe_status moe_backward(const moe_shape* shape, const moe_bwd_weights* bw, const
   MOE_TRY_HIP(moe::launch_gate_grad(topk_gate, dg, topk_idx, T, E, static_cast<int>(Ep), k, dl, s));
   MOE_TRY_HIP(moe::launch_gemm(dense_args(dl, Ep, T, bw->w_router_t, 0, D, static_cast<int>(Ep), dx_r, D),
                                moe::kEpiF32, s));
-  MOE_TRY_HIP(moe::launch_seg_transpose(dl, Ep, static_cast<int>(Ep), seg_off, seg_pad, 1, Tpad, dlT, Tpad, s));
-  MOE_TRY_HIP(moe::launch_gemm(one_group(dlT, E, x_T, D, g->dw_router, D), moe::kEpiF32, s));
+  MOE_TRY_HIP(moe::launch_seg_transpose(dl, Ep, static_cast<int>(Ep), seg_off, seg_pad, 1, Tpad, dlT, Tpad, s, true));
+  MOE_TRY_HIP(moe::launch_gemm(one_group(dlT, E, Ep, 0, x_T, D, g->dw_router, D), moe::kEpiF32, s));
 
   // ---- dx, in a fixed order ----
   return hip_status(moe::launch_dx_assemble(dx_s, dx_r, dx_ring, route_dst, T, D, k, P, g->dx, dev_error, s));
